@@ -1,0 +1,168 @@
+/*
+ * moe_mi355x.h -- C ABI of the fused MoE layer for one MI355X (gfx950).
+ *
+ * The layer (the pages describe it only step by step; the arithmetic below is the plainest
+ * reading of a top-k softmax-routed SwiGLU MoE layer):
+ *   route    per token, the k largest of E fp32 router logits (descending, ties to the lower expert
+ *            id, -0.0 == +0.0) and their softmax renormalised over the selected k.  "Once routing
+ *            completes, each layer's ... volumes become known" (Weave, Abstract).
+ *   permute  expert histogram, exclusive prefix sum and a stable counting sort of the slots
+ *            s = t*k + j into expert-contiguous rows: the single-GPU share of token dispatch
+ *            (GC-MoE, summary; Weave, Abstract).
+ *   experts  grouped gate/up GEMM with fused SwiGLU, then the grouped down GEMM, on shapes that
+ *            follow the live routing histogram, chosen on the device with no host sync
+ *            ("Decoding the Skew: Distribution-Aware MoE Inference with Adaptive Kernel Dispatch",
+ *            Abstract; GC-MoE, summary: fused SwiGLU, FP8 requantisation, optional shared experts).
+ *   combine  out[t] = sum_j w[t,j] * y[slot_dst[t*k+j]] (+ shared[t]), summed in fp32 in j order,
+ *            rounded once to bf16 (GC-MoE, summary: "combine step").
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller; the two structs are host memory
+ *     read during the call only.  The library never allocates, frees or synchronises: every call
+ *     only enqueues work on `stream` and returns; outputs are valid once the stream reaches them.
+ *   - Layouts are row-major.  bf16 values are 16-bit bfloat16 bit patterns; fp8 values are OCP
+ *     E4M3FN bytes (bias 7, max 448, S.1111.111 = NaN).
+ *   - Expert weights are stored with the contraction dimension contiguous:
+ *       w_gate, w_up [E][d_ff][d_model]   (math shape d_model x d_ff)
+ *       w_down       [E][d_model][d_ff]   (math shape d_ff x d_model)
+ *     fp8 weights carry one fp32 scale per 128x128 block: s_gate, s_up [E][d_ff/128][d_model/128],
+ *     s_down [E][d_model/128][d_ff/128]; the weight's value is code * scale.
+ *   - Return value: MOE_OK or an error code; moe_status_string() names it.  Arguments are checked
+ *     on the host only (null pointers, sizes, 16-byte alignment, workspace size).  Device data is
+ *     not validated: non-finite logits or out-of-range expert ids are undefined behaviour.
+ *     T = 0 is a valid no-op.  A failed launch returns MOE_ERR_HIP.
+ *   - Limits: 1 <= k <= 8, k <= E <= 512, d_model and d_ff multiples of 128, T*k < 2^31.
+ *   - Calls are reentrant: no mutable global state; concurrent calls need distinct workspaces.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* shape or dtype outside the limits above */
+  MOE_ERR_WORKSPACE = 3,   /* workspace null or smaller than the *_workspace_bytes() figure */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+};
+
+enum moe_dtype {
+  MOE_DTYPE_BF16 = 0,
+  MOE_DTYPE_FP8_E4M3 = 1
+};
+
+/* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert from
+ * the live histogram; the others force one family for every expert (used by tests to cover each). */
+enum moe_config {
+  MOE_CONFIG_AUTO = -1,
+  MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: all of an expert's rows (<= 64) per pass */
+  MOE_CONFIG_MFMA128 = 1, /* LDS-tiled MFMA tiles of 128 rows */
+  MOE_CONFIG_MFMA256 = 2  /* LDS-tiled MFMA tiles of 256 rows */
+};
+
+typedef struct moe_problem {
+  int32_t T;           /* tokens */
+  int32_t d_model;     /* hidden size d */
+  int32_t d_ff;        /* routed expert intermediate size f */
+  int32_t num_experts; /* E */
+  int32_t top_k;       /* k */
+  int32_t wdtype;      /* enum moe_dtype of the expert weights (activations are bf16 at the boundary) */
+  int32_t has_shared;  /* 1: one always-active shared SwiGLU expert, added with weight 1 */
+  int32_t d_ff_shared; /* its intermediate size (multiple of 128) */
+  int32_t config;      /* enum moe_config */
+} moe_problem;
+
+typedef struct moe_weights {
+  const void* w_gate; /* [E][f][d] bf16 or e4m3 */
+  const void* w_up;   /* [E][f][d] */
+  const void* w_down; /* [E][d][f] */
+  const float* s_gate; /* fp8 only: [E][f/128][d/128]; NULL for bf16 */
+  const float* s_up;
+  const float* s_down; /* [E][d/128][f/128] */
+  const void* sh_gate; /* shared expert (has_shared), [f_sh][d], same dtype */
+  const void* sh_up;
+  const void* sh_down; /* [d][f_sh] */
+  const float* s_sh_gate; /* fp8 only */
+  const float* s_sh_up;
+  const float* s_sh_down;
+} moe_weights;
+
+/* Optional routing outputs of moe_layer (any member may be NULL to skip it). */
+typedef struct moe_routing {
+  int32_t* topk_ids; /* [T][k] */
+  float* topk_w;     /* [T][k] */
+  int32_t* counts;   /* [E] */
+  int32_t* offsets;  /* [E+1] */
+  int32_t* perm_src; /* [T*k] */
+  int32_t* slot_dst; /* [T*k] */
+} moe_routing;
+
+/* Route: topk_ids[t][j] = j-th largest logit's expert (ties -> lower id), topk_w[t][j] = its
+ * weight in the softmax renormalised over the selected k, computed in fp32 (expf of the gap to the
+ * largest selected logit, divided by their sum).
+ *   logits [T][E] fp32.  Outputs [T][k]. */
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream);
+
+/* Permute (dispatch share): counts[e] = #slots routed to e; offsets[0..E] its exclusive prefix sum
+ * (offsets[E] = T*k); perm_src[row] = slot s = t*k+j placed at expert-contiguous row `row`, in
+ * increasing s inside each expert (stable); slot_dst[s] = row.  If x_perm is not NULL, also gathers
+ * x_perm[row] = x[perm_src[row] / k]: act_dtype MOE_DTYPE_BF16 copies d bf16 values per row;
+ * MOE_DTYPE_FP8_E4M3 copies d e4m3 bytes per row and, if x_perm_scale is not NULL, the d/128 fp32
+ * scales per row from x_scale.
+ *   topk_ids [T][k] int32 in [0, E).  ws: moe_permute_workspace_bytes(T, E, k) bytes. */
+int moe_permute(const int32_t* topk_ids, int T, int E, int k, const void* x, const float* x_scale,
+                int d, int act_dtype, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                int32_t* slot_dst, void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+
+/* Activation quantisation for fp8 weights: per token and per 128 channels,
+ * s = fp32(amax / 448) (s = 1 when amax is 0 or the quotient underflows to 0),
+ * q = e4m3(fp32(x / s)) with IEEE division, nearest-even rounding, saturation at +-448 and the
+ * sign kept (negative values that round to zero give 0x80).
+ *   x [T][d] bf16 -> xq [T][d] e4m3, xs [T][d/128] fp32. */
+int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t stream);
+
+/* Grouped expert FFN on expert-contiguous rows: for every expert e with counts[e] > 0, rows
+ * [offsets[e], offsets[e]+counts[e]) of x_perm go through (SiLU(X Wg^T) * (X Wu^T)) Wd^T; the result
+ * lands in the same rows of y_perm ([rows][d] bf16, rows = offsets[E]).  bf16 weights: x_perm is
+ * bf16 and x_perm_scale NULL.  fp8 weights: x_perm is e4m3 with x_perm_scale [rows][d/128]; the
+ * SwiGLU output is requantised to e4m3 per row and 128 channels before the down GEMM.  Tile
+ * shapes are chosen on the device from counts (p->config may force one family).  The shared expert
+ * fields of p and w are ignored here.
+ *   ws: moe_grouped_ffn_workspace_bytes(p) bytes (rows = T*k of p). */
+int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
+                    const int32_t* counts, const int32_t* offsets, const moe_weights* w,
+                    void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_grouped_ffn_workspace_bytes(const moe_problem* p);
+
+/* Combine: out[t] = bf16( sum_{j<k} topk_w[t][j] * y_perm[slot_dst[t*k+j]] (+ shared_y[t]) ),
+ * the sum in fp32 in increasing j, the shared row (if not NULL) added last.
+ *   y_perm [T*k][d] bf16, shared_y [T][d] bf16 or NULL, out [T][d] bf16. */
+int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w, int T, int k,
+                int d, const void* shared_y, void* out, hipStream_t stream);
+
+/* The whole layer: route -> permute -> (fp8: quantise activations) -> grouped gate/up + SwiGLU ->
+ * grouped down (+ shared expert) -> combine.  The token gather is fused into the gate/up GEMM's
+ * activation loads.
+ *   logits [T][E] fp32, x [T][d] bf16, out [T][d] bf16.  keep: optional routing outputs.
+ *   ws: moe_layer_workspace_bytes(p) bytes. */
+int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
+              void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t moe_layer_workspace_bytes(const moe_problem* p);
+
+/* Static name of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

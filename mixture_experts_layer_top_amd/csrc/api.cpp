@@ -1,0 +1,360 @@
+// Host side of the C ABI declared in include/moe_mi355x.h: argument checks, workspace carving and
+// kernel launches on the caller's stream.  No allocation, no synchronisation, no host reads of
+// device data: every decision that depends on the routing is taken on the device.
+#include "moe_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 8;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sequential carving of a workspace (or a dry run that only sums the sizes when base is null).
+struct Carver {
+  uint8_t* base;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+// Compute-unit count of the current device (read-only after the first query per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int check_route_shape(int T, int E, int k) {
+  if (T < 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxTopK || E > kMaxExperts || k > E) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  int st = check_route_shape(p->T, p->num_experts, p->top_k);
+  if (st) return st;
+  if (p->d_model <= 0 || p->d_ff <= 0) return MOE_ERR_INVALID_ARG;
+  if (p->d_model % 128 || p->d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
+  if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA256) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  const void* need[] = {w->w_gate, w->w_up, w->w_down};
+  for (const void* q : need)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3) {
+    if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_INVALID_ARG;
+  }
+  if (with_shared && p->has_shared) {
+    const void* sh[] = {w->sh_gate, w->sh_up, w->sh_down};
+    for (const void* q : sh)
+      if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+    if (p->wdtype == MOE_DTYPE_FP8_E4M3 && (!w->s_sh_gate || !w->s_sh_up || !w->s_sh_down))
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of the grouped GEMMs: segment lists, queue counters and the SwiGLU output.
+struct FfnWs {
+  Seg* segs;
+  int32_t* meta;
+  void* h;
+  float* hs;
+  void* h_sh;
+  float* hs_sh;
+  void* y_sh;
+};
+
+void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
+  const size_t n = (size_t)p->T * p->top_k;
+  const size_t wb = p->wdtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
+  f.segs = c.take<Seg>((size_t)2 * kNumFam * kSegCap);
+  f.meta = c.take<int32_t>(2 * kNumFam * kMetaStride);
+  f.h = c.take<uint8_t>(n * p->d_ff * wb);
+  f.hs = wb == 1 ? c.take<float>(n * (p->d_ff / 128)) : nullptr;
+  f.h_sh = f.hs_sh = nullptr;
+  f.y_sh = nullptr;
+  if (with_shared && p->has_shared) {
+    f.h_sh = c.take<uint8_t>((size_t)p->T * p->d_ff_shared * wb);
+    f.hs_sh = wb == 1 ? c.take<float>((size_t)p->T * (p->d_ff_shared / 128)) : nullptr;
+    f.y_sh = c.take<uint16_t>((size_t)p->T * p->d_model);
+  }
+}
+
+hipError_t launch_gemms(const SelectOut& o, int fp8, hipStream_t s) {
+  return fp8 ? moe::launch_gemms_fp8(o, device_cus(), s) : moe::launch_gemms_bf16(o, device_cus(), s);
+}
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null, misaligned or out-of-range argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype outside the supported limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream) {
+  int st = check_route_shape(T, E, k);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(logits, T, E, k, topk_ids, topk_w, stream));
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+  if (check_route_shape(T, E, k)) return 0;
+  const size_t n = (size_t)T * k;
+  Carver c{nullptr};
+  c.take<int32_t>(n);
+  c.take<int32_t>((size_t)permute_nchunk((int)n) * E);
+  return c.used;
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int E, int k, const void* x, const float* x_scale,
+                int d, int act_dtype, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                int32_t* slot_dst, void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int st = check_route_shape(T, E, k);
+  if (st) return st;
+  if (!counts || !offsets || !perm_src || !slot_dst) return MOE_ERR_INVALID_ARG;
+  if (x_perm) {
+    if (!x || d <= 0) return MOE_ERR_INVALID_ARG;
+    if (d % 128) return MOE_ERR_UNSUPPORTED;
+    if (act_dtype != MOE_DTYPE_BF16 && act_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+    if (act_dtype == MOE_DTYPE_FP8_E4M3 && x_perm_scale && !x_scale) return MOE_ERR_INVALID_ARG;
+  }
+  if (T > 0 && !topk_ids) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_permute_workspace_bytes(T, E, k);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int n = T * k;
+  Carver c{static_cast<uint8_t*>(ws)};
+  int32_t* rank = c.take<int32_t>(n);
+  int32_t* hist = c.take<int32_t>((size_t)permute_nchunk(n) * E);
+  hipError_t e = launch_permute(topk_ids, T, E, k, counts, offsets, perm_src, slot_dst, nullptr,
+                                rank, hist, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (x_perm && n > 0) {
+    const int fp8 = act_dtype == MOE_DTYPE_FP8_E4M3;
+    e = launch_gather(x, fp8 ? x_scale : nullptr, perm_src, n, k, fp8 ? d : 2 * d, d / 128, x_perm,
+                      fp8 ? x_perm_scale : nullptr, stream);
+  }
+  return hip_status(e);
+}
+
+int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t stream) {
+  if (T < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 128) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !xq || !xs) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_act(x, T, d, xq, xs, stream));
+}
+
+size_t moe_grouped_ffn_workspace_bytes(const moe_problem* p) {
+  if (check_problem(p)) return 0;
+  Carver c{nullptr};
+  FfnWs f;
+  carve_ffn(c, p, false, f);
+  return c.used;
+}
+
+int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
+                    const int32_t* counts, const int32_t* offsets, const moe_weights* w,
+                    void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_problem(p);
+  if (st) return st;
+  st = check_weights(p, w, false);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  const int fp8 = p->wdtype == MOE_DTYPE_FP8_E4M3;
+  if (!x_perm || !counts || !offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && !x_perm_scale) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_grouped_ffn_workspace_bytes(p);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  Carver c{static_cast<uint8_t*>(ws)};
+  FfnWs f;
+  carve_ffn(c, p, false, f);
+  SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.counts = counts;
+  a.offsets = offsets;
+  a.E = p->num_experts;
+  a.T = p->T;
+  a.k = p->top_k;
+  a.d = p->d_model;
+  a.f = p->d_ff;
+  a.has_shared = 0;
+  a.config = p->config;
+  a.fp8 = fp8;
+  a.x = x_perm;
+  a.xs = fp8 ? x_perm_scale : nullptr;
+  a.tok = nullptr;
+  a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+  a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+  a.h = f.h; a.hs = f.hs;
+  a.y = y_perm;
+  SelectOut o{f.segs, f.meta};
+  hipError_t e = launch_select(a, o, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_gemms(o, fp8, stream));
+}
+
+int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w, int T, int k,
+                int d, const void* shared_y, void* out, hipStream_t stream) {
+  if (T < 0 || k <= 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxTopK || d % 128) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !slot_dst || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(out) || (shared_y && !aligned16(shared_y)))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, slot_dst, topk_w, T, k, d, shared_y, out, stream));
+}
+
+// Workspace of the whole layer (see carve_layer for the order).
+namespace {
+struct LayerWs {
+  int32_t *ids, *counts, *offsets, *perm_src, *slot_dst, *tok, *rank, *hist;
+  float* w;
+  uint8_t* xq;
+  float* xs;
+  void* y;
+  FfnWs ffn;
+};
+
+void carve_layer(Carver& c, const moe_problem* p, LayerWs& L) {
+  const size_t n = (size_t)p->T * p->top_k;
+  const int E = p->num_experts;
+  L.ids = c.take<int32_t>(n);
+  L.w = c.take<float>(n);
+  L.counts = c.take<int32_t>(E);
+  L.offsets = c.take<int32_t>(E + 1);
+  L.perm_src = c.take<int32_t>(n);
+  L.slot_dst = c.take<int32_t>(n);
+  L.tok = c.take<int32_t>(n);
+  L.rank = c.take<int32_t>(n);
+  L.hist = c.take<int32_t>((size_t)permute_nchunk((int)n) * E);
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3) {
+    L.xq = c.take<uint8_t>((size_t)p->T * p->d_model);
+    L.xs = c.take<float>((size_t)p->T * (p->d_model / 128));
+  } else {
+    L.xq = nullptr;
+    L.xs = nullptr;
+  }
+  carve_ffn(c, p, true, L.ffn);
+  L.y = c.take<uint16_t>(n * p->d_model);
+}
+}  // namespace
+
+size_t moe_layer_workspace_bytes(const moe_problem* p) {
+  if (check_problem(p)) return 0;
+  Carver c{nullptr};
+  LayerWs L;
+  carve_layer(c, p, L);
+  return c.used;
+}
+
+int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
+              void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_problem(p);
+  if (st) return st;
+  st = check_weights(p, w, true);
+  if (st) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!logits || !x || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_layer_workspace_bytes(p);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  Carver c{static_cast<uint8_t*>(ws)};
+  LayerWs L;
+  carve_layer(c, p, L);
+  const int T = p->T, E = p->num_experts, k = p->top_k, d = p->d_model;
+  const int fp8 = p->wdtype == MOE_DTYPE_FP8_E4M3;
+  int32_t* ids = (keep && keep->topk_ids) ? keep->topk_ids : L.ids;
+  float* wts = (keep && keep->topk_w) ? keep->topk_w : L.w;
+  int32_t* counts = (keep && keep->counts) ? keep->counts : L.counts;
+  int32_t* offsets = (keep && keep->offsets) ? keep->offsets : L.offsets;
+  int32_t* perm_src = (keep && keep->perm_src) ? keep->perm_src : L.perm_src;
+  int32_t* slot_dst = (keep && keep->slot_dst) ? keep->slot_dst : L.slot_dst;
+
+  hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
+  if (e == hipSuccess)
+    e = launch_permute(ids, T, E, k, counts, offsets, perm_src, slot_dst, L.tok, L.rank, L.hist,
+                       stream);
+  if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.counts = counts;
+  a.offsets = offsets;
+  a.E = E;
+  a.T = T;
+  a.k = k;
+  a.d = d;
+  a.f = p->d_ff;
+  a.f_sh = p->has_shared ? p->d_ff_shared : 0;
+  a.has_shared = p->has_shared;
+  a.config = p->config;
+  a.fp8 = fp8;
+  a.x = fp8 ? static_cast<const void*>(L.xq) : x;
+  a.xs = L.xs;
+  a.tok = L.tok;
+  a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+  a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
+  a.sh_gate = w->sh_gate; a.sh_up = w->sh_up; a.sh_down = w->sh_down;
+  a.s_sh_gate = w->s_sh_gate; a.s_sh_up = w->s_sh_up; a.s_sh_down = w->s_sh_down;
+  a.h = L.ffn.h; a.hs = L.ffn.hs;
+  a.h_sh = L.ffn.h_sh; a.hs_sh = L.ffn.hs_sh;
+  a.y = L.y; a.y_sh = L.ffn.y_sh;
+  SelectOut o{L.ffn.segs, L.ffn.meta};
+  e = launch_select(a, o, stream);
+  if (e == hipSuccess) e = launch_gemms(o, fp8, stream);
+  if (e == hipSuccess)
+    e = launch_combine(L.y, slot_dst, wts, T, k, d, p->has_shared ? L.ffn.y_sh : nullptr, out,
+                       stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

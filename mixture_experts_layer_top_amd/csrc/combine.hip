@@ -1,0 +1,59 @@
+// Combine: gate-weighted gather-reduce back to token order (GC-MoE, summary: the combine step that
+// follows the grouped GEMMs).  out[t] = bf16(sum_{j<k} w[t][j] * y[slot_dst[t*k+j]] (+ shared[t])),
+// accumulated in fp32 in increasing j with the shared row last: deterministic, no atomics.
+// Each thread owns 8 consecutive channels (16-byte loads and stores); grid = (d/2048 blocks, T).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ slot_dst,
+                                                      const float* __restrict__ w, int k, int d,
+                                                      const uint16_t* __restrict__ sh,
+                                                      uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= d) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int row = slot_dst[(size_t)t * k + j];
+    const float wj = w[(size_t)t * k + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)row * d + c);
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wj * bf16_to_f32(uint16_t(p[i] & 0xFFFF));
+      acc[2 * i + 1] += wj * bf16_to_f32(uint16_t(p[i] >> 16));
+    }
+  }
+  if (sh) {
+    const uint4 v = *reinterpret_cast<const uint4*>(sh + (size_t)t * d + c);
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(uint16_t(p[i] & 0xFFFF));
+      acc[2 * i + 1] += bf16_to_f32(uint16_t(p[i] >> 16));
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = o;
+}
+
+hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
+                          int d, const void* shared_y, void* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((d / 8 + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(y), slot_dst, w, k, d,
+                                      static_cast<const uint16_t*>(shared_y),
+                                      static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace moe

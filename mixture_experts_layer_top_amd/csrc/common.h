@@ -1,0 +1,61 @@
+// Internal helpers shared by the HIP kernels of the MoE layer (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern <-> float (bf16 is the high half of an fp32).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// SiLU(g) * u in fp32.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// MFMA wrappers.  Operand convention used throughout: the first operand ("A", MFMA rows i) holds
+// weight rows, the second ("B", MFMA columns j) holds token rows; both are K-contiguous fragments.
+//   16x16x32 bf16: lane l holds 8 bf16 of row/column (l % 16); C: lane l holds C[4*(l/16)+r][l%16].
+//   32x32x16 bf16: lane l holds 8 bf16 of row/column (l % 32);
+//                  C: lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15.
+//   16x16x128 fp8: lane l holds 32 e4m3 bytes of row/column (l % 16); C as 16x16x32.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// fp8 x fp8 (both OCP e4m3, format code 0), unit E8M0 scales (127 = 2^0).
+__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Tile descriptors written by the selection kernel and read by the GEMM kernels.
+struct Tile {
+  int32_t expert;  // expert index (E = the shared expert)
+  int32_t m0;      // first row inside the expert's segment
+  int32_t n0;      // first output column (weight row)
+  int32_t rows;    // rows of this tile (<= the tile height)
+};
+
+}  // namespace moe

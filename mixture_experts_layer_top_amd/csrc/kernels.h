@@ -1,0 +1,75 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tile families of the expert GEMMs.
+enum Family { kFamStream = 0, kFamMfma = 1, kNumFam = 2 };
+enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
+
+constexpr int kStreamMaxRows = 64;  // rows per weight-streaming tile
+constexpr int kMfmaBM = 128;        // rows per LDS-tiled MFMA tile
+constexpr int kMfmaBN = 128;        // output columns per LDS-tiled MFMA tile
+constexpr int kStreamBN = 64;       // output columns per weight-streaming tile (4 waves x 16)
+constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
+
+// One expert's share of one grouped GEMM: out[row0 + r][n] for r < rows, n < N, from activation
+// rows (gathered through `tok` when it is not null) and the expert's [N][K] weights.
+struct Seg {
+  const void* a;        // activation base ([.][K], bf16 or e4m3)
+  const int32_t* tok;   // row -> activation row (null: row0 + r)
+  const float* as;      // fp8: activation scales [.][K/128]
+  const void* w0;       // gate (gate/up GEMM) or down weights, [N][K]
+  const void* w1;       // up weights (gate/up GEMM), [N][K]
+  const float* s0;      // fp8 block scales of w0, [N/128][K/128]
+  const float* s1;      // fp8 block scales of w1
+  void* out;            // output base [.][N] (bf16, or e4m3 for the fp8 gate/up GEMM)
+  float* outs;          // fp8 gate/up: output scales [.][N/128]
+  int32_t row0, rows, N, K;
+  int32_t tile_base, mtiles, ntiles, expert;
+};
+
+// Where the selection kernel writes its results (all inside the caller's workspace).
+struct SelectOut {
+  Seg* segs;        // [2 gemms][kNumFam][E + 1]
+  int32_t* meta;    // [2 gemms][kNumFam] { nseg, ntiles, queue } -> 3 ints each, 16 entries padded
+};
+
+// Everything the selection kernel needs to describe the two GEMMs.
+struct SelectArgs {
+  const int32_t* counts;   // [E]
+  const int32_t* offsets;  // [E + 1]
+  int E, T, k, d, f, f_sh, has_shared, config, fp8;
+  const void* x;           // gate/up activations (bf16 x, or e4m3 xq)
+  const float* xs;         // fp8 activation scales
+  const int32_t* tok;      // row -> token, for routed rows (null: rows are already permuted)
+  const void* w_gate; const void* w_up; const void* w_down;
+  const float* s_gate; const float* s_up; const float* s_down;
+  const void* sh_gate; const void* sh_up; const void* sh_down;
+  const float* s_sh_gate; const float* s_sh_up; const float* s_sh_down;
+  void* h; float* hs;      // routed gate/up output [T*k][f] (+ fp8 scales [T*k][f/128])
+  void* h_sh; float* hs_sh;  // shared gate/up output [T][f_sh]
+  void* y; void* y_sh;     // down outputs [T*k][d], [T][d]
+};
+
+constexpr int kMetaStride = 4;  // ints per (gemm, family): nseg, ntiles, queue, pad
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+int permute_nchunk(int n);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_src, int32_t* slot_dst, int32_t* tok,
+                          int32_t* rank_ws, int32_t* hist_ws, hipStream_t s);
+hipError_t launch_gather(const void* x, const float* xs, const int32_t* perm_src, int n, int k,
+                         int row_bytes, int nb, void* xp, float* xps, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, const SelectOut& o, hipStream_t s);
+hipError_t launch_gemms_bf16(const SelectOut& o, int num_cus, hipStream_t s);
+hipError_t launch_gemms_fp8(const SelectOut& o, int num_cus, hipStream_t s);
+hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
+                          int d, const void* shared_y, void* out, hipStream_t s);
+hipError_t launch_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,166 @@
+// Dispatch, single-GPU share: expert histogram, exclusive prefix sum, stable counting sort of the
+// slots s = t*k + j into expert-contiguous rows, and the row gather.
+//
+// "Decoding the Skew ..." (Abstract) drives kernel choice from the live routing histogram; GC-MoE
+// (summary) and Weave (Abstract) place token dispatch before the grouped GEMMs.  The layout here is
+// unpadded: expert e owns rows [offsets[e], offsets[e+1]).
+//
+// Deterministic without float atomics and without a host sync:
+//   count   : one workgroup per chunk of 2048 slots, processed as 8 rounds of 256 in slot order.
+//             Inside a wavefront, lanes with the same expert are found with 9 ballots over the id
+//             bits; a lane's rank is the popcount of equal lanes below it, plus the counts of the
+//             earlier wavefronts and rounds of the chunk (LDS).  Writes rank[s] and the chunk's
+//             histogram.
+//   scan    : one workgroup; per expert, chunk histograms -> chunk base rows; counts; offsets.
+//   scatter : row = chunk_base[chunk][e] + rank[s]; perm_src[row] = s; slot_dst[s] = row;
+//             tok[row] = t (the activation row the GEMM gathers).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kChunk = 2048;
+constexpr int kMaxE = 512;
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ ids, int n,
+                                                         int E, int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ chunk_hist) {
+  __shared__ int running[kMaxE];
+  __shared__ int wcnt[4][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < E; e += 256) {
+    running[e] = 0;
+    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
+  }
+  __syncthreads();
+  const int base = blockIdx.x * kChunk;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < kChunk / 256; ++r) {
+    const int s = base + r * 256 + tid;
+    const bool valid = s < n;
+    const int e = valid ? ids[s] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int rank_w = __popcll(same & below);
+    const int cnt_w = __popcll(same);
+    const bool leader = valid && rank_w == 0;
+    if (leader) wcnt[wv][e] = cnt_w;
+    __syncthreads();
+    if (valid) {
+      int rk = running[e] + rank_w;
+      for (int w = 0; w < wv; ++w) rk += wcnt[w][e];
+      rank[s] = rk;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&running[e], cnt_w);
+      wcnt[wv][e] = 0;
+    }
+    __syncthreads();
+  }
+  int32_t* hist = chunk_hist + (size_t)blockIdx.x * E;
+  for (int e = tid; e < E; e += 256) hist[e] = running[e];
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_hist,
+                                                         int nchunk, int E, int n,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int tot[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunk; ++c) {
+      const int h = chunk_hist[(size_t)c * E + e];
+      chunk_hist[(size_t)c * E + e] = total;
+      total += h;
+    }
+    counts[e] = total;
+  }
+  tot[e] = (e < E) ? total : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1024 entries.
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = (e >= off) ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int excl = tot[e] - total;
+    offsets[e] = excl;
+    for (int c = 0; c < nchunk; ++c) chunk_hist[(size_t)c * E + e] += excl;
+  }
+  if (e == 0) offsets[E] = n;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ rank,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int n, int E, int k,
+                                                           int32_t* __restrict__ perm_src,
+                                                           int32_t* __restrict__ slot_dst,
+                                                           int32_t* __restrict__ tok) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= n) return;
+  const int e = ids[s];
+  const int row = chunk_base[(size_t)(s / kChunk) * E + e] + rank[s];
+  if (perm_src) perm_src[row] = s;
+  if (slot_dst) slot_dst[s] = row;
+  if (tok) tok[row] = s / k;
+}
+
+// x_perm[row] = x[tok[row]]: `bytes` per row, 16-byte vectors; one workgroup per 4 rows.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm_src,
+                                                          int n, int k, int bytes,
+                                                          uint8_t* __restrict__ xp) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const int t = perm_src[row] / k;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * bytes);
+  uint4* dst = reinterpret_cast<uint4*>(xp + (size_t)row * bytes);
+  for (int i = threadIdx.x & 63; i < bytes / 16; i += 64) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ xs,
+                                                            const int32_t* __restrict__ perm_src,
+                                                            int n, int k, int nb,
+                                                            float* __restrict__ xps) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * nb) return;
+  const int row = i / nb, b = i % nb;
+  xps[i] = xs[(size_t)(perm_src[row] / k) * nb + b];
+}
+
+int permute_nchunk(int n) { return (n + kChunk - 1) / kChunk; }
+
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_src, int32_t* slot_dst, int32_t* tok,
+                          int32_t* rank_ws, int32_t* hist_ws, hipStream_t s) {
+  const int n = T * k;
+  const int nchunk = permute_nchunk(n);
+  if (n > 0) perm_count_kernel<<<nchunk, 256, 0, s>>>(ids, n, E, rank_ws, hist_ws);
+  perm_scan_kernel<<<1, 1024, 0, s>>>(hist_ws, nchunk, E, n, counts, offsets);
+  if (n > 0)
+    perm_scatter_kernel<<<(n + 255) / 256, 256, 0, s>>>(ids, rank_ws, hist_ws, n, E, k, perm_src,
+                                                        slot_dst, tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* x, const float* xs, const int32_t* perm_src, int n, int k,
+                         int row_bytes, int nb, void* xp, float* xps, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  gather_rows_kernel<<<(n + 3) / 4, 256, 0, s>>>(static_cast<const uint8_t*>(x), perm_src, n, k,
+                                                 row_bytes, static_cast<uint8_t*>(xp));
+  if (xs && xps)
+    gather_scales_kernel<<<(n * nb + 255) / 256, 256, 0, s>>>(xs, perm_src, n, k, nb, xps);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+"""Thin Python binding of libmoe_mi355x.so (the C ABI in include/moe_mi355x.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.  torch is
+used for device memory (output and workspace tensors) and for the current HIP stream.  If the
+library is not built this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+DTYPE_BF16, DTYPE_FP8 = 0, 1
+CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA128, CONFIG_MFMA256 = -1, 0, 1, 2
+
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("has_shared", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("config", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+        "sh_gate", "sh_up", "sh_down", "s_sh_gate", "s_sh_up", "s_sh_down")]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_ids", "topk_w", "counts", "offsets", "perm_src", "slot_dst")]
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the library (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoEError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_top_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_route": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
+            "moe_permute": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]),
+            "moe_permute_workspace_bytes": (_sz, [_i, _i, _i]),
+            "moe_quant_act": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+            "moe_grouped_ffn": (_i, [ctypes.POINTER(Problem), _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(Weights), _vp, _vp, _sz, _vp]),
+            "moe_grouped_ffn_workspace_bytes": (_sz, [ctypes.POINTER(Problem)]),
+            "moe_combine": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+            "moe_layer": (_i, [ctypes.POINTER(Problem), _vp, _vp, ctypes.POINTER(Weights), _vp,
+                               ctypes.POINTER(Routing), _vp, _sz, _vp]),
+            "moe_layer_workspace_bytes": (_sz, [ctypes.POINTER(Problem)]),
+            "moe_status_string": (ctypes.c_char_p, [_i]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
+            "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
+            "moe_layer_workspace_bytes", "moe_status_string")
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        raise MoEError(f"{what}: {lib().moe_status_string(status).decode()}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise MoEError("tensors must live on the GPU")
+    return t.device
+
+
+@dataclass
+class ExpertWeights:
+    """Device tensors of the expert weights in the library's storage layout."""
+    gate: torch.Tensor
+    up: torch.Tensor
+    down: torch.Tensor
+    s_gate: torch.Tensor | None = None
+    s_up: torch.Tensor | None = None
+    s_down: torch.Tensor | None = None
+    sh_gate: torch.Tensor | None = None
+    sh_up: torch.Tensor | None = None
+    sh_down: torch.Tensor | None = None
+    s_sh_gate: torch.Tensor | None = None
+    s_sh_up: torch.Tensor | None = None
+    s_sh_down: torch.Tensor | None = None
+
+    def struct(self) -> Weights:
+        w = Weights()
+        for name, _ in Weights._fields_:
+            key = {"w_gate": "gate", "w_up": "up", "w_down": "down"}.get(name, name)
+            setattr(w, name, _ptr(getattr(self, key)))
+        return w
+
+    @property
+    def fp8(self) -> bool:
+        return self.gate.dtype == torch.uint8
+
+    @property
+    def has_shared(self) -> bool:
+        return self.sh_gate is not None
+
+
+def problem(T, d, f, E, k, fp8=False, shared_f=0, config=CONFIG_AUTO) -> Problem:
+    return Problem(T, d, f, E, k, DTYPE_FP8 if fp8 else DTYPE_BF16, 1 if shared_f else 0,
+                   shared_f, config)
+
+
+# ------------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------------
+
+def route(logits: torch.Tensor, k: int):
+    T, E = logits.shape
+    dev = _dev(logits)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream()), "moe_route")
+    return ids, w
+
+
+def permute(ids: torch.Tensor, E: int, x: torch.Tensor | None = None,
+            x_scale: torch.Tensor | None = None):
+    """Returns counts, offsets, perm_src, slot_dst (and x_perm, x_perm_scale if x is given).
+    x: bf16 [T, d] as int16 bits, or e4m3 [T, d] uint8 (with x_scale [T, d/128])."""
+    T, k = ids.shape
+    dev = _dev(ids)
+    n = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm_src = torch.empty(n, dtype=torch.int32, device=dev)
+    slot_dst = torch.empty(n, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, lib().moe_permute_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+    xp = xps = None
+    d = 0
+    act = DTYPE_BF16
+    if x is not None:
+        d = x.shape[1]
+        act = DTYPE_FP8 if x.dtype == torch.uint8 else DTYPE_BF16
+        xp = torch.empty((n, d), dtype=x.dtype, device=dev)
+        if x_scale is not None:
+            xps = torch.empty((n, d // 128), dtype=torch.float32, device=dev)
+    _check(lib().moe_permute(_ptr(ids), T, E, k, _ptr(x), _ptr(x_scale), d, act, _ptr(counts),
+                             _ptr(offsets), _ptr(perm_src), _ptr(slot_dst), _ptr(xp), _ptr(xps),
+                             _ptr(ws), ws.numel(), _stream()), "moe_permute")
+    return counts, offsets, perm_src, slot_dst, xp, xps
+
+
+def quant_act(x: torch.Tensor):
+    T, d = x.shape
+    dev = _dev(x)
+    xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+    _check(lib().moe_quant_act(_ptr(x), T, d, _ptr(xq), _ptr(xs), _stream()), "moe_quant_act")
+    return xq, xs
+
+
+def grouped_ffn(x_perm, x_perm_scale, counts, offsets, weights: ExpertWeights, T: int, k: int,
+                config: int = CONFIG_AUTO):
+    n, d = x_perm.shape
+    E = counts.shape[0]
+    f = weights.gate.shape[1]
+    p = problem(T, d, f, E, k, fp8=weights.fp8, config=config)
+    dev = _dev(x_perm)
+    y = torch.empty((n, d), dtype=torch.int16, device=dev)
+    ws = torch.empty(max(1, lib().moe_grouped_ffn_workspace_bytes(ctypes.byref(p))),
+                     dtype=torch.uint8, device=dev)
+    w = weights.struct()
+    _check(lib().moe_grouped_ffn(ctypes.byref(p), _ptr(x_perm), _ptr(x_perm_scale), _ptr(counts),
+                                 _ptr(offsets), ctypes.byref(w), _ptr(y), _ptr(ws), ws.numel(),
+                                 _stream()), "moe_grouped_ffn")
+    return y
+
+
+def combine(y_perm, slot_dst, topk_w, shared_y=None):
+    T, k = topk_w.shape
+    d = y_perm.shape[1]
+    out = torch.empty((T, d), dtype=torch.int16, device=_dev(y_perm))
+    _check(lib().moe_combine(_ptr(y_perm), _ptr(slot_dst), _ptr(topk_w), T, k, d, _ptr(shared_y),
+                             _ptr(out), _stream()), "moe_combine")
+    return out
+
+
+class Layer:
+    """The whole layer with a workspace kept between calls (no allocation per call)."""
+
+    def __init__(self, weights: ExpertWeights, T: int, E: int, k: int, config: int = CONFIG_AUTO,
+                 device=None):
+        d = weights.gate.shape[2]
+        f = weights.gate.shape[1]
+        shf = weights.sh_gate.shape[0] if weights.has_shared else 0
+        self.weights = weights
+        self.p = problem(T, d, f, E, k, fp8=weights.fp8, shared_f=shf, config=config)
+        self.w = weights.struct()
+        dev = device if device is not None else weights.gate.device
+        self.ws = torch.empty(max(1, lib().moe_layer_workspace_bytes(ctypes.byref(self.p))),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, d), dtype=torch.int16, device=dev)
+
+    def __call__(self, logits, x, keep: dict | None = None, out=None):
+        r = Routing()
+        if keep:
+            for name in keep:
+                setattr(r, name, _ptr(keep[name]))
+        out = self.out if out is None else out
+        _check(lib().moe_layer(ctypes.byref(self.p), _ptr(logits), _ptr(x), ctypes.byref(self.w),
+                               _ptr(out), ctypes.byref(r), _ptr(self.ws), self.ws.numel(),
+                               _stream()), "moe_layer")
+        return out
+
+
+def layer(logits, x, weights: ExpertWeights, k: int, config: int = CONFIG_AUTO, keep_routing=False):
+    """One call of the whole layer; returns out (bf16 bits, int16) and optionally the routing."""
+    T, E = logits.shape
+    L = Layer(weights, T, E, k, config)
+    keep = None
+    if keep_routing:
+        dev = logits.device
+        n = T * k
+        keep = dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                    topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                    counts=torch.empty(E, dtype=torch.int32, device=dev),
+                    offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                    perm_src=torch.empty(n, dtype=torch.int32, device=dev),
+                    slot_dst=torch.empty(n, dtype=torch.int32, device=dev))
+    out = L(logits, x, keep)
+    return (out, keep) if keep_routing else out

@@ -1,0 +1,67 @@
+"""Shared test plumbing: input upload, oracle weight access, comparisons."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from mixture_experts_layer_top_amd import inputs as I
+
+BF16_TOL = 2e-2
+FP8_TOL = 6e-2
+
+
+def bits_to_f64(t) -> np.ndarray:
+    """bf16 bit patterns (int16 tensor / uint16 array) -> float64 (test-side decode)."""
+    a = t.cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
+    return (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Inputs:
+    """One workload's inputs: numpy copies for the oracle, device tensors for the library."""
+
+    def __init__(self, p: I.Problem, device="cuda", weights=None):
+        self.p = p
+        self.logits = I.gen_logits(p)
+        self.x = I.gen_x(p)
+        self.W = weights if weights is not None else I.gen_weights(p, device)
+        self.d_logits = torch.from_numpy(self.logits).to(device)
+        self.d_x = torch.from_numpy(self.x.view(np.int16)).to(device)
+        self._cache = {}
+
+    def expert_weights(self):
+        from mixture_experts_layer_top_amd.moe import ExpertWeights
+        W = self.W
+        kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
+        if self.p.wdtype == I.WDT_FP8:
+            kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
+        if self.p.shared:
+            kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
+            if self.p.wdtype == I.WDT_FP8:
+                kw.update(s_sh_gate=W["s_sh_gate"], s_sh_up=W["s_sh_up"], s_sh_down=W["s_sh_down"])
+        return ExpertWeights(**kw)
+
+    # The oracle reads the generator's weight bytes.  On a GPU machine they were generated there by the
+    # same device-independent generator (tests check CPU == GPU generation bit for bit), and are
+    # copied back per expert; no HIP-library output is involved.
+    def get(self, e):
+        if e not in self._cache:
+            r = {n: self.W[n][e].cpu().numpy() for n in ("gate", "up", "down")}
+            if self.p.wdtype == I.WDT_FP8:
+                r.update({"s_" + n: self.W["s_" + n][e].cpu().numpy() for n in ("gate", "up", "down")})
+            if len(self._cache) > 24:
+                self._cache.clear()
+            self._cache[e] = r
+        return self._cache[e]
+
+    def get_shared(self):
+        if not self.p.shared:
+            return None
+        r = {n: self.W["sh_" + n].cpu().numpy() for n in ("gate", "up", "down")}
+        if self.p.wdtype == I.WDT_FP8:
+            r.update({"s_" + n: self.W["s_sh_" + n].cpu().numpy() for n in ("gate", "up", "down")})
+        return r
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    m = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (m if m > 0 else 1.0))

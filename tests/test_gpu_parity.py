@@ -1,0 +1,203 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU fp64 oracle on the same seeded
+inputs.  Routing, counts, offsets and permutations must match bit for bit; topk_w within 2e-6;
+outputs within 2e-2 * max|ref| (bf16 weights) or 6e-2 * max|ref| (fp8 weights)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_top_amd import inputs as I
+from oracle import moe_oracle as O
+
+from helpers import BF16_TOL, FP8_TOL, Inputs, bits_to_f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_top_amd import moe as m
+    m.lib()
+    return m
+
+
+def _small(name, **kw):
+    base = dict(cfg_index=100, T=64, d=256, f=512, E=8, k=2)
+    base.update(kw)
+    return I.Problem(name, **base)
+
+
+# ------------------------------------------------------------------------------------------------
+# route
+# ------------------------------------------------------------------------------------------------
+
+ROUTE_CASES = [(64, 8, 2), (300, 1, 1), (257, 64, 8), (100, 65, 3), (64, 256, 8), (33, 384, 8),
+               (17, 512, 8), (50, 8, 8), (4096, 8, 2)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+def test_route_random(moe, T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = moe.route(torch.from_numpy(L).cuda(), k)
+    rids, rw = O.route(L, k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 2e-6
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (256, 8), (384, 8), (512, 5)])
+def test_route_planted_ties(moe, E, k):
+    rng = np.random.default_rng(E)
+    L = rng.integers(-2, 3, size=(200, E)).astype(np.float32)
+    L[::7] = 0.0
+    L[1::7] = -0.0
+    L[2::7, ::2] = -0.0
+    ids, w = moe.route(torch.from_numpy(L).cuda(), k)
+    rids, rw = O.route(L, k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 2e-6
+
+
+@pytest.mark.parametrize("T,alpha", [(1, 0.1), (16, 1.0), (64, 10.0), (256, 0.1)])
+def test_route_dirichlet_workloads(moe, T, alpha):
+    p = I.dsv3_point(T, alpha)
+    L = I.gen_logits(p)
+    ids, w = moe.route(torch.from_numpy(L).cuda(), p.k)
+    rids, rw = O.route(L, p.k)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 2e-6
+
+
+# ------------------------------------------------------------------------------------------------
+# permute
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (64, 8, 2), (1000, 16, 4), (2048, 256, 8),
+                                   (8192, 384, 8), (3, 512, 8), (700, 1, 1)])
+def test_permute_bit_exact(moe, T, E, k):
+    rng = np.random.default_rng(T + E)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:, :3] += 2.0  # skew: some experts heavy, several tails
+    rids, _ = O.route(L, k)
+    x = rng.integers(-30000, 30000, size=(T, 128)).astype(np.int16)
+    counts, offsets, perm_src, slot_dst, xp, _ = moe.permute(
+        torch.from_numpy(rids).cuda(), E, torch.from_numpy(x).cuda())
+    rc, ro = O.histogram(rids, E)
+    rps, rsd = O.permute(rids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm_src.cpu().numpy(), rps)
+    assert np.array_equal(slot_dst.cpu().numpy(), rsd)
+    assert np.array_equal(xp.cpu().numpy(), x[rps // k])
+
+
+# ------------------------------------------------------------------------------------------------
+# combine and grouped FFN, each fed with the oracle's own intermediates
+# ------------------------------------------------------------------------------------------------
+
+def test_combine_matches_oracle(moe):
+    rng = np.random.default_rng(3)
+    T, E, k, d = 77, 16, 4, 384
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    rids, rw = O.route(L, k)
+    _, rsd = O.permute(rids, E)
+    y = I.f32_to_bf16_bits(rng.standard_normal((T * k, d)).astype(np.float32))
+    sh = I.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w32 = rw.astype(np.float32)
+    for shared in (None, sh):
+        out = moe.combine(torch.from_numpy(y.view(np.int16)).cuda(),
+                          torch.from_numpy(rsd.astype(np.int32)).cuda(),
+                          torch.from_numpy(w32).cuda(),
+                          None if shared is None else torch.from_numpy(shared.view(np.int16)).cuda())
+        S = None if shared is None else bits_to_f64(shared)
+        ref = O.combine(bits_to_f64(y), rsd, w32.astype(np.float64), S)
+        got = bits_to_f64(out)
+        # one bf16 rounding of an fp32 sum: within 2^-8 relative (plus fp32 summation noise)
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
+
+GFFN = [
+    _small("gffn_tiny"),
+    _small("gffn_ragged", T=300, d=384, f=640, E=6, k=2, cfg_index=101),
+    _small("gffn_one", T=5, d=128, f=128, E=3, k=1, cfg_index=102),
+    _small("gffn_skew", T=200, d=256, f=256, E=40, k=4, routing="dirichlet", alpha=0.1, cfg_index=103),
+]
+
+
+@pytest.mark.parametrize("config", [-1, 0, 1])
+@pytest.mark.parametrize("p", GFFN, ids=lambda p: p.name)
+def test_grouped_ffn_matches_oracle(moe, p, config):
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    x_perm = inp.x[perm_src // p.k]
+    y = moe.grouped_ffn(torch.from_numpy(x_perm.view(np.int16)).cuda(), None,
+                        torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k, config=config)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get)["y_perm"]
+    got = bits_to_f64(y)
+    assert rel_err(got, ref) <= BF16_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# the whole layer
+# ------------------------------------------------------------------------------------------------
+
+LAYER = [
+    I.TINY,
+    _small("layer_ragged", T=300, d=384, f=640, E=6, k=2, cfg_index=104),
+    _small("layer_e1k1", T=40, d=256, f=384, E=1, k=1, cfg_index=105),
+    _small("layer_skew", T=333, d=256, f=512, E=48, k=6, routing="dirichlet", alpha=0.1, cfg_index=106),
+    _small("layer_T1", T=1, d=512, f=256, E=16, k=4, routing="dirichlet", alpha=1.0, cfg_index=107),
+    _small("layer_big_expert", T=700, d=128, f=256, E=4, k=1, routing="dirichlet", alpha=0.1,
+           cfg_index=108),
+]
+
+
+def _check_layer(moe, inp, config=-1, tol=BF16_TOL, runs=1):
+    p = inp.p
+    out, keep = moe.layer(inp.d_logits, inp.d_x, inp.expert_weights(), p.k, config=config,
+                          keep_routing=True)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, inp.get_shared(), act_fp8=p.wdtype == I.WDT_FP8)
+    assert np.array_equal(keep["topk_ids"].cpu().numpy(), ref["ids"])
+    assert np.abs(keep["topk_w"].cpu().numpy() - ref["w"]).max() <= 2e-6
+    assert np.array_equal(keep["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(keep["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(keep["perm_src"].cpu().numpy(), ref["perm_src"])
+    assert np.array_equal(keep["slot_dst"].cpu().numpy(), ref["slot_dst"])
+    err = rel_err(bits_to_f64(out), ref["out"])
+    assert err <= tol, err
+    first = out.clone()
+    for _ in range(runs - 1):
+        again = moe.layer(inp.d_logits, inp.d_x, inp.expert_weights(), p.k, config=config)
+        assert torch.equal(again, first)  # bitwise deterministic
+    return err
+
+
+@pytest.mark.parametrize("config", [-1, 0, 1])
+@pytest.mark.parametrize("p", LAYER, ids=lambda p: p.name)
+def test_layer_matches_oracle(moe, p, config):
+    _check_layer(moe, Inputs(p), config=config, runs=2)
+
+
+def test_generator_device_independent(moe):
+    for p, which, e in ((I.TINY, "gate", 3), (I.DSV3, "down", 200), (I.FP8, "up", 7)):
+        a = I.gen_expert_weight(p, which, e, "cpu")
+        b = I.gen_expert_weight(p, which, e, "cuda").cpu()
+        assert torch.equal(a, b)
+    a = I.gen_expert_scales(I.FP8, "down", 5, "cpu")
+    b = I.gen_expert_scales(I.FP8, "down", 5, "cuda").cpu()
+    assert torch.equal(a, b)
+
+
+def test_t0_is_noop(moe):
+    p = I.TINY
+    W = Inputs(p).expert_weights()
+    L = moe.Layer(W, 0, p.E, p.k)
+    out = L(torch.empty((0, p.E), device="cuda"), torch.empty((0, p.d), dtype=torch.int16, device="cuda"))
+    assert out.shape == (0, p.d)
