@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T T] [--alpha A]
+
+One step = one call of the whole layer (route -> permute -> [fp8 activation quantisation] ->
+tile selection -> gate/up GEMM + SwiGLU -> down GEMM -> combine) on one batch of synthetic inputs
+already resident in HBM.  The default workload is the Mixtral-8x7B-shaped prefill layer
+(T=4096, d=4096, f=14336, E=8, k=2, bf16).  Prints one JSON line with tokens/s, the roofline of the
+dominant kernel (timed with HIP events on the stream the library launches on) and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % HBM peak (decode) / % MFMA peak (prefill), 1 GPU"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense MFMA bf16
+PEAK_FP8_TFLOPS = 5000.0       # dense MFMA fp8
+PREFILL_MIN_T = 4096           # prefill workloads are judged against MFMA, decode against HBM
+
+
+def workload(args):
+    from mixture_experts_layer_top_amd import inputs as I
+    name = args.config
+    if name == "tiny":
+        return I.TINY
+    if name == "mixtral_prefill":
+        return I.MIXTRAL
+    if name == "kimi_prefill":
+        return I.KIMI
+    if name == "dsv3_decode":
+        return I.dsv3_point(args.T or 256, args.alpha if args.alpha is not None else 1.0)
+    if name == "fp8_dsv3_decode":
+        return I.fp8_point(args.T or 128)
+    raise SystemExit(f"unknown --config {name}")
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic(p, n_active: int):
+    """FLOPs and bytes the layer must move (only experts with rows count; intermediates such as
+    the permuted rows, h and y are implementation overhead and are not credited)."""
+    wb = 1 if p.wdtype == "fp8" else 2
+    sh_f = p.shared_f if p.shared else 0
+    flop_gu = 4.0 * p.d * (p.f * p.T * p.k + sh_f * p.T)
+    flop_dn = 2.0 * p.d * (p.f * p.T * p.k + sh_f * p.T)
+    w_gu = n_active * 2.0 * p.f * p.d * wb + (2.0 * sh_f * p.d * wb if p.shared else 0.0)
+    w_dn = n_active * 1.0 * p.f * p.d * wb + (1.0 * sh_f * p.d * wb if p.shared else 0.0)
+    if p.wdtype == "fp8":
+        w_gu += (n_active * 2 * p.f * p.d + (2 * sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
+        w_dn += (n_active * p.f * p.d + (sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
+    x_bytes = p.T * p.d * 2.0
+    out_bytes = p.T * p.d * 2.0
+    logit_bytes = p.T * p.E * 4.0
+    return dict(flop=flop_gu + flop_dn, flop_gu=flop_gu, flop_dn=flop_dn,
+                bytes=w_gu + w_dn + x_bytes + out_bytes + logit_bytes,
+                bytes_gu=w_gu + x_bytes, bytes_dn=w_dn + out_bytes)
+
+
+def cpu_baseline(p, logits, x, W, sample_tokens: int):
+    """The CPU oracle as it stands, timed on the first `sample_tokens` tokens of the same inputs
+    (routing, permutation, experts and combine are row-wise, so this is the same workload at a
+    smaller batch).  Weight bytes are copied to host memory before the clock starts."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = len(os.sched_getaffinity(0))
+    S = min(sample_tokens, p.T)
+    L = logits[:S]
+    xs = x[:S]
+    ids, _ = O.route(L, p.k)
+    needed = sorted(set(int(e) for e in np.unique(ids)))
+    host = {}
+    for e in needed:
+        host[e] = {n: W[n][e].cpu().numpy() for n in ("gate", "up", "down")}
+        if p.wdtype == "fp8":
+            host[e].update({"s_" + n: W["s_" + n][e].cpu().numpy() for n in ("gate", "up", "down")})
+    sh = None
+    if p.shared:
+        sh = {n: W["sh_" + n].cpu().numpy() for n in ("gate", "up", "down")}
+        if p.wdtype == "fp8":
+            sh.update({"s_" + n: W["s_sh_" + n].cpu().numpy() for n in ("gate", "up", "down")})
+    t0 = time.perf_counter()
+    O.moe_layer(L, xs, p.k, lambda e: host[e], (lambda: sh) if sh else None,
+                act_fp8=p.wdtype == "fp8")
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"first {S} of {p.T} tokens of {p.name} ({len(needed)} experts), "
+                      f"float64 numpy/OpenBLAS, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_prefill",
+                    choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode"])
+    ap.add_argument("--T", type=int, default=None, help="tokens (decode workloads)")
+    ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
+    ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite a 512 MiB buffer before every step to evict L2 and the MALL; "
+                         "the value then comes from per-step events around the layer only")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM byte-counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(experts would shard across GPUs with an all-to-all dispatch; not built).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from mixture_experts_layer_top_amd import inputs as I
+    from mixture_experts_layer_top_amd import moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    p = workload(args)
+    print(f"[bench] workload {p.name}: T={p.T} d={p.d} f={p.f} E={p.E} k={p.k} {p.wdtype}"
+          f"{' +shared' if p.shared else ''}", file=sys.stderr, flush=True)
+    t_gen = time.perf_counter()
+    logits = I.gen_logits(p)
+    x = I.gen_x(p)
+    W = I.gen_weights(p, "cuda")
+    d_logits = torch.from_numpy(logits).cuda()
+    d_x = torch.from_numpy(x.view(np.int16)).cuda()
+    kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
+    if p.wdtype == "fp8":
+        kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
+    if p.shared:
+        kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
+        if p.wdtype == "fp8":
+            kw.update(s_sh_gate=W["s_sh_gate"], s_sh_up=W["s_sh_up"], s_sh_down=W["s_sh_down"])
+    ew = moe.ExpertWeights(**kw)
+    layer = moe.Layer(ew, p.T, p.E, p.k, config=args.tile_config)
+    counts = torch.zeros(p.E, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    hip = HipEvents()
+    K, Wm = args.steps, args.warmup
+    evs = [hip.create(moe.TRACE_EVENTS) for _ in range(K)]
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+
+    for i in range(Wm):
+        layer(d_logits, d_x, keep={"counts": counts} if i == 0 else None)
+    torch.cuda.synchronize()
+    if Wm == 0:
+        layer(d_logits, d_x, keep={"counts": counts})
+        torch.cuda.synchronize()
+
+    # Timed region: K steps.  Only the two events around the dominant kernel (gate/up GEMM) are
+    # recorded per step (plus the step's first and last when flushing), since every timing event
+    # costs GPU time.
+    GU0, GU1 = 4, 5
+    keep_idx = {GU0, GU1} | ({0, moe.TRACE_EVENTS - 1} if args.flush else set())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        layer.traced(d_logits, d_x, [e if j in keep_idx else None for j, e in enumerate(evs[i])])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_launch_ms = [hip.elapsed_ms(evs[i][GU0], evs[i][GU1]) for i in range(K)]
+    step_ms = ([hip.elapsed_ms(evs[i][0], evs[i][-1]) for i in range(K)] if args.flush else [])
+
+    # Phase breakdown (not timed): a few more steps with every phase boundary recorded.
+    phases = {name: [] for name in moe.TRACE_PHASES}
+    for i in range(min(K, 5)):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        layer.traced(d_logits, d_x, evs[i])
+    torch.cuda.synchronize()
+    for i in range(min(K, 5)):
+        for j, name in enumerate(moe.TRACE_PHASES):
+            phases[name].append(hip.elapsed_ms(evs[i][j], evs[i][j + 1]))
+    for e in evs:
+        hip.destroy(e)
+
+    n_active = int((counts.cpu() > 0).sum())
+    alg = algorithmic(p, n_active)
+    if args.flush:
+        ms_per_step = statistics.median(step_ms)
+        timing = "median of per-step events around the layer; 512 MiB cache flush before each step"
+    else:
+        ms_per_step = wall * 1e3 / K
+        timing = "wall clock over the timed steps (synchronised before and after)"
+    value = p.T / (ms_per_step * 1e-3)
+
+    prefill = p.T >= PREFILL_MIN_T
+    peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" else PEAK_BF16_TFLOPS
+    gu_ms = statistics.mean(gu_launch_ms)
+    if prefill:
+        achieved = alg["flop_gu"] / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
+    else:
+        achieved = alg["bytes_gu"] / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"kernel": "gate/up grouped GEMM + SwiGLU (both tile families)",
+                 "avg_launch_ms": round(gu_ms, 4), "traffic": None})
+
+    layer_s = ms_per_step * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if p.wdtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "T": p.T, "d_model": p.d, "d_ff": p.f, "experts": p.E,
+                   "top_k": p.k, "routing": p.routing + (f"(alpha={p.alpha:g})" if p.routing == "dirichlet" else ""),
+                   "shared_expert_d_ff": p.shared_f if p.shared else 0, "n_active": n_active,
+                   "tile_config": args.tile_config},
+        "roofline": roof,
+        "layer": {"mfma_frac": round(alg["flop"] / layer_s / 1e12 / peak_flops, 4),
+                  "hbm_frac": round(alg["bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "phase_ms": {k: round(statistics.mean(v), 4) for k, v in phases.items()},
+                  "phase_note": "separate untimed steps with every phase boundary recorded (each "
+                                "timing event adds ~5 us of GPU time)",
+                  "timing": timing},
+    }
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or {"mixtral_prefill": 2048, "kimi_prefill": 512}.get(p.name, p.T)
+        print(f"[bench] CPU oracle on {sample} tokens ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(p, logits, x, W, sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

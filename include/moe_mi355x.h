@@ -159,6 +159,19 @@ int moe_layer(const moe_problem* p, const float* logits, const void* x, const mo
               void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_layer_workspace_bytes(const moe_problem* p);
 
+/* moe_layer with phase timing: records events[0] before the first launch and events[i] after
+ * phase i, for the phases route (1), permute (2), activation quantisation (3, empty for bf16),
+ * tile selection (4), gate/up GEMM + SwiGLU (5), down GEMM (6) and combine (7).  The caller creates
+ * the MOE_TRACE_EVENTS events (hipEventCreate) and reads them after the stream has passed them.
+ * NULL entries are skipped (each recorded timing event adds a few microseconds of GPU time, so
+ * a caller may record only the boundaries it needs).  Same results as moe_layer; num_events must
+ * be MOE_TRACE_EVENTS.  Meant for profiling tools
+ * ("where the time goes": the pages attribute decode time to dispatch and weight traffic). */
+#define MOE_TRACE_EVENTS 8
+int moe_layer_traced(const moe_problem* p, const float* logits, const void* x,
+                     const moe_weights* w, void* out, const moe_routing* keep, void* ws,
+                     size_t ws_bytes, hipEvent_t* events, int num_events, hipStream_t stream);
+
 /* Static name of a status code. */
 const char* moe_status_string(int status);
 

@@ -115,8 +115,9 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
   }
 }
 
-hipError_t launch_gemms(const SelectOut& o, int fp8, hipStream_t s) {
-  return fp8 ? moe::launch_gemms_fp8(o, device_cus(), s) : moe::launch_gemms_bf16(o, device_cus(), s);
+hipError_t launch_gemms(const SelectOut& o, int gemm, int fp8, hipStream_t s) {
+  return fp8 ? moe::launch_gemms_fp8(o, gemm, device_cus(), s)
+             : moe::launch_gemms_bf16(o, gemm, device_cus(), s);
 }
 }  // namespace
 
@@ -237,8 +238,9 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.y = y_perm;
   SelectOut o{f.segs, f.meta};
   hipError_t e = launch_select(a, o, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_gemms(o, fp8, stream));
+  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, stream);
+  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, stream);
+  return hip_status(e);
 }
 
 int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w, int T, int k,
@@ -295,8 +297,10 @@ size_t moe_layer_workspace_bytes(const moe_problem* p) {
   return c.used;
 }
 
-int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
-              void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+int layer_impl(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
+               void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipEvent_t* ev,
+               hipStream_t stream) {
   int st = check_problem(p);
   if (st) return st;
   st = check_weights(p, w, true);
@@ -318,11 +322,18 @@ int moe_layer(const moe_problem* p, const float* logits, const void* x, const mo
   int32_t* perm_src = (keep && keep->perm_src) ? keep->perm_src : L.perm_src;
   int32_t* slot_dst = (keep && keep->slot_dst) ? keep->slot_dst : L.slot_dst;
 
-  hipError_t e = launch_route(logits, T, E, k, ids, wts, stream);
+  auto mark = [&](int i) -> hipError_t {
+    return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_route(logits, T, E, k, ids, wts, stream);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_permute(ids, T, E, k, counts, offsets, perm_src, slot_dst, L.tok, L.rank, L.hist,
                        stream);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+  if (e == hipSuccess) e = mark(3);
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   SelectArgs a;
@@ -350,11 +361,29 @@ int moe_layer(const moe_problem* p, const float* logits, const void* x, const mo
   a.y = L.y; a.y_sh = L.ffn.y_sh;
   SelectOut o{L.ffn.segs, L.ffn.meta};
   e = launch_select(a, o, stream);
-  if (e == hipSuccess) e = launch_gemms(o, fp8, stream);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, stream);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, stream);
+  if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)
     e = launch_combine(L.y, slot_dst, wts, T, k, d, p->has_shared ? L.ffn.y_sh : nullptr, out,
                        stream);
+  if (e == hipSuccess) e = mark(7);
   return hip_status(e);
+}
+}  // namespace
+
+int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
+              void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_impl(p, logits, x, w, out, keep, ws, ws_bytes, nullptr, stream);
+}
+
+int moe_layer_traced(const moe_problem* p, const float* logits, const void* x,
+                     const moe_weights* w, void* out, const moe_routing* keep, void* ws,
+                     size_t ws_bytes, hipEvent_t* events, int num_events, hipStream_t stream) {
+  if (!events || num_events != MOE_TRACE_EVENTS) return MOE_ERR_INVALID_ARG;
+  return layer_impl(p, logits, x, w, out, keep, ws, ws_bytes, events, stream);
 }
 
 }  // extern "C"

@@ -50,12 +50,25 @@ __device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, cons
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Tile descriptors written by the selection kernel and read by the GEMM kernels.
-struct Tile {
-  int32_t expert;  // expert index (E = the shared expert)
-  int32_t m0;      // first row inside the expert's segment
-  int32_t n0;      // first output column (weight row)
-  int32_t rows;    // rows of this tile (<= the tile height)
-};
+// Loads through the global address space (pointers read from memory are generic; flat loads would
+// also count against the LDS wait counter and need 64-bit per-lane addresses).
+typedef __attribute__((address_space(1))) const char gchar;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gload16(const void* base, uint32_t off) {
+  const u32x4 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>((gchar*)base + off);
+  return __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ uint2 gload8(const void* base, uint32_t off) {
+  const u32x2 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x2*>((gchar*)base + off);
+  return __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ int32_t gload_i32(const int32_t* p, int i) {
+  return reinterpret_cast<__attribute__((address_space(1))) const int32_t*>((gchar*)p)[i];
+}
+__device__ __forceinline__ float gload_f32(const float* p, int i) {
+  return reinterpret_cast<__attribute__((address_space(1))) const float*>((gchar*)p)[i];
+}
+
 
 }  // namespace moe

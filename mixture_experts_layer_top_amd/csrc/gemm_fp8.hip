@@ -4,6 +4,6 @@
 
 namespace moe {
 
-hipError_t launch_gemms_fp8(const SelectOut&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_gemms_fp8(const SelectOut&, int, int, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace moe

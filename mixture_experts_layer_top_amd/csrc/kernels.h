@@ -11,8 +11,10 @@ enum Family { kFamStream = 0, kFamMfma = 1, kNumFam = 2 };
 enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
 
 constexpr int kStreamMaxRows = 64;  // rows per weight-streaming tile
-constexpr int kMfmaBM = 128;        // rows per LDS-tiled MFMA tile
-constexpr int kMfmaBN = 128;        // output columns per LDS-tiled MFMA tile
+constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
+constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
+constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
+constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 constexpr int kStreamBN = 64;       // output columns per weight-streaming tile (4 waves x 16)
 constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
 
@@ -55,7 +57,10 @@ struct SelectArgs {
   void* y; void* y_sh;     // down outputs [T*k][d], [T][d]
 };
 
-constexpr int kMetaStride = 4;  // ints per (gemm, family): nseg, ntiles, queue, pad
+// ints per (gemm, family): nseg, ntiles, then kXcds queue counters (the stream family uses the
+// first), zeroed by the selection kernel before each GEMM.
+constexpr int kMetaStride = 16;
+constexpr int kMetaQueue = 2;
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t s);
@@ -66,8 +71,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
 hipError_t launch_gather(const void* x, const float* xs, const int32_t* perm_src, int n, int k,
                          int row_bytes, int nb, void* xp, float* xps, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, const SelectOut& o, hipStream_t s);
-hipError_t launch_gemms_bf16(const SelectOut& o, int num_cus, hipStream_t s);
-hipError_t launch_gemms_fp8(const SelectOut& o, int num_cus, hipStream_t s);
+// Launches both tile families of one GEMM (kGemmGateUp or kGemmDown).
+hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
+hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
 hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
                           int d, const void* shared_y, void* out, hipStream_t s);
 hipError_t launch_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t s);

@@ -53,9 +53,11 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, SelectOut o)
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
   const int tm = (fm == kFamStream) ? kStreamMaxRows : kMfmaBM;
-  const int tn = (fm == kFamStream) ? kStreamBN : kMfmaBN;
+  const int tn_gu = (fm == kFamStream) ? kStreamBN : kMfmaBNGateUp;
+  const int tn_dn = (fm == kFamStream) ? kStreamBN : kMfmaBNDown;
   const int mtiles = (c + tm - 1) / tm;
-  const int nt_gu = ffe / tn, nt_dn = a.d / tn;
+  // f and d are multiples of 128; a down tile of 256 columns may be half full at the edge
+  const int nt_gu = ffe / tn_gu, nt_dn = (a.d + tn_dn - 1) / tn_dn;
   if (fm >= 0) {
     scan[kGemmGateUp][fm][rank] = mtiles * nt_gu;
     scan[kGemmDown][fm][rank] = mtiles * nt_dn;
@@ -144,8 +146,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, SelectOut o)
     for (int q = 0; q < nexp; ++q) nseg += (fam[q] == f);
     o.meta[e * kMetaStride + 0] = nseg;
     o.meta[e * kMetaStride + 1] = scan[g][f][kSelMax - 1];
-    o.meta[e * kMetaStride + 2] = 0;
-    o.meta[e * kMetaStride + 3] = 0;
+    for (int q = kMetaQueue; q < kMetaStride; ++q) o.meta[e * kMetaStride + q] = 0;
   }
 }
 

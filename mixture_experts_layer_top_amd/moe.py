@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer": (_i, [ctypes.POINTER(Problem), _vp, _vp, ctypes.POINTER(Weights), _vp,
                                ctypes.POINTER(Routing), _vp, _sz, _vp]),
             "moe_layer_workspace_bytes": (_sz, [ctypes.POINTER(Problem)]),
+            "moe_layer_traced": (_i, [ctypes.POINTER(Problem), _vp, _vp, ctypes.POINTER(Weights), _vp,
+                                      ctypes.POINTER(Routing), _vp, _sz, ctypes.POINTER(_vp), _i, _vp]),
             "moe_status_string": (ctypes.c_char_p, [_i]),
         }
         for name, (res, args) in sig.items():
@@ -78,7 +80,10 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
             "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
-            "moe_layer_workspace_bytes", "moe_status_string")
+            "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string")
+
+TRACE_EVENTS = 8
+TRACE_PHASES = ("route", "permute", "quant", "select", "gate_up", "down", "combine")
 
 
 def _check(status: int, what: str) -> None:
@@ -237,6 +242,21 @@ class Layer:
         _check(lib().moe_layer(ctypes.byref(self.p), _ptr(logits), _ptr(x), ctypes.byref(self.w),
                                _ptr(out), ctypes.byref(r), _ptr(self.ws), self.ws.numel(),
                                _stream()), "moe_layer")
+        return out
+
+    def traced(self, logits, x, events, keep: dict | None = None, out=None):
+        """Same as __call__, recording the TRACE_EVENTS hipEvent_t handles in `events` at the
+        phase boundaries (see moe_layer_traced in the C header)."""
+        r = Routing()
+        if keep:
+            for name in keep:
+                setattr(r, name, _ptr(keep[name]))
+        out = self.out if out is None else out
+        arr = (ctypes.c_void_p * TRACE_EVENTS)(*events)
+        _check(lib().moe_layer_traced(ctypes.byref(self.p), _ptr(logits), _ptr(x),
+                                      ctypes.byref(self.w), _ptr(out), ctypes.byref(r),
+                                      _ptr(self.ws), self.ws.numel(), arr, TRACE_EVENTS,
+                                      _stream()), "moe_layer_traced")
         return out
 
 
