@@ -142,172 +142,202 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // LDS-tiled MFMA family
 //
 // Tile: 256 token rows x 256 weight rows (gate/up: 128 gate + 128 up rows -> 128 h columns; down:
-// 256 y columns), K-steps of 64 through two LDS stages of 64 KB (rows of 128 B, 16-byte chunks
-// XOR-swizzled by row so ds_read_b128 is conflict-free).  4 wavefronts as 2 (tokens) x 2 (weights),
-// each 128 x 128 with MFMA 32x32x16: 16 accumulator blocks, 4 A and 4 B fragments per k-substep,
-// every fragment reused 4 times.  Global -> LDS through registers, one K-step ahead; LDS -> register
-// fragments one k-substep ahead.  Bases are wavefront-uniform (scalar), per-lane offsets 32-bit.
+// 256 y columns).  4 wavefronts as 2 (tokens) x 2 (weights), each 128 x 128 with MFMA 32x32x16:
+// 16 accumulator blocks, 4 A and 4 B fragments per k-substep, every fragment reused 4 times.
+//
+// Memory pipeline: K-steps of 32 through 4 LDS stages of 32 KB (512 rows of 64 B).  Global data goes
+// straight into LDS (global_load_lds_dwordx4, no staging registers) three steps ahead of its use, so
+// 96 KB per CU are in flight while the MFMAs run.  Each step: wait until this wavefront's loads for
+// the step have landed (vmcnt), barrier (then every wavefront's have), issue the loads for step + 3
+// into the stage read in the previous step, then 2 k-substeps of 16 MFMAs.  The stages are distinct
+// LDS arrays so the compiler can tell the asynchronous LDS writes from the reads.  Rows of 64 B keep
+// 4 chunks of 16 B, XOR-swizzled by (row >> 2) & 3 so the 16 lanes of a ds_read_b128 group (16 rows,
+// same chunk) cover all 64 banks.
 //
 // Scheduling: one persistent workgroup per CU.  The tile order puts the m-tiles of one weight tile
 // next to each other; consecutive runs of (CUs per XCD) tiles go to one XCD, so tiles that share
 // weight and activation tiles run side by side on the same L2.  Each XCD has its own queue; a
 // workgroup whose queue is empty takes work from the other XCDs' queues.
 // ------------------------------------------------------------------------------------------------
-constexpr int BM = kMfmaBM, BK = 64;
-constexpr int BNW = 256;                 // weight rows per tile
-constexpr int LROWS = BM + BNW;          // LDS rows per stage
-constexpr int STAGE = LROWS * 128;       // bytes per stage (64 KB)
-constexpr int LPT = LROWS * 8 / 256;     // 16-byte global loads per thread per stage (16)
-constexpr int kMfmaLds = 2 * STAGE;
+constexpr int BM = kMfmaBM, BK = 32, NSTAGE = 4;
+constexpr int BNW = 256;                  // weight rows per tile
+constexpr int LROWS = BM + BNW;           // LDS rows per stage
+constexpr int ROWB = BK * 2;              // bytes per LDS row (64)
+constexpr int STAGE = LROWS * ROWB;       // bytes per stage (32 KB)
+constexpr int DMA_PER_STAGE = STAGE / (256 * 16);  // 16-byte loads per thread per stage (8)
 
-// byte offset of 16-byte chunk `ch` (0..7) of LDS row `r` (rows of BK bf16 = 128 B)
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+__shared__ __attribute__((aligned(1024))) uint8_t g_st0[STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t g_st1[STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t g_st2[STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t g_st3[STAGE];
+template <int S> __device__ __forceinline__ uint8_t* stage_ptr() {
+  return S == 0 ? g_st0 : S == 1 ? g_st1 : S == 2 ? g_st2 : g_st3;
+}
 
+// byte offset of 16-byte chunk `c` (0..3) of LDS row `r`
+__device__ __forceinline__ int lds_off(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// vmcnt(n) only (expcnt and lgkmcnt left at their maxima), gfx9 encoding
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 template <bool GU>
-__device__ __forceinline__ void mfma_tile_bf16(const Seg& sg, int m0, int rows, int n0,
-                                               uint8_t* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
-  const int K = sg.K, N = sg.N;
-  const uint32_t rowbytes = (uint32_t)K * 2;
-  const char* abase = static_cast<const char*>(sg.a);
-  const char* w0 = static_cast<const char*>(sg.w0);
-  const char* w1 = static_cast<const char*>(GU ? sg.w1 : sg.w0);
-
-  // Load slot i of this thread: LDS row 32*i + tid/8, chunk tid%8.  Slots 0..7 are token rows,
-  // 8..15 weight rows (gate/up: 8..11 gate, 12..15 up).
-  const int rsub = tid >> 3, ch = tid & 7;
-  const uint32_t lds0 = lds_off(rsub, ch);
-  uint32_t off[LPT];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int r = 32 * i + rsub;
-    r = r < rows ? r : rows - 1;  // padded rows re-read a valid row and are never stored
-    const int gr = sg.row0 + m0 + r;
-    const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-    off[i] = (uint32_t)src * rowbytes + ch * 16;
-  }
-#pragma unroll
-  for (int i = 8; i < 16; ++i) {
-    int wr;
-    if (GU) wr = n0 + 32 * ((i - 8) & 3) + rsub;  // gate rows (i < 12) or up rows (i >= 12)
-    else wr = n0 + 32 * (i - 8) + rsub;
-    wr = wr < N ? wr : N - 1;  // half-full edge tile of the down GEMM
-    off[i] = (uint32_t)wr * rowbytes + ch * 16;
-  }
-
+struct MfmaTile {
+  // Load slot j of wavefront wv fills LDS rows [16*(4*j + wv), +16): slots 0..3 token rows,
+  // 4..7 weight rows (gate/up: slots 4,5 gate rows 0..127, slots 6,7 up rows 0..127).  The base of
+  // a slot is therefore fixed by j; only the per-lane offset depends on the row.
+  const char* abase;
+  const char* wbase0;
+  const char* wbase1;
+  uint32_t off[DMA_PER_STAGE];      // per lane: byte offset of this lane's 16 bytes at k = 0
+  int wvu;                          // wavefront index (uniform)
+  int arow[4], brow[4];             // this lane's fragment rows (A = weights, B = tokens)
   f32x16 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  uint4 stg[LPT];
-  auto gload = [&](int kt) {
-    const uint32_t ko = (uint32_t)kt * (BK * 2);
+  __device__ __forceinline__ const char* slot_base(int j) const {
+    return j < 4 ? abase : ((!GU || j < 6) ? wbase0 : wbase1);
+  }
+
+  __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0) {
+    const int lane = threadIdx.x & 63;
+    wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wvu & 1, wn = wvu >> 1;
+    const uint32_t rowbytes = (uint32_t)sg.K * 2;
+    abase = static_cast<const char*>(sg.a);
+    wbase0 = static_cast<const char*>(sg.w0);
+    wbase1 = static_cast<const char*>(GU ? sg.w1 : sg.w0);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const char* base = i < 8 ? abase : ((!GU || i < 12) ? w0 : w1);
-      stg[i] = gload16(base, off[i] + ko);
+    for (int j = 0; j < DMA_PER_STAGE; ++j) {
+      const int r = 16 * (4 * j + wvu) + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);  // global chunk that lands in this lane's slot
+      if (j < 4) {
+        int rr = r < rows ? r : rows - 1;  // padded rows re-read a valid row, never stored
+        const int gr = sg.row0 + m0 + rr;
+        const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
+        off[j] = (uint32_t)src * rowbytes + c * 16;
+      } else {
+        int wr = GU ? n0 + ((r - BM) & 127) : n0 + (r - BM);
+        wr = wr < sg.N ? wr : sg.N - 1;  // half-full edge tile of the down GEMM
+        off[j] = (uint32_t)wr * rowbytes + c * 16;
+      }
     }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* dst = lds + stage * STAGE + lds0;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) *reinterpret_cast<uint4*>(dst + i * 32 * 128) = stg[i];
-  };
-
-  const int l32 = lane & 31, khalf = lane >> 5;
-  // LDS rows of this wave's fragments: A (weights) blocks a = 0..3, B (tokens) blocks b = 0..3
-  int arow[4], brow[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-    arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
-                 : (BM + wn * 128 + a * 32 + l32);
-#pragma unroll
-  for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
-
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  if (nk > 1) gload(1);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = lds + (kt & 1) * STAGE;
-    bf16x8 fa[2][4], fb[2][4];
+    const int l32 = lane & 31;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      fa[0][a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], khalf)));
+      arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
+                   : (BM + wn * 128 + a * 32 + l32);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      fb[0][b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], khalf)));
+    for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  }
+
+  template <int S>
+  __device__ __forceinline__ void issue(int kt) {
+    uint8_t* st = stage_ptr<S>() + wvu * 16 * ROWB;
+    const uint32_t ko = (uint32_t)kt * ROWB;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_STAGE; ++j)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<__attribute__((address_space(1))) const void*>((gchar*)slot_base(j) + off[j] + ko),
+          (lds_void*)(st + j * 64 * ROWB), 16, 0, 0);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void compute() {
+    const uint8_t* st = stage_ptr<S>();
+    const int khalf = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < BK / 16) {
-        const int c2 = (kk + 1) * 2 + khalf;
+      const int c = kk * 2 + khalf;
+      bf16x8 fa[4], fb[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          fa[nxt][a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], c2)));
+      for (int a = 0; a < 4; ++a) fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], c)));
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          fb[nxt][b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], c2)));
-      }
+      for (int b = 0; b < 4; ++b) fb[b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], c)));
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[cur][a], fb[cur][b], acc[a][b]);
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
     }
-    if (kt + 1 < nk) {
-      lstore((kt + 1) & 1);
-      if (kt + 2 < nk) gload(kt + 2);
-    }
-    __syncthreads();
   }
 
-  // epilogue: lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
-  uint16_t* out = static_cast<uint16_t*>(sg.out);
+  // Step kt on stage S: loads for kt+3 go to stage (S+3)&3 (clamped to the last step at the tail,
+  // so every step issues the same number of loads and the vmcnt count stays exact).
+  template <int S>
+  __device__ __forceinline__ void step(int kt, int nk) {
+    __builtin_amdgcn_sched_barrier(0);  // keep each step's work inside the step
+    MOE_WAIT_VMCNT(2 * DMA_PER_STAGE);
+    __builtin_amdgcn_s_barrier();
+    issue<(S + 3) & 3>(min(kt + 3, nk - 1));
+    compute<S>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ __forceinline__ void run(int K) {
+    const int nk = K / BK;  // K is a multiple of 128, so nk is a multiple of 4
+    issue<0>(0);
+    issue<1>(1);
+    issue<2>(2);
+    for (int kt = 0; kt < nk; kt += 4) {
+      step<0>(kt, nk);
+      step<1>(kt + 1, nk);
+      step<2>(kt + 2, nk);
+      step<3>(kt + 3, nk);
+    }
+    MOE_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();  // stages free for the next tile
+  }
+
+  __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv & 1, wn = wv >> 1;
+    const int l32 = lane & 31, khalf = lane >> 5;
+    const int N = sg.N;
+    uint16_t* out = static_cast<uint16_t*>(sg.out);
+    // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int r = wm * 128 + b * 32 + l32;
-    if (r >= rows) continue;
-    uint16_t* orow = out + (size_t)(sg.row0 + m0 + r) * N;
-    if (GU) {
+    for (int b = 0; b < 4; ++b) {
+      const int r = wm * 128 + b * 32 + l32;
+      if (r >= rows) continue;
+      uint16_t* orow = out + (size_t)(sg.row0 + m0 + r) * N;
+      if (GU) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int c0 = n0 + wn * 64 + a * 32 + khalf * 4;
+        for (int a = 0; a < 2; ++a) {
+          const int c0 = n0 + wn * 64 + a * 32 + khalf * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v[4];
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[a][b][q * 4 + s], acc[a + 2][b][q * 4 + s]);
-          uint2 pk;
-          pk.x = pack_bf16x2(v[0], v[1]);
-          pk.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+            for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[a][b][q * 4 + s], acc[a + 2][b][q * 4 + s]);
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+          }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int cb = n0 + wn * 128 + a * 32;
-        if (cb >= N) continue;
-        const int c0 = cb + khalf * 4;
+        for (int a = 0; a < 4; ++a) {
+          const int cb = n0 + wn * 128 + a * 32;
+          if (cb >= N) continue;
+          const int c0 = cb + khalf * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 pk;
-          pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
-          pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+          for (int q = 0; q < 4; ++q) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
+            pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
+            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+          }
         }
       }
     }
   }
-}
+};
 
 // Next tile for this workgroup from the per-XCD queues (see the scheduling note above), or -1.
 // `q` is the workgroup's current queue offset (0 = its own XCD), kept across calls.
@@ -332,12 +362,12 @@ __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chu
 template <bool GU>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__ segs,
                                                           int32_t* __restrict__ meta) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int slot;
   const int nseg = meta[0], ntiles = meta[1];
   if (ntiles == 0) return;
   const int chunk = max(1, (int)gridDim.x / kXcds);
   int q = 0;
+  MfmaTile<GU> tile;
   for (;;) {
     const int t = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);
     if (t < 0) break;
@@ -346,29 +376,25 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     const int m0 = mt * BM;
-    mfma_tile_bf16<GU>(sg, m0, min(BM, sg.rows - m0), nt * (GU ? kMfmaBNGateUp : kMfmaBNDown), lds);
+    const int rows = min(BM, sg.rows - m0);
+    const int n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
+    tile.setup(sg, m0, rows, n0);
+    tile.run(sg.K);
+    tile.store(sg, m0, rows, n0);
   }
 }
 
 hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_bf16<true>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_bf16<false>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
-    attr_done = true;
-  }
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
   if (g == kGemmGateUp) {
     gemm_stream_bf16<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    gemm_mfma_bf16<true><<<num_cus, 256, kMfmaLds, s>>>(sm, mm);
+    gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm);
   } else {
     gemm_stream_bf16<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    gemm_mfma_bf16<false><<<num_cus, 256, kMfmaLds, s>>>(sm, mm);
+    gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm);
   }
   return hipGetLastError();
 }
