@@ -247,34 +247,56 @@ struct MfmaTile {
           (lds_void*)(st + j * 64 * ROWB), 16, 0, 0);
   }
 
+  // Fragments of k-substep kk (0 or 1) of stage S into f (4 A then 4 B).
   template <int S>
-  __device__ __forceinline__ void compute() {
+  __device__ __forceinline__ void read_frags(int kk, bf16x8 (&f)[8]) const {
     const uint8_t* st = stage_ptr<S>();
-    const int khalf = (threadIdx.x & 63) >> 5;
+    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + khalf;
-      bf16x8 fa[4], fb[4];
+    for (int a = 0; a < 4; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], c)));
 #pragma unroll
-      for (int a = 0; a < 4; ++a) fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], c)));
-#pragma unroll
-      for (int b = 0; b < 4; ++b) fb[b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], c)));
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
-    }
+    for (int b = 0; b < 4; ++b) f[4 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], c)));
   }
 
-  // Step kt on stage S: loads for kt+3 go to stage (S+3)&3 (clamped to the last step at the tail,
-  // so every step issues the same number of loads and the vmcnt count stays exact).
+  __device__ __forceinline__ void mfmas(const bf16x8 (&f)[8]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(f[a], f[4 + b], acc[a][b]);
+  }
+
+  // Step kt on stage S.  On entry f0 holds substep 0 of stage S.  The barrier sits between the two
+  // halves so that the fragments of the next half are always already in registers: MFMAs on
+  // substep 0 while substep 1 is read; wait for this wavefront's loads of stage S+1, barrier (now
+  // stage S+1 is complete and every wavefront is done with stage S-1); loads for step kt+3 into
+  // stage S-1 (clamped at the tail so the vmcnt count stays exact); MFMAs on substep 1 while
+  // substep 0 of stage S+1 is read into f0.
   template <int S>
-  __device__ __forceinline__ void step(int kt, int nk) {
-    __builtin_amdgcn_sched_barrier(0);  // keep each step's work inside the step
-    MOE_WAIT_VMCNT(2 * DMA_PER_STAGE);
+  __device__ __forceinline__ void step(int kt, int nk, bf16x8 (&f0)[8], bf16x8 (&f1)[8]) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<S>(1, f1);
+    mfmas(f0);
+    // issue order: the 8 fragment reads right behind the first 8 MFMAs, then the other 8 MFMAs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_WAIT_VMCNT(DMA_PER_STAGE);
     __builtin_amdgcn_s_barrier();
     issue<(S + 3) & 3>(min(kt + 3, nk - 1));
-    compute<S>();
+    read_frags<(S + 1) & 3>(0, f0);
+    mfmas(f1);
+    // one global->LDS load and one fragment read behind each of the first 8 MFMAs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -283,14 +305,19 @@ struct MfmaTile {
     issue<0>(0);
     issue<1>(1);
     issue<2>(2);
+    MOE_WAIT_VMCNT(2 * DMA_PER_STAGE);
+    __builtin_amdgcn_s_barrier();
+    bf16x8 f0[8], f1[8];
+    read_frags<0>(0, f0);
     for (int kt = 0; kt < nk; kt += 4) {
-      step<0>(kt, nk);
-      step<1>(kt + 1, nk);
-      step<2>(kt + 2, nk);
-      step<3>(kt + 3, nk);
+      step<0>(kt, nk, f0, f1);
+      step<1>(kt + 1, nk, f0, f1);
+      step<2>(kt + 2, nk, f0, f1);
+      step<3>(kt + 3, nk, f0, f1);
     }
     MOE_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();  // stages free for the next tile
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the last (unused) fragment reads are done
+    __builtin_amdgcn_s_barrier();        // stages free for the next tile
   }
 
   __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
