@@ -28,8 +28,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
-// SiLU(g) * u in fp32.
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u in fp32, with the hardware exp2 and reciprocal (about 1 ulp each; the result is then
+// rounded to bf16 or fp8).  g -> -inf gives exp -> inf, rcp -> 0 and the limit 0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // MFMA wrappers.  Operand convention used throughout: the first operand ("A", MFMA rows i) holds
 // weight rows, the second ("B", MFMA columns j) holds token rows; both are K-contiguous fragments.

@@ -178,8 +178,56 @@ template <int S> __device__ __forceinline__ uint8_t* stage_ptr() {
 // byte offset of 16-byte chunk `c` (0..3) of LDS row `r`
 __device__ __forceinline__ int lds_off(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
 
-// vmcnt(n) only (expcnt and lgkmcnt left at their maxima), gfx9 encoding
-#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+// s_waitcnt with vmcnt(vm) and lgkmcnt(lg), expcnt left at its maximum (gfx9 encoding)
+#define MOE_WAITCNT(vm, lg) \
+  __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | 0x70 | (((lg) & 15) << 8))
+
+template <bool GU>
+__device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const Seg& sg, int m0,
+                                              int rows, int n0) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv & 1, wn = wv >> 1;
+    const int l32 = lane & 31, khalf = lane >> 5;
+    const int N = sg.N;
+    uint16_t* out = static_cast<uint16_t*>(sg.out);
+    // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = wm * 128 + b * 32 + l32;
+      if (r >= rows) continue;
+      uint16_t* orow = out + (size_t)(sg.row0 + m0 + r) * N;
+      if (GU) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int c0 = n0 + wn * 64 + a * 32 + khalf * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[a][b][q * 4 + s], acc[a + 2][b][q * 4 + s]);
+            uint2 pk;
+            pk.x = pack_bf16x2(v[0], v[1]);
+            pk.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int cb = n0 + wn * 128 + a * 32;
+          if (cb >= N) continue;
+          const int c0 = cb + khalf * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
+            pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
+            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+          }
+        }
+      }
+    }
+  }
 
 template <bool GU>
 struct MfmaTile {
@@ -228,12 +276,6 @@ struct MfmaTile {
                    : (BM + wn * 128 + a * 32 + l32);
 #pragma unroll
     for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   }
 
   template <int S>
@@ -266,11 +308,13 @@ struct MfmaTile {
   }
 
   // Step kt on stage S.  On entry f0 holds substep 0 of stage S.  The barrier sits between the two
-  // halves so that the fragments of the next half are always already in registers: MFMAs on
-  // substep 0 while substep 1 is read; wait for this wavefront's loads of stage S+1, barrier (now
-  // stage S+1 is complete and every wavefront is done with stage S-1); loads for step kt+3 into
-  // stage S-1 (clamped at the tail so the vmcnt count stays exact); MFMAs on substep 1 while
-  // substep 0 of stage S+1 is read into f0.
+  // halves so the fragments of the next half are always already in registers:
+  //   first half : MFMAs on substep 0 while substep 1 of stage S is read;
+  //   wait until this wavefront's fragment reads are done (so it no longer needs stage S) and its
+  //   loads of stage S+1 have landed; barrier (now stage S+1 is complete and stage S is free);
+  //   second half: loads for step kt+4 into stage S (clamped at the tail so the vmcnt count stays
+  //   exact), MFMAs on substep 1 while substep 0 of stage S+1 is read into f0.
+  // Loads are issued three steps before their first read.
   template <int S>
   __device__ __forceinline__ void step(int kt, int nk, bf16x8 (&f0)[8], bf16x8 (&f1)[8]) {
     __builtin_amdgcn_sched_barrier(0);
@@ -284,9 +328,9 @@ struct MfmaTile {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
-    MOE_WAIT_VMCNT(DMA_PER_STAGE);
+    MOE_WAITCNT(2 * DMA_PER_STAGE, 0);
     __builtin_amdgcn_s_barrier();
-    issue<(S + 3) & 3>(min(kt + 3, nk - 1));
+    issue<S>(min(kt + 4, nk - 1));
     read_frags<(S + 1) & 3>(0, f0);
     mfmas(f1);
     // one global->LDS load and one fragment read behind each of the first 8 MFMAs
@@ -300,12 +344,23 @@ struct MfmaTile {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  __device__ __forceinline__ void run(int K) {
-    const int nk = K / BK;  // K is a multiple of 128, so nk is a multiple of 4
+  // The first four stages of a tile (may be issued while the previous tile's epilogue runs).
+  __device__ __forceinline__ void prologue() {
     issue<0>(0);
     issue<1>(1);
     issue<2>(2);
-    MOE_WAIT_VMCNT(2 * DMA_PER_STAGE);
+    issue<3>(3);
+  }
+
+  __device__ __forceinline__ void run(int K) {
+    const int nk = K / BK;  // K is a multiple of 128, so nk is a multiple of 4 (>= 4)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    MOE_WAITCNT(3 * DMA_PER_STAGE, 15);
     __builtin_amdgcn_s_barrier();
     bf16x8 f0[8], f1[8];
     read_frags<0>(0, f0);
@@ -315,54 +370,170 @@ struct MfmaTile {
       step<2>(kt + 2, nk, f0, f1);
       step<3>(kt + 3, nk, f0, f1);
     }
-    MOE_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the last (unused) fragment reads are done
-    __builtin_amdgcn_s_barrier();        // stages free for the next tile
+    MOE_WAITCNT(0, 0);                  // every load landed, the last (unused) reads done
+    __builtin_amdgcn_s_barrier();       // stages free for the next tile
   }
 
   __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wm = wv & 1, wn = wv >> 1;
-    const int l32 = lane & 31, khalf = lane >> 5;
-    const int N = sg.N;
-    uint16_t* out = static_cast<uint16_t*>(sg.out);
-    // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
+    MfmaTileStore<GU>(acc, sg, m0, rows, n0);
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// The same tile with K-steps of 64: two LDS stages of 64 KB (512 rows of 128 B), so every
+// global->LDS instruction moves 8 whole 128-byte lines (with 64-byte rows each line would be
+// requested twice, one step apart).  Rows of 128 B keep 8 chunks XOR-swizzled by (row >> 1) & 7.
+// Step kt on stage S: substeps 0..2 run while substeps 1..3 are read; wait until this wavefront's
+// reads are done and every load it issued has landed; barrier (stage S^1 complete, stage S free);
+// loads for step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
+// ------------------------------------------------------------------------------------------------
+constexpr int BK64 = 64;
+constexpr int ROWB64 = 128;
+constexpr int STAGE64 = LROWS * ROWB64;            // 64 KB
+constexpr int DMA64 = STAGE64 / (256 * 16);        // 16 loads per thread per stage
+__shared__ __attribute__((aligned(1024))) uint8_t g_bs0[STAGE64];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bs1[STAGE64];
+template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return S == 0 ? g_bs0 : g_bs1; }
+
+__device__ __forceinline__ int lds_off64(int r, int c) { return r * ROWB64 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <bool GU>
+struct MfmaTile64 {
+  // Load slot j of wavefront wv fills LDS rows [32*j + 8*wv, +8): slots 0..7 token rows,
+  // 8..15 weight rows (gate/up: 8..11 gate rows 0..127, 12..15 up rows 0..127).
+  const char* abase;
+  const char* wbase0;
+  const char* wbase1;
+  uint32_t off[DMA64];
+  int wvu;
+  int arow[4], brow[4];
+  f32x16 acc[4][4];
+
+  __device__ __forceinline__ const char* slot_base(int j) const {
+    return j < 8 ? abase : ((!GU || j < 12) ? wbase0 : wbase1);
+  }
+
+  __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0) {
+    const int lane = threadIdx.x & 63;
+    wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wvu & 1, wn = wvu >> 1;
+    const uint32_t rowbytes = (uint32_t)sg.K * 2;
+    abase = static_cast<const char*>(sg.a);
+    wbase0 = static_cast<const char*>(sg.w0);
+    wbase1 = static_cast<const char*>(GU ? sg.w1 : sg.w0);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = wm * 128 + b * 32 + l32;
-      if (r >= rows) continue;
-      uint16_t* orow = out + (size_t)(sg.row0 + m0 + r) * N;
-      if (GU) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int c0 = n0 + wn * 64 + a * 32 + khalf * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[a][b][q * 4 + s], acc[a + 2][b][q * 4 + s]);
-            uint2 pk;
-            pk.x = pack_bf16x2(v[0], v[1]);
-            pk.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
-          }
-        }
+    for (int j = 0; j < DMA64; ++j) {
+      const int r = 32 * j + 8 * wvu + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      if (j < 8) {
+        int rr = r < rows ? r : rows - 1;
+        const int gr = sg.row0 + m0 + rr;
+        const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
+        off[j] = (uint32_t)src * rowbytes + c * 16;
       } else {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int cb = n0 + wn * 128 + a * 32;
-          if (cb >= N) continue;
-          const int c0 = cb + khalf * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint2 pk;
-            pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
-            pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
-          }
-        }
+        int wr = GU ? n0 + ((r - BM) & 127) : n0 + (r - BM);
+        wr = wr < sg.N ? wr : sg.N - 1;
+        off[j] = (uint32_t)wr * rowbytes + c * 16;
       }
     }
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
+                   : (BM + wn * 128 + a * 32 + l32);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
+  }
+
+  template <int S>
+  __device__ __forceinline__ void issue(int kt) {
+    uint8_t* st = stage64_ptr<S>() + wvu * 8 * ROWB64;
+    const uint32_t ko = (uint32_t)kt * ROWB64;
+#pragma unroll
+    for (int j = 0; j < DMA64; ++j)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<__attribute__((address_space(1))) const void*>((gchar*)slot_base(j) + off[j] + ko),
+          (lds_void*)(st + j * 32 * ROWB64), 16, 0, 0);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void read_frags(int kk, bf16x8 (&f)[8]) const {
+    const uint8_t* st = stage64_ptr<S>();
+    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(arow[a], c)));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(brow[b], c)));
+  }
+
+  __device__ __forceinline__ void mfmas(const bf16x8 (&f)[8]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(f[a], f[4 + b], acc[a][b]);
+  }
+
+  // 16 MFMAs with the 8 fragment reads issued behind the first 8
+  template <int S>
+  __device__ __forceinline__ void sub(int kk, const bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<S>(kk, nxt);
+    mfmas(cur);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int S>
+  __device__ __forceinline__ void step(int kt, int nk, bf16x8 (&f0)[8], bf16x8 (&f1)[8]) {
+    sub<S>(1, f0, f1);
+    sub<S>(2, f1, f0);
+    sub<S>(3, f0, f1);
+    MOE_WAITCNT(0, 0);
+    __builtin_amdgcn_s_barrier();
+    issue<S>(min(kt + 2, nk - 1));
+    read_frags<S ^ 1>(0, f0);
+    mfmas(f1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ __forceinline__ void prologue() {
+    issue<0>(0);
+    issue<1>(1);
+  }
+
+  __device__ __forceinline__ void run(int K) {
+    const int nk = K / BK64;  // K is a multiple of 128, so nk is even
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    MOE_WAITCNT(DMA64, 15);
+    __builtin_amdgcn_s_barrier();
+    bf16x8 f0[8], f1[8];
+    read_frags<0>(0, f0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step<0>(kt, nk, f0, f1);
+      step<1>(kt + 1, nk, f0, f1);
+    }
+    MOE_WAITCNT(0, 0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
+    MfmaTileStore<GU>(acc, sg, m0, rows, n0);
   }
 };
 
@@ -394,20 +565,36 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   if (ntiles == 0) return;
   const int chunk = max(1, (int)gridDim.x / kXcds);
   int q = 0;
+#ifndef MOE_MFMA_BK32
+  MfmaTile64<GU> tile;
+#else
   MfmaTile<GU> tile;
-  for (;;) {
+#endif
+  struct Cur { int si, m0, rows, n0; };
+  auto claim = [&](Cur& c) -> bool {
     const int t = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);
-    if (t < 0) break;
-    const int si = __builtin_amdgcn_readfirstlane(find_seg(segs, nseg, t));
-    const Seg& sg = segs[si];
+    if (t < 0) return false;
+    c.si = __builtin_amdgcn_readfirstlane(find_seg(segs, nseg, t));
+    const Seg& sg = segs[c.si];
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
-    const int m0 = mt * BM;
-    const int rows = min(BM, sg.rows - m0);
-    const int n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
-    tile.setup(sg, m0, rows, n0);
-    tile.run(sg.K);
-    tile.store(sg, m0, rows, n0);
+    c.m0 = mt * BM;
+    c.rows = min(BM, sg.rows - c.m0);
+    c.n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
+    tile.setup(sg, c.m0, c.rows, c.n0);
+    tile.prologue();
+    return true;
+  };
+  Cur cur;
+  if (!claim(cur)) return;
+  for (;;) {
+    tile.run(segs[cur.si].K);
+    // start the next tile's loads before this tile's epilogue
+    Cur nxt;
+    const bool more = claim(nxt);
+    tile.store(segs[cur.si], cur.m0, cur.rows, cur.n0);
+    if (!more) break;
+    cur = nxt;
   }
 }
 
