@@ -17,6 +17,11 @@ constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
 constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 constexpr int kStreamBN = 64;       // output columns per weight-streaming tile (4 waves x 16)
 constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
+// fp8 weights (streaming family only): rows per pass, h columns per gate/up tile (one whole
+// 128-column requantisation block), y columns per down tile
+constexpr int kStreamMaxRows8 = 128;
+constexpr int kStream8BNGateUp = 128;
+constexpr int kStream8BNDown = 64;
 
 // One expert's share of one grouped GEMM: out[row0 + r][n] for r < rows, n < N, from activation
 // rows (gathered through `tok` when it is not null) and the expert's [N][K] weights.

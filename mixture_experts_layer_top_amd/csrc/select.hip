@@ -9,7 +9,8 @@
 // between the permutation and the GEMMs:
 //   c_e <= 64  -> weight-streaming tiles: the expert's rows ride along while its weights stream
 //                 from HBM once (decode-sized experts are bandwidth-bound: c_e FLOP per weight byte);
-//   c_e  > 64  -> LDS-tiled MFMA tiles of 128 rows (padding only the last tile of the expert).
+//   c_e  > 64  -> LDS-tiled MFMA tiles of 256 rows (padding only the last tile of the expert).
+// Block-scaled fp8 experts always take the streaming family (up to 128 rows per pass).
 // Experts of a family are ordered heaviest first (ties by id) so the persistent GEMM queues start
 // with the longest work.  Experts with no rows get no segment and their weights are never read.
 #include "common.h"
@@ -19,8 +20,9 @@ namespace moe {
 
 constexpr int kSelMax = kSegCap;
 
-__device__ __forceinline__ int pick_family(int c, int config) {
+__device__ __forceinline__ int pick_family(int c, int config, int fp8) {
   if (c <= 0) return -1;
+  if (fp8) return kFamStream;  // block-scaled fp8 experts: streaming family only
   if (config == 0) return kFamStream;
   if (config >= 1) return kFamMfma;
   return c <= kStreamMaxRows ? kFamStream : kFamMfma;
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, SelectOut o)
   int c = 0, fm = -1;
   if (e < nexp) {
     c = (e < a.E) ? a.counts[e] : a.T;
-    fm = pick_family(c, a.config);
+    fm = pick_family(c, a.config, a.fp8);
   }
   cnt[e] = c;
   fam[e] = fm;
@@ -52,9 +54,9 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, SelectOut o)
 
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
-  const int tm = (fm == kFamStream) ? kStreamMaxRows : kMfmaBM;
-  const int tn_gu = (fm == kFamStream) ? kStreamBN : kMfmaBNGateUp;
-  const int tn_dn = (fm == kFamStream) ? kStreamBN : kMfmaBNDown;
+  const int tm = a.fp8 ? kStreamMaxRows8 : (fm == kFamStream) ? kStreamMaxRows : kMfmaBM;
+  const int tn_gu = a.fp8 ? kStream8BNGateUp : (fm == kFamStream) ? kStreamBN : kMfmaBNGateUp;
+  const int tn_dn = a.fp8 ? kStream8BNDown : (fm == kFamStream) ? kStreamBN : kMfmaBNDown;
   const int mtiles = (c + tm - 1) / tm;
   // f and d are multiples of 128; a down tile of 256 columns may be half full at the edge
   const int nt_gu = ffe / tn_gu, nt_dn = (a.d + tn_dn - 1) / tn_dn;

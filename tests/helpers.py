@@ -54,12 +54,13 @@ class Inputs:
         return self._cache[e]
 
     def get_shared(self):
+        """The shared expert's stored weights for the oracle, as a getter (None without one)."""
         if not self.p.shared:
             return None
         r = {n: self.W["sh_" + n].cpu().numpy() for n in ("gate", "up", "down")}
         if self.p.wdtype == I.WDT_FP8:
             r.update({"s_" + n: self.W["s_sh_" + n].cpu().numpy() for n in ("gate", "up", "down")})
-        return r
+        return lambda: r
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -201,3 +201,76 @@ def test_t0_is_noop(moe):
     L = moe.Layer(W, 0, p.E, p.k)
     out = L(torch.empty((0, p.E), device="cuda"), torch.empty((0, p.d), dtype=torch.int16, device="cuda"))
     assert out.shape == (0, p.d)
+
+
+# ------------------------------------------------------------------------------------------------
+# fp8: activation quantisation (bit-exact) and the block-scaled layer
+# ------------------------------------------------------------------------------------------------
+
+def _all_bf16_below_448():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = (b.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    return b[keep]
+
+
+def test_quant_act_exhaustive_bf16(moe):
+    """A 448 in every 128-block makes s = 1 exactly, so q must be the oracle's encoding of every
+    finite bf16 value of magnitude <= 448 (all binades, subnormals, both zeros, every tie)."""
+    vals = _all_bf16_below_448()
+    per, d = 127, 1024
+    nblk = (vals.size + per - 1) // per
+    nblk += (-nblk) % (d // 128)  # whole rows of 8 blocks
+    pad = np.full(nblk * per - vals.size, 0x3F80, np.uint16)  # 1.0
+    body = np.concatenate([vals, pad]).reshape(nblk, per)
+    blocks = np.concatenate([np.full((nblk, 1), 0x43E0, np.uint16), body], axis=1)  # 448.0 first
+    x = blocks.reshape(-1, d)
+    xq, xs = moe.quant_act(torch.from_numpy(x.view(np.int16)).cuda())
+    rq, rs = O.quant_act_e4m3(x)
+    assert np.array_equal(xs.cpu().numpy(), rs)
+    assert np.all(rs == 1.0)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("scale", [1.0, 1e-3, 37.0, 1e-30])
+def test_quant_act_random(moe, scale):
+    rng = np.random.default_rng(int(scale * 1000) + 1)
+    x = (rng.standard_normal((37, 640)) * scale).astype(np.float32)
+    x[3, 128:256] = 0.0
+    x[5, :128] = -0.0
+    x[7, 256:384] = rng.integers(-3, 4, 128)
+    bits = I.f32_to_bf16_bits(x)
+    xq, xs = moe.quant_act(torch.from_numpy(bits.view(np.int16)).cuda())
+    rq, rs = O.quant_act_e4m3(bits)
+    assert np.array_equal(xs.cpu().numpy(), rs)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+FP8_SMALL = [
+    I.Problem("fp8_tiny", 110, T=24, d=256, f=256, E=16, k=4, routing="dirichlet", alpha=1.0,
+              wdtype=I.WDT_FP8, shared=True, shared_f=256),
+    I.Problem("fp8_ragged", 111, T=150, d=384, f=512, E=12, k=3, routing="dirichlet", alpha=0.3,
+              wdtype=I.WDT_FP8, shared=True, shared_f=384),
+    I.Problem("fp8_noshared", 112, T=70, d=256, f=384, E=8, k=2, wdtype=I.WDT_FP8),
+]
+
+
+@pytest.mark.parametrize("p", FP8_SMALL, ids=lambda p: p.name)
+def test_fp8_layer_matches_oracle(moe, p):
+    _check_layer(moe, Inputs(p), tol=FP8_TOL, runs=2)
+
+
+def test_fp8_grouped_ffn_matches_oracle(moe):
+    p = FP8_SMALL[1]
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    xq, xs = O.quant_act_e4m3(inp.x)
+    y = moe.grouped_ffn(torch.from_numpy(xq[perm_src // p.k]).cuda(),
+                        torch.from_numpy(xs[perm_src // p.k]).cuda(),
+                        torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, None, act_fp8=True)["y_perm"]
+    assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
