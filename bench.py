@@ -96,6 +96,34 @@ def algorithmic(p, n_active: int):
                 bytes_gu=w_gu + x_bytes, bytes_dn=w_dn + out_bytes)
 
 
+TRAFFIC_SOURCES = ("mixture_experts_layer_top_amd/csrc/gemm_bf16.hip",
+                   "mixture_experts_layer_top_amd/csrc/common.h")
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3 counter summary
+    (profiles/gate_up_gemm_<workload>_traffic.md), or None if there is none or the kernel sources
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("-", "|", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(p, logits, x, W, sample_tokens: int):
     """The CPU oracle as it stands, timed on the first `sample_tokens` tokens of the same inputs
     (routing, permutation, experts and combine are row-wise, so this is the same workload at a
@@ -250,8 +278,12 @@ def main() -> int:
         achieved = alg["bytes_gu"] / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    traffic = profiled_traffic(p.name)
     roof.update({"kernel": "gate/up grouped GEMM + SwiGLU (both tile families)",
-                 "avg_launch_ms": round(gu_ms, 4), "traffic": None})
+                 "avg_launch_ms": round(gu_ms, 4),
+                 "traffic": traffic, "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + "
+                 "WRITE_SIZE, calibrated on a 1 GiB copy)" if traffic else None,
+                 "algorithmic_per_launch": alg["flop_gu"] if prefill else alg["bytes_gu"]})
 
     layer_s = ms_per_step * 1e-3
     out = {
@@ -286,7 +318,7 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral_prefill": 2048, "kimi_prefill": 512}.get(p.name, p.T)
+        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 512}.get(p.name, p.T)
         print(f"[bench] CPU oracle on {sample} tokens ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, logits, x, W, sample)
     print(json.dumps(out), flush=True)
