@@ -325,16 +325,6 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   auto mark = [&](int i) -> hipError_t {
     return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
   };
-  hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_route(logits, T, E, k, ids, wts, stream);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = launch_permute(ids, T, E, k, counts, offsets, perm_src, slot_dst, L.tok, L.rank, L.hist,
-                       stream);
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
-  if (e == hipSuccess) e = mark(3);
-  if (e != hipSuccess) return MOE_ERR_HIP;
 
   SelectArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -360,8 +350,30 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.h_sh = L.ffn.h_sh; a.hs_sh = L.ffn.hs_sh;
   a.y = L.y; a.y_sh = L.ffn.y_sh;
   SelectOut o{L.ffn.segs, L.ffn.meta};
-  e = launch_select(a, o, stream);
-  if (e == hipSuccess) e = mark(4);
+
+  hipError_t e = mark(0);
+  if (front_small_fits(T, k)) {
+    // decode-sized: route, permute and select in one launch (phases 1, 2 and 4 share it)
+    if (e == hipSuccess)
+      e = launch_front_small(logits, T, E, k, ids, wts, counts, offsets, perm_src, slot_dst,
+                             L.tok, a, o, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(4);
+  } else {
+    if (e == hipSuccess) e = launch_route(logits, T, E, k, ids, wts, stream);
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess)
+      e = launch_permute(ids, T, E, k, counts, offsets, perm_src, slot_dst, L.tok, L.rank,
+                         L.hist, stream);
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = launch_select(a, o, stream);
+    if (e == hipSuccess) e = mark(4);
+  }
   if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, stream);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, stream);

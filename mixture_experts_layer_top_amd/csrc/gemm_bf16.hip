@@ -41,17 +41,29 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 
 // ------------------------------------------------------------------------------------------------
 // weight-streaming family
+//
+// One workgroup = 16 weight rows (gate/up: 16 gate + 16 up) and all (<= 64) rows of an expert's
+// segment; its 4 wavefronts split K in quarters and their partial sums meet in LDS (added in a
+// fixed order, so results are deterministic).  Small tiles give decode-sized layers enough
+// workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its quarter of
+// the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
 // ------------------------------------------------------------------------------------------------
-template <int MQ, bool GU>
-__device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+template <int MQ, bool GU, int WK>
+__device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0,
+                                                 float* red) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K, N = sg.N;
-  const int nrow = n0 + wv * 16 + r16;  // this lane's weight row (A operand)
+  // WK = 4: the wavefronts split K over the same 16 rows; WK = 1: wavefront wv takes rows 16*wv..
+  const int kw = WK == 4 ? wv : 0;
+  if (WK == 1) n0 += 16 * wv;
+  const int nrow = n0 + r16;  // this lane's weight row (A operand)
   const void* wg = sg.w0;
   const void* wu = GU ? sg.w1 : sg.w0;
   const void* xa = sg.a;
-  const uint32_t woff = (uint32_t)nrow * K * 2 + kg * 16;
+  const int kq = K / WK;  // this wavefront's K range [kw*kq, (kw+1)*kq); K % 128 == 0
+  const uint32_t kbase = (uint32_t)(kw * kq) * 2 + kg * 16;
+  const uint32_t woff = (uint32_t)nrow * K * 2 + kbase;
   uint32_t xoff[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
@@ -59,7 +71,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
     r = r < rows ? r : rows - 1;  // padded columns re-read a valid row; never stored
     const int gr = sg.row0 + m0 + r;
     const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-    xoff[q] = (uint32_t)src * K * 2 + kg * 16;
+    xoff[q] = (uint32_t)src * K * 2 + kbase;
   }
   f32x4 acc0[MQ], acc1[MQ];
 #pragma unroll
@@ -67,32 +79,41 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
     acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  constexpr int U = (MQ == 1) ? 8 : 4;
-  const int nsteps = K / 32;
-  int ks = 0;
-  for (; ks + U <= nsteps; ks += U) {
-    uint4 a0[U], a1[U], b[U][MQ];
+  constexpr int U = (MQ == 1) ? 4 : 2;  // K-steps (of 32) per batch
+  struct Batch { uint4 a0[U], a1[U], b[U][MQ]; };
+  auto load = [&](Batch& bt, int ks) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t ko = (uint32_t)(ks + u) * 64;
-      a0[u] = gload16(wg, woff + ko);
-      if (GU) a1[u] = gload16(wu, woff + ko);
+      bt.a0[u] = gload16(wg, woff + ko);
+      if (GU) bt.a1[u] = gload16(wu, woff + ko);
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) b[u][q] = gload16(xa, xoff[q] + ko);
+      for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(xa, xoff[q] + ko);
     }
+  };
+  auto compute = [&](const Batch& bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        acc0[q] = mfma16(as_bf16x8(a0[u]), as_bf16x8(b[u][q]), acc0[q]);
-        if (GU) acc1[q] = mfma16(as_bf16x8(a1[u]), as_bf16x8(b[u][q]), acc1[q]);
+        acc0[q] = mfma16(as_bf16x8(bt.a0[u]), as_bf16x8(bt.b[u][q]), acc0[q]);
+        if (GU) acc1[q] = mfma16(as_bf16x8(bt.a1[u]), as_bf16x8(bt.b[u][q]), acc1[q]);
       }
+  };
+  const int nsteps = kq / 32;             // K-steps of this wavefront (>= 1)
+  const int nfull = nsteps / U * U;        // pipelined part: whole batches only
+  Batch b0, b1;
+  if (nfull > 0) load(b0, 0);
+  for (int ks = 0; ks < nfull; ks += 2 * U) {
+    if (ks + U < nfull) load(b1, ks + U);
+    compute(b0);
+    if (ks + 2 * U < nfull) load(b0, ks + 2 * U);
+    if (ks + U < nfull) compute(b1);
   }
-  for (; ks < nsteps; ++ks) {
+  for (int ks = nfull; ks < nsteps; ++ks) {  // remainder, one K-step at a time
     const uint32_t ko = (uint32_t)ks * 64;
     const uint4 a0 = gload16(wg, woff + ko);
-    uint4 a1 = a0;
-    if (GU) a1 = gload16(wu, woff + ko);
+    const uint4 a1 = GU ? gload16(wu, woff + ko) : a0;
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       const uint4 b = gload16(xa, xoff[q] + ko);
@@ -100,7 +121,35 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
   }
-  // C[i][j]: i = weight row 4*kg + r (within this wave's 16), j = token r16 of group q
+  // split-K reduction: wavefronts 1..3 park their partials, wavefront 0 adds them in order
+  constexpr int NV = MQ * 4 * (GU ? 2 : 1);  // floats per lane
+  if (WK == 4) __syncthreads();  // red[] may still be read by the previous tile
+  if (WK == 4 && wv > 0) {
+    float* dst = red + ((wv - 1) * NV) * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < MQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[(q * 4 + i) * 64] = acc0[q][i];
+        if (GU) dst[(MQ * 4 + q * 4 + i) * 64] = acc1[q][i];
+      }
+  }
+  if (WK == 4) {
+    __syncthreads();
+    if (wv != 0) return;
+  }
+#pragma unroll
+  for (int w = 0; w < (WK == 4 ? 3 : 0); ++w) {
+    const float* src = red + (w * NV) * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < MQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0[q][i] += src[(q * 4 + i) * 64];
+        if (GU) acc1[q][i] += src[(MQ * 4 + q * 4 + i) * 64];
+      }
+  }
+  // C[i][j]: i = weight row 4*kg + r, j = token r16 of group q
   uint16_t* out = static_cast<uint16_t*>(sg.out);
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
@@ -112,7 +161,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       uint2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
       pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(out + (size_t)(sg.row0 + m0 + r) * N + n0 + wv * 16 + kg * 4) = pk;
+      *reinterpret_cast<uint2*>(out + (size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) = pk;
     }
   }
 }
@@ -121,6 +170,8 @@ template <bool GU>
 __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ segs,
                                                          int32_t* __restrict__ meta) {
   __shared__ int slot;
+  // split-K partials of wavefronts 1..3: up to 4 token groups x 4 x 2 floats per lane
+  __shared__ float red[3 * 4 * 4 * 2 * 64];
   const int nseg = meta[0], ntiles = meta[1];
   if (ntiles == 0) return;
   for (;;) {
@@ -131,10 +182,16 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     const int m0 = mt * kStreamMaxRows;
     const int rows = min(kStreamMaxRows, sg.rows - m0);
-    const int n0 = nt * kStreamBN;
-    if (rows <= 16) stream_tile_bf16<1, GU>(sg, m0, rows, n0);
-    else if (rows <= 32) stream_tile_bf16<2, GU>(sg, m0, rows, n0);
-    else stream_tile_bf16<4, GU>(sg, m0, rows, n0);
+    const int n0 = nt * sg.tn;
+    if (sg.tn == 16) {  // long K: split across the wavefronts
+      if (rows <= 16) stream_tile_bf16<1, GU, 4>(sg, m0, rows, n0, red);
+      else if (rows <= 32) stream_tile_bf16<2, GU, 4>(sg, m0, rows, n0, red);
+      else stream_tile_bf16<4, GU, 4>(sg, m0, rows, n0, red);
+    } else {
+      if (rows <= 16) stream_tile_bf16<1, GU, 1>(sg, m0, rows, n0, red);
+      else if (rows <= 32) stream_tile_bf16<2, GU, 1>(sg, m0, rows, n0, red);
+      else stream_tile_bf16<4, GU, 1>(sg, m0, rows, n0, red);
+    }
   }
 }
 

@@ -15,7 +15,10 @@ constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
 constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
-constexpr int kStreamBN = 64;       // output columns per weight-streaming tile (4 waves x 16)
+// Weight-streaming tiles: the 4 wavefronts split K when K is long (16 output columns per tile),
+// otherwise each takes 16 of 64 output columns over the whole K.
+constexpr int kStreamSplitK = 4096;
+__host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 64; }
 constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
 // fp8 weights (streaming family only): rows per pass, h columns per gate/up tile (one whole
 // 128-column requantisation block), y columns per down tile
@@ -37,6 +40,7 @@ struct Seg {
   float* outs;          // fp8 gate/up: output scales [.][N/128]
   int32_t row0, rows, N, K;
   int32_t tile_base, mtiles, ntiles, expert;
+  int32_t tn;           // output columns per tile
 };
 
 // Where the selection kernel writes its results (all inside the caller's workspace).
@@ -76,6 +80,12 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* coun
 hipError_t launch_gather(const void* x, const float* xs, const int32_t* perm_src, int n, int k,
                          int row_bytes, int nb, void* xp, float* xps, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, const SelectOut& o, hipStream_t s);
+// Decode front end (route + permute + select in one workgroup) when T*k <= 2048.
+bool front_small_fits(int T, int k);
+hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* slot_dst, int32_t* tok, const SelectArgs& sa,
+                              const SelectOut& so, hipStream_t s);
 // Launches both tile families of one GEMM (kGemmGateUp or kGemmDown).
 hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);

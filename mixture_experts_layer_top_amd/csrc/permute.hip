@@ -16,6 +16,8 @@
 //             tok[row] = t (the activation row the GEMM gathers).
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
+#include "select_dev.h"
 
 namespace moe {
 
@@ -136,6 +138,114 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restr
   if (i >= n * nb) return;
   const int row = i / nb, b = i % nb;
   xps[i] = xs[(size_t)(perm_src[row] / k) * nb + b];
+}
+
+// ------------------------------------------------------------------------------------------------
+// Decode front end: for T*k <= 2048, one workgroup of 1024 threads routes every token (one
+// wavefront per token), ranks the slots stably inside LDS (two rounds of 1024, same ballot scheme
+// as perm_count_kernel), scans the histogram, scatters the permutation and selects the tile
+// families -- one launch instead of five.
+// ------------------------------------------------------------------------------------------------
+constexpr int kFrontMax = 2048;
+
+template <int VPL>
+__global__ __launch_bounds__(1024) void front_small_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int32_t* __restrict__ ids,
+                                                           float* __restrict__ w,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm_src,
+                                                           int32_t* __restrict__ slot_dst,
+                                                           int32_t* __restrict__ tok,
+                                                           SelectArgs sa, SelectOut so) {
+  __shared__ int s_ids[kFrontMax];
+  __shared__ int wcnt[16][kMaxE];
+  __shared__ int running[kMaxE];
+  __shared__ int s_off[kMaxE];
+  __shared__ int scan_lds[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = T * k;
+  for (int t = wv; t < T; t += 16) route_token<VPL>(logits, t, E, k, ids, w, s_ids);
+  for (int e = tid; e < E; e += 1024) {
+    running[e] = 0;
+    for (int q = 0; q < 16; ++q) wcnt[q][e] = 0;
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int myrank[2], myexp[2];
+  for (int r = 0; r < 2; ++r) {
+    const int s = r * 1024 + tid;
+    const bool valid = s < n;
+    const int e = valid ? s_ids[s] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int rank_w = __popcll(same & below);
+    const int cnt_w = __popcll(same);
+    const bool leader = valid && rank_w == 0;
+    if (leader) wcnt[wv][e] = cnt_w;
+    __syncthreads();
+    int rk = 0;
+    if (valid) {
+      rk = running[e] + rank_w;
+      for (int q = 0; q < wv; ++q) rk += wcnt[q][e];
+    }
+    myrank[r] = rk;
+    myexp[r] = e;
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&running[e], cnt_w);
+      wcnt[wv][e] = 0;
+    }
+    __syncthreads();
+  }
+  // histogram scan (E <= 512 <= 1024 threads)
+  int v[1], ex[1], tot[1];
+  v[0] = tid < E ? running[tid] : 0;
+  block_scan<1, 16>(v, ex, tot, scan_lds);
+  if (tid < E) {
+    s_off[tid] = ex[0];
+    counts[tid] = v[0];
+    offsets[tid] = ex[0];
+  }
+  if (tid == 0) offsets[E] = n;
+  __syncthreads();
+  for (int r = 0; r < 2; ++r) {
+    const int s = r * 1024 + tid;
+    if (s < n) {
+      const int row = s_off[myexp[r]] + myrank[r];
+      perm_src[row] = s;
+      slot_dst[s] = row;
+      tok[row] = s / k;
+    }
+  }
+  __syncthreads();  // counts/offsets visible to the whole workgroup
+  select_block(sa, so);
+}
+
+bool front_small_fits(int T, int k) { return T * k <= kFrontMax; }
+
+hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* slot_dst, int32_t* tok, const SelectArgs& sa,
+                              const SelectOut& so, hipStream_t s) {
+  if (E <= 64)
+    front_small_kernel<1><<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, perm_src,
+                                             slot_dst, tok, sa, so);
+  else if (E <= 128)
+    front_small_kernel<2><<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, perm_src,
+                                             slot_dst, tok, sa, so);
+  else if (E <= 256)
+    front_small_kernel<4><<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, perm_src,
+                                             slot_dst, tok, sa, so);
+  else
+    front_small_kernel<8><<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, perm_src,
+                                             slot_dst, tok, sa, so);
+  return hipGetLastError();
 }
 
 int permute_nchunk(int n) { return (n + kChunk - 1) / kChunk; }
