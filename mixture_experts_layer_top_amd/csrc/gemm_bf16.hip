@@ -202,38 +202,16 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // 256 y columns).  4 wavefronts as 2 (tokens) x 2 (weights), each 128 x 128 with MFMA 32x32x16:
 // 16 accumulator blocks, 4 A and 4 B fragments per k-substep, every fragment reused 4 times.
 //
-// Memory pipeline: K-steps of 32 through 4 LDS stages of 32 KB (512 rows of 64 B).  Global data goes
-// straight into LDS (global_load_lds_dwordx4, no staging registers) three steps ahead of its use, so
-// 96 KB per CU are in flight while the MFMAs run.  Each step: wait until this wavefront's loads for
-// the step have landed (vmcnt), barrier (then every wavefront's have), issue the loads for step + 3
-// into the stage read in the previous step, then 2 k-substeps of 16 MFMAs.  The stages are distinct
-// LDS arrays so the compiler can tell the asynchronous LDS writes from the reads.  Rows of 64 B keep
-// 4 chunks of 16 B, XOR-swizzled by (row >> 2) & 3 so the 16 lanes of a ds_read_b128 group (16 rows,
-// same chunk) cover all 64 banks.
-//
 // Scheduling: one persistent workgroup per CU.  The tile order puts the m-tiles of one weight tile
 // next to each other; consecutive runs of (CUs per XCD) tiles go to one XCD, so tiles that share
 // weight and activation tiles run side by side on the same L2.  Each XCD has its own queue; a
 // workgroup whose queue is empty takes work from the other XCDs' queues.
 // ------------------------------------------------------------------------------------------------
-constexpr int BM = kMfmaBM, BK = 32, NSTAGE = 4;
+constexpr int BM = kMfmaBM;
 constexpr int BNW = 256;                  // weight rows per tile
 constexpr int LROWS = BM + BNW;           // LDS rows per stage
-constexpr int ROWB = BK * 2;              // bytes per LDS row (64)
-constexpr int STAGE = LROWS * ROWB;       // bytes per stage (32 KB)
-constexpr int DMA_PER_STAGE = STAGE / (256 * 16);  // 16-byte loads per thread per stage (8)
 
 typedef __attribute__((address_space(3))) void lds_void;
-__shared__ __attribute__((aligned(1024))) uint8_t g_st0[STAGE];
-__shared__ __attribute__((aligned(1024))) uint8_t g_st1[STAGE];
-__shared__ __attribute__((aligned(1024))) uint8_t g_st2[STAGE];
-__shared__ __attribute__((aligned(1024))) uint8_t g_st3[STAGE];
-template <int S> __device__ __forceinline__ uint8_t* stage_ptr() {
-  return S == 0 ? g_st0 : S == 1 ? g_st1 : S == 2 ? g_st2 : g_st3;
-}
-
-// byte offset of 16-byte chunk `c` (0..3) of LDS row `r`
-__device__ __forceinline__ int lds_off(int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // s_waitcnt with vmcnt(vm) and lgkmcnt(lg), expcnt left at its maximum (gfx9 encoding)
 #define MOE_WAITCNT(vm, lg) \
@@ -286,160 +264,13 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
     }
   }
 
-template <bool GU>
-struct MfmaTile {
-  // Load slot j of wavefront wv fills LDS rows [16*(4*j + wv), +16): slots 0..3 token rows,
-  // 4..7 weight rows (gate/up: slots 4,5 gate rows 0..127, slots 6,7 up rows 0..127).  The base of
-  // a slot is therefore fixed by j; only the per-lane offset depends on the row.
-  const char* abase;
-  const char* wbase0;
-  const char* wbase1;
-  uint32_t off[DMA_PER_STAGE];      // per lane: byte offset of this lane's 16 bytes at k = 0
-  int wvu;                          // wavefront index (uniform)
-  int arow[4], brow[4];             // this lane's fragment rows (A = weights, B = tokens)
-  f32x16 acc[4][4];
-
-  __device__ __forceinline__ const char* slot_base(int j) const {
-    return j < 4 ? abase : ((!GU || j < 6) ? wbase0 : wbase1);
-  }
-
-  __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0) {
-    const int lane = threadIdx.x & 63;
-    wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wvu & 1, wn = wvu >> 1;
-    const uint32_t rowbytes = (uint32_t)sg.K * 2;
-    abase = static_cast<const char*>(sg.a);
-    wbase0 = static_cast<const char*>(sg.w0);
-    wbase1 = static_cast<const char*>(GU ? sg.w1 : sg.w0);
-#pragma unroll
-    for (int j = 0; j < DMA_PER_STAGE; ++j) {
-      const int r = 16 * (4 * j + wvu) + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);  // global chunk that lands in this lane's slot
-      if (j < 4) {
-        int rr = r < rows ? r : rows - 1;  // padded rows re-read a valid row, never stored
-        const int gr = sg.row0 + m0 + rr;
-        const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-        off[j] = (uint32_t)src * rowbytes + c * 16;
-      } else {
-        int wr = GU ? n0 + ((r - BM) & 127) : n0 + (r - BM);
-        wr = wr < sg.N ? wr : sg.N - 1;  // half-full edge tile of the down GEMM
-        off[j] = (uint32_t)wr * rowbytes + c * 16;
-      }
-    }
-    const int l32 = lane & 31;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
-                   : (BM + wn * 128 + a * 32 + l32);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
-  }
-
-  template <int S>
-  __device__ __forceinline__ void issue(int kt) {
-    uint8_t* st = stage_ptr<S>() + wvu * 16 * ROWB;
-    const uint32_t ko = (uint32_t)kt * ROWB;
-#pragma unroll
-    for (int j = 0; j < DMA_PER_STAGE; ++j)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<__attribute__((address_space(1))) const void*>((gchar*)slot_base(j) + off[j] + ko),
-          (lds_void*)(st + j * 64 * ROWB), 16, 0, 0);
-  }
-
-  // Fragments of k-substep kk (0 or 1) of stage S into f (4 A then 4 B).
-  template <int S>
-  __device__ __forceinline__ void read_frags(int kk, bf16x8 (&f)[8]) const {
-    const uint8_t* st = stage_ptr<S>();
-    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(arow[a], c)));
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[4 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off(brow[b], c)));
-  }
-
-  __device__ __forceinline__ void mfmas(const bf16x8 (&f)[8]) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(f[a], f[4 + b], acc[a][b]);
-  }
-
-  // Step kt on stage S.  On entry f0 holds substep 0 of stage S.  The barrier sits between the two
-  // halves so the fragments of the next half are always already in registers:
-  //   first half : MFMAs on substep 0 while substep 1 of stage S is read;
-  //   wait until this wavefront's fragment reads are done (so it no longer needs stage S) and its
-  //   loads of stage S+1 have landed; barrier (now stage S+1 is complete and stage S is free);
-  //   second half: loads for step kt+4 into stage S (clamped at the tail so the vmcnt count stays
-  //   exact), MFMAs on substep 1 while substep 0 of stage S+1 is read into f0.
-  // Loads are issued three steps before their first read.
-  template <int S>
-  __device__ __forceinline__ void step(int kt, int nk, bf16x8 (&f0)[8], bf16x8 (&f1)[8]) {
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags<S>(1, f1);
-    mfmas(f0);
-    // issue order: the 8 fragment reads right behind the first 8 MFMAs, then the other 8 MFMAs
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_WAITCNT(2 * DMA_PER_STAGE, 0);
-    __builtin_amdgcn_s_barrier();
-    issue<S>(min(kt + 4, nk - 1));
-    read_frags<(S + 1) & 3>(0, f0);
-    mfmas(f1);
-    // one global->LDS load and one fragment read behind each of the first 8 MFMAs
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // The first four stages of a tile (may be issued while the previous tile's epilogue runs).
-  __device__ __forceinline__ void prologue() {
-    issue<0>(0);
-    issue<1>(1);
-    issue<2>(2);
-    issue<3>(3);
-  }
-
-  __device__ __forceinline__ void run(int K) {
-    const int nk = K / BK;  // K is a multiple of 128, so nk is a multiple of 4 (>= 4)
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    MOE_WAITCNT(3 * DMA_PER_STAGE, 15);
-    __builtin_amdgcn_s_barrier();
-    bf16x8 f0[8], f1[8];
-    read_frags<0>(0, f0);
-    for (int kt = 0; kt < nk; kt += 4) {
-      step<0>(kt, nk, f0, f1);
-      step<1>(kt + 1, nk, f0, f1);
-      step<2>(kt + 2, nk, f0, f1);
-      step<3>(kt + 3, nk, f0, f1);
-    }
-    MOE_WAITCNT(0, 0);                  // every load landed, the last (unused) reads done
-    __builtin_amdgcn_s_barrier();       // stages free for the next tile
-  }
-
-  __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
-    MfmaTileStore<GU>(acc, sg, m0, rows, n0);
-  }
-};
-
 // ------------------------------------------------------------------------------------------------
-// The same tile with K-steps of 64: two LDS stages of 64 KB (512 rows of 128 B), so every
-// global->LDS instruction moves 8 whole 128-byte lines (with 64-byte rows each line would be
-// requested twice, one step apart).  Rows of 128 B keep 8 chunks XOR-swizzled by (row >> 1) & 7.
+// Memory pipeline: K-steps of 64 through two LDS stages of 64 KB (512 rows of 128 B).  Global data
+// goes straight into LDS (global_load_lds_dwordx4, no staging registers), every instruction moving
+// 8 whole 128-byte lines.  Rows keep 8 chunks of 16 B XOR-swizzled by (row >> 1) & 7, so the 16
+// lanes a ds_read_b128 serves together (16 rows, one chunk index) cover all 64 banks.  The stages
+// are distinct LDS arrays so the compiler can tell the asynchronous LDS writes from the reads, and
+// waits are explicit (vmcnt) around a plain barrier so prefetches stay in flight.
 // Step kt on stage S: substeps 0..2 run while substeps 1..3 are read; wait until this wavefront's
 // reads are done and every load it issued has landed; barrier (stage S^1 complete, stage S free);
 // loads for step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
@@ -483,10 +314,11 @@ struct MfmaTile64 {
       const int r = 32 * j + 8 * wvu + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       if (j < 8) {
-        int rr = r < rows ? r : rows - 1;
-        const int gr = sg.row0 + m0 + rr;
+        // padded rows (r >= rows) all read the first row's first 16 bytes: one coalesced request
+        // per instruction instead of eight lines; their LDS rows are never stored
+        const int gr = sg.row0 + m0 + (r < rows ? r : 0);
         const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-        off[j] = (uint32_t)src * rowbytes + c * 16;
+        off[j] = (uint32_t)src * rowbytes + (r < rows ? c * 16 : 0);
       } else {
         int wr = GU ? n0 + ((r - BM) & 127) : n0 + (r - BM);
         wr = wr < sg.N ? wr : sg.N - 1;
@@ -622,11 +454,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   if (ntiles == 0) return;
   const int chunk = max(1, (int)gridDim.x / kXcds);
   int q = 0;
-#ifndef MOE_MFMA_BK32
   MfmaTile64<GU> tile;
-#else
-  MfmaTile<GU> tile;
-#endif
   struct Cur { int si, m0, rows, n0; };
   auto claim = [&](Cur& c) -> bool {
     const int t = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);

@@ -223,11 +223,13 @@ __global__ __launch_bounds__(1024) void front_small_kernel(const float* __restri
       tok[row] = s / k;
     }
   }
-  __syncthreads();  // counts/offsets visible to the whole workgroup
-  select_block(sa, so);
+  __syncthreads();
+  select_block(sa, so, running, s_off);
 }
 
-bool front_small_fits(int T, int k) { return T * k <= kFrontMax; }
+// One wavefront routes T/16 tokens one after the other, so the fused path only pays off while
+// that is at most two tokens.
+bool front_small_fits(int T, int k) { return T <= 32 && T * k <= kFrontMax; }
 
 hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                               int32_t* counts, int32_t* offsets, int32_t* perm_src,

@@ -22,14 +22,17 @@ __device__ __forceinline__ int pick_family(int c, int config, int fp8) {
 // place in its family's list.  Order inside a family: experts with two or more m-tiles first
 // ("heavy first", so the persistent queues start with the longest work), then by expert id; the
 // ranks and tile bases come from one block-wide scan of 12 per-expert counts.  Every thread of the
-// block must call this (it contains barriers).
-__device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOut& o) {
+// block must call this (it contains barriers).  Counts and offsets come from LDS when the caller
+// has them there (lds_counts, lds_offsets), else from a.counts / a.offsets.
+__device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOut& o,
+                                             const int* lds_counts = nullptr,
+                                             const int* lds_offsets = nullptr) {
   __shared__ int scan_lds[16 * 12];
   const int e = threadIdx.x;
   const int nexp = a.E + (a.has_shared ? 1 : 0);
   int c = 0, fm = -1;
   if (e < nexp) {
-    c = (e < a.E) ? gload_i32(a.counts, e) : a.T;
+    c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
     fm = pick_family(c, a.config, a.fp8);
   }
   const bool shared = e == a.E;
@@ -55,7 +58,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   if (fm >= 0) {
     const int rank = (cls == 1 ? tot[fm * 2] : 0) + ex[fm * 2 + cls];
     const size_t wb = a.fp8 ? 1 : 2;
-    const int row0 = shared ? 0 : gload_i32(a.offsets, e);
+    const int row0 = shared ? 0 : (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e));
     const int kb_d = a.d / 128, kb_f = ffe / 128;
     for (int g = 0; g < 2; ++g) {
       const int ti = 4 + (g * 2 + fm) * 2;
