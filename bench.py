@@ -19,6 +19,7 @@ import os
 import statistics
 import sys
 import time
+from dataclasses import replace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -27,7 +28,6 @@ METRIC = "MoE-layer tokens/s + % HBM peak (decode) / % MFMA peak (prefill), 1 GP
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense MFMA bf16
 PEAK_FP8_TFLOPS = 5000.0       # dense MFMA fp8
-PREFILL_MIN_T = 4096           # prefill workloads are judged against MFMA, decode against HBM
 
 
 def workload(args):
@@ -35,10 +35,11 @@ def workload(args):
     name = args.config
     if name == "tiny":
         return I.TINY
-    if name == "mixtral_prefill":
-        return I.MIXTRAL
-    if name == "kimi_prefill":
-        return I.KIMI
+    if name in ("mixtral_prefill", "kimi_prefill"):
+        base = I.MIXTRAL if name == "mixtral_prefill" else I.KIMI
+        if args.T and args.T != base.T:
+            return replace(base, T=args.T, name=f"{base.name}_T{args.T}")
+        return base
     if name == "dsv3_decode":
         return I.dsv3_point(args.T or 256, args.alpha if args.alpha is not None else 1.0)
     if name == "fp8_dsv3_decode":
@@ -166,7 +167,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill",
                     choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode"])
-    ap.add_argument("--T", type=int, default=None, help="tokens (decode workloads)")
+    ap.add_argument("--T", type=int, default=None, help="tokens (overrides the workload's batch)")
     ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
     ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
     ap.add_argument("--flush", action="store_true",
@@ -267,8 +268,9 @@ def main() -> int:
         timing = "wall clock over the timed steps (synchronised before and after)"
     value = p.T / (ms_per_step * 1e-3)
 
-    prefill = p.T >= PREFILL_MIN_T
     peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" else PEAK_BF16_TFLOPS
+    # the dominant kernel's bound: whichever of its algorithmic flops and bytes takes longer at peak
+    prefill = alg["flop_gu"] / (peak_flops * 1e12) > alg["bytes_gu"] / (PEAK_HBM_GBS * 1e9)
     gu_ms = statistics.mean(gu_launch_ms)
     if prefill:
         achieved = alg["flop_gu"] / (gu_ms * 1e-3) / 1e12

@@ -58,13 +58,13 @@ enum moe_dtype {
   MOE_DTYPE_FP8_E4M3 = 1
 };
 
-/* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert from
- * the live histogram; the others force one family for every expert (used by tests to cover each). */
+/* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert and per
+ * GEMM from the live histogram; the others force one family for every expert (used by tests to
+ * cover each).  Block-scaled fp8 weights always use the weight-streaming family. */
 enum moe_config {
   MOE_CONFIG_AUTO = -1,
-  MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: all of an expert's rows (<= 64) per pass */
-  MOE_CONFIG_MFMA128 = 1, /* LDS-tiled MFMA tiles of 128 rows */
-  MOE_CONFIG_MFMA256 = 2  /* LDS-tiled MFMA tiles of 256 rows */
+  MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
+  MOE_CONFIG_MFMA = 1    /* LDS-tiled MFMA tiles of 256 rows x 256 weight rows */
 };
 
 typedef struct moe_problem {

@@ -64,7 +64,7 @@ int check_problem(const moe_problem* p) {
   if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
-  if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA256) return MOE_ERR_INVALID_ARG;
+  if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 

@@ -11,6 +11,10 @@ enum Family { kFamStream = 0, kFamMfma = 1, kNumFam = 2 };
 enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
 
 constexpr int kStreamMaxRows = 64;  // rows per weight-streaming tile
+// Automatic selection: an expert takes the weight-streaming family for a GEMM while its row
+// count is at most this, the LDS-tiled MFMA family above it.
+constexpr int kStreamRowsGateUp = 8;
+constexpr int kStreamRowsDown = 16;
 constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
@@ -67,9 +71,12 @@ struct SelectArgs {
 };
 
 // ints per (gemm, family): nseg, ntiles, then kXcds queue counters (the stream family uses the
-// first), zeroed by the selection kernel before each GEMM.
+// first), zeroed by the selection kernel before each GEMM, then the number of heavy tiles (those
+// of experts with two or more m-tiles, which come first in tile order).
 constexpr int kMetaStride = 16;
 constexpr int kMetaQueue = 2;
+constexpr int kMetaHeavy = kMetaQueue + kXcds;
+static_assert(kMetaHeavy < kMetaStride, "meta layout");
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t s);

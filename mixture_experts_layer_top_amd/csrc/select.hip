@@ -5,15 +5,19 @@
 // buckets ignore the per-expert distribution that decides tile padding and memory reuse; the
 // dispatch runtime reads the live histogram on the GPU, with no CPU-GPU synchronisation.
 //
-// Here the choice is made per expert, from its row count c_e, inside one workgroup that runs
-// between the permutation and the GEMMs:
-//   c_e <= 64  -> weight-streaming tiles: the expert's rows ride along while its weights stream
-//                 from HBM once (decode-sized experts are bandwidth-bound: c_e FLOP per weight byte);
-//   c_e  > 64  -> LDS-tiled MFMA tiles of 256 rows (padding only the last tile of the expert).
-// Block-scaled fp8 experts always take the streaming family (up to 128 rows per pass).
-// Experts with several m-tiles come first in their family's list, so the persistent GEMM queues
-// start with the longest work.  Experts with no rows get no segment and their weights are never
-// read.
+// Here the choice is made per expert and per GEMM, from the expert's row count c_e, inside one
+// workgroup that runs between the permutation and the GEMMs:
+//   c_e <= 8 (gate/up) or 16 (down) -> weight-streaming tiles: the expert's rows ride along while
+//                 its weights stream from HBM once (a handful of rows: c_e FLOP per weight byte);
+//   above that -> LDS-tiled MFMA tiles of 256 rows.  A tile runs MFMAs only for its 32-row blocks
+//                 that hold rows, so a light expert's tile streams its weights through LDS once and
+//                 costs MFMA time in proportion to its rows.
+// The streaming family re-reads an expert's rows from L2 for every 16 weight rows, which is what
+// caps it at a few rows per expert.  Block-scaled fp8 experts always take the streaming family (up
+// to 128 rows per pass).  Inside a (GEMM, family) list, experts with several m-tiles come first
+// ("heavy"); the MFMA kernels spread the light tiles evenly between the heavy ones, so HBM-bound
+// and MFMA-bound tiles run side by side.  Experts with no rows get no segment and their weights are
+// never read.
 #include "select_dev.h"
 
 namespace moe {

@@ -10,69 +10,89 @@ namespace moe {
 
 constexpr int kSelMax = kSegCap;
 
-__device__ __forceinline__ int pick_family(int c, int config, int fp8) {
+__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
   if (c <= 0) return -1;
   if (fp8) return kFamStream;  // block-scaled fp8 experts: streaming family only
   if (config == 0) return kFamStream;
   if (config >= 1) return kFamMfma;
-  return c <= kStreamMaxRows ? kFamStream : kFamMfma;
+  return c <= (g == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown) ? kFamStream : kFamMfma;
 }
 
-// Per expert (one thread each, blockDim.x = 1024 >= E + 1): family, tile counts, and the segment's
-// place in its family's list.  Order inside a family: experts with two or more m-tiles first
-// ("heavy first", so the persistent queues start with the longest work), then by expert id; the
-// ranks and tile bases come from one block-wide scan of 12 per-expert counts.  Every thread of the
-// block must call this (it contains barriers).  Counts and offsets come from LDS when the caller
-// has them there (lds_counts, lds_offsets), else from a.counts / a.offsets.
+// Per expert (one thread each, blockDim.x = 1024 >= E + 1) and per GEMM: family, tile counts, and
+// the segment's place in its (GEMM, family) list.  Order inside a list: experts with two or more
+// m-tiles first ("heavy"), then the rest ("light"), each by expert id; the ranks and tile bases
+// come from one block-wide scan of 16 per-expert counts.  Every thread of the block must call this
+// (it contains barriers).  Counts and offsets come from LDS when the caller has them there
+// (lds_counts, lds_offsets), else from a.counts / a.offsets.
 __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOut& o,
                                              const int* lds_counts = nullptr,
                                              const int* lds_offsets = nullptr) {
-  __shared__ int scan_lds[16 * 12];
+  __shared__ int scan_lds[16 * 16];
   const int e = threadIdx.x;
   const int nexp = a.E + (a.has_shared ? 1 : 0);
-  int c = 0, fm = -1;
-  if (e < nexp) {
-    c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
-    fm = pick_family(c, a.config, a.fp8);
-  }
+  int c = 0;
+  if (e < nexp) c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
-  const int tm = a.fp8 ? kStreamMaxRows8 : (fm == kFamStream) ? kStreamMaxRows : kMfmaBM;
-  const int tn_gu = a.fp8 ? kStream8BNGateUp : (fm == kFamStream) ? stream_bn(a.d) : kMfmaBNGateUp;
-  const int tn_dn = a.fp8 ? kStream8BNDown : (fm == kFamStream) ? stream_bn(ffe) : kMfmaBNDown;
-  const int mtiles = (c + tm - 1) / tm;
-  // f and d are multiples of 128; a down tile of 256 columns may be half full at the edge
-  const int nt_gu = ffe / tn_gu, nt_dn = (a.d + tn_dn - 1) / tn_dn;
-  const int cls = mtiles >= 2 ? 0 : 1;
-  // v[4*f + 2*... ]: flags [fam][cls] (4), then tiles [gemm][fam][cls] (8)
-  int v[12], ex[12], tot[12];
+  int fm[2], mt[2], nt[2], tn[2], cls[2];
+  // v: flags [gemm][fam][cls] (8), then tiles [gemm][fam][cls] (8)
+  int v[16], ex[16], tot[16];
 #pragma unroll
-  for (int i = 0; i < 12; ++i) v[i] = 0;
-  if (fm >= 0) {
-    v[fm * 2 + cls] = 1;
-    v[4 + (kGemmGateUp * 2 + fm) * 2 + cls] = mtiles * nt_gu;
-    v[4 + (kGemmDown * 2 + fm) * 2 + cls] = mtiles * nt_dn;
+  for (int i = 0; i < 16; ++i) v[i] = 0;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8) : -1;
+    const bool st = fm[g] == kFamStream;
+    const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
+    if (g == kGemmGateUp) {
+      tn[g] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
+      nt[g] = ffe / tn[g];  // f is a multiple of 128
+    } else {
+      tn[g] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
+      nt[g] = (a.d + tn[g] - 1) / tn[g];  // a down tile of 256 columns may be half full at the edge
+    }
+    mt[g] = (c + tm - 1) / tm;
+    cls[g] = mt[g] >= 2 ? 0 : 1;
+    // (all indexing below is static after unrolling, so nothing lands in scratch memory)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (fm[g] >= 0 && i == (g * 2 + fm[g]) * 2 + cls[g]) {
+        v[i] = 1;
+        v[8 + i] = mt[g] * nt[g];
+      }
   }
-  block_scan<12, 16>(v, ex, tot, scan_lds);
+  block_scan<16, 16>(v, ex, tot, scan_lds);
+  int rank[2], tbase[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    rank[g] = tbase[g] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (fm[g] >= 0 && i == (g * 2 + fm[g]) * 2 + cls[g]) {
+        // light experts follow all heavy ones of their list
+        rank[g] = ((i & 1) ? tot[i - 1] : 0) + ex[i];
+        tbase[g] = ((i & 1) ? tot[8 + i - 1] : 0) + ex[8 + i];
+      }
+  }
 
-  if (fm >= 0) {
-    const int rank = (cls == 1 ? tot[fm * 2] : 0) + ex[fm * 2 + cls];
-    const size_t wb = a.fp8 ? 1 : 2;
-    const int row0 = shared ? 0 : (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e));
-    const int kb_d = a.d / 128, kb_f = ffe / 128;
+  const size_t wb = a.fp8 ? 1 : 2;
+  const int kb_d = a.d / 128, kb_f = ffe / 128;
+  const int row0 = (e < nexp && !shared) ? (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e)) : 0;
+  {
+#pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int ti = 4 + (g * 2 + fm) * 2;
+      if (fm[g] < 0) continue;
       Seg sg;
       sg.row0 = row0;
       sg.rows = c;
-      sg.mtiles = mtiles;
+      sg.mtiles = mt[g];
       sg.expert = e;
-      sg.tile_base = (cls == 1 ? tot[ti] : 0) + ex[ti + cls];
-      sg.tn = (g == kGemmGateUp) ? tn_gu : tn_dn;
+      sg.tile_base = tbase[g];
+      sg.tn = tn[g];
       if (g == kGemmGateUp) {
         sg.N = ffe;
         sg.K = a.d;
-        sg.ntiles = nt_gu;
+        sg.ntiles = nt[g];
         sg.a = a.x;
         sg.as = a.xs;
         sg.tok = shared ? nullptr : a.tok;
@@ -96,7 +116,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       } else {
         sg.N = a.d;
         sg.K = ffe;
-        sg.ntiles = nt_dn;
+        sg.ntiles = nt[g];
         sg.tok = nullptr;
         sg.w1 = nullptr;
         sg.s1 = nullptr;
@@ -115,15 +135,24 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
           sg.out = a.y;
         }
       }
-      o.segs[((size_t)g * kNumFam + fm) * kSelMax + rank] = sg;
+      o.segs[((size_t)g * kNumFam + fm[g]) * kSelMax + rank[g]] = sg;
     }
   }
-  // per (gemm, family): segment count, tile count, zeroed queues
-  if (e < 2 * kNumFam) {
-    const int g = e / kNumFam, f = e % kNumFam;
-    o.meta[e * kMetaStride + 0] = tot[f * 2] + tot[f * 2 + 1];
-    o.meta[e * kMetaStride + 1] = tot[4 + (g * 2 + f) * 2] + tot[4 + (g * 2 + f) * 2 + 1];
-    for (int q = kMetaQueue; q < kMetaStride; ++q) o.meta[e * kMetaStride + q] = 0;
+  // per (gemm, family): segment count, tile count, zeroed queues, heavy tile count
+  if (e < 2 * kNumFam) {  // e = gemm * kNumFam + family; its flags and tiles sit at 2e, 2e + 1
+    int nseg = 0, ntl = 0, heavy = 0;
+#pragma unroll
+    for (int i = 0; i < 2 * kNumFam; ++i)
+      if (i == e) {
+        nseg = tot[2 * i] + tot[2 * i + 1];
+        ntl = tot[8 + 2 * i] + tot[8 + 2 * i + 1];
+        heavy = tot[8 + 2 * i];
+      }
+    int32_t* m = o.meta + e * kMetaStride;
+    m[0] = nseg;
+    m[1] = ntl;
+    for (int q = kMetaQueue; q < kMetaQueue + kXcds; ++q) m[q] = 0;
+    m[kMetaHeavy] = heavy;
   }
 }
 

@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 DTYPE_BF16, DTYPE_FP8 = 0, 1
-CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA128, CONFIG_MFMA256 = -1, 0, 1, 2
+CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 
