@@ -115,9 +115,15 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
   }
 }
 
-hipError_t launch_gemms(const SelectOut& o, int gemm, int fp8, hipStream_t s) {
-  return fp8 ? moe::launch_gemms_fp8(o, gemm, device_cus(), s)
-             : moe::launch_gemms_bf16(o, gemm, device_cus(), s);
+// max_rows bounds the rows of any one expert; when no expert can pass the streaming threshold the
+// MFMA kernel (whose queue would be empty) is not launched.
+hipError_t launch_gemms(const SelectOut& o, int gemm, int fp8, int config, int64_t max_rows,
+                        hipStream_t s) {
+  if (fp8) return moe::launch_gemms_fp8(o, gemm, device_cus(), s);
+  const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
+  const bool stream = config != MOE_CONFIG_MFMA;
+  const bool mfma = config == MOE_CONFIG_MFMA || (config == MOE_CONFIG_AUTO && max_rows > thr);
+  return moe::launch_gemms_bf16(o, gemm, device_cus(), stream, mfma, s);
 }
 }  // namespace
 
@@ -238,8 +244,9 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.y = y_perm;
   SelectOut o{f.segs, f.meta};
   hipError_t e = launch_select(a, o, stream);
-  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, stream);
-  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, stream);
+  const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
+  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, p->config, n, stream);
+  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, p->config, n, stream);
   return hip_status(e);
 }
 
@@ -374,9 +381,10 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
     if (e == hipSuccess) e = launch_select(a, o, stream);
     if (e == hipSuccess) e = mark(4);
   }
-  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, stream);
+  // each token routes to k distinct experts, so no expert (nor the shared one) holds more than T rows
+  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, p->config, T, stream);
   if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, stream);
+  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, p->config, T, stream);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)
     e = launch_combine(L.y, slot_dst, wts, T, k, d, p->has_shared ? L.ffn.y_sh : nullptr, out,

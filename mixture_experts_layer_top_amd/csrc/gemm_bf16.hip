@@ -517,17 +517,18 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   }
 }
 
-hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, hipStream_t s) {
+hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, bool stream, bool mfma,
+                             hipStream_t s) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
   if (g == kGemmGateUp) {
-    gemm_stream_bf16<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm);
+    if (stream) gemm_stream_bf16<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm);
   } else {
-    gemm_stream_bf16<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm);
+    if (stream) gemm_stream_bf16<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm);
   }
   return hipGetLastError();
 }

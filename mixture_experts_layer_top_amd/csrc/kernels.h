@@ -94,7 +94,9 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
                               int32_t* slot_dst, int32_t* tok, const SelectArgs& sa,
                               const SelectOut& so, hipStream_t s);
 // Launches both tile families of one GEMM (kGemmGateUp or kGemmDown).
-hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
+// Launches the persistent kernel of each family that may hold tiles (the other's queue is empty).
+hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, bool stream, bool mfma,
+                             hipStream_t s);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
 hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
                           int d, const void* shared_y, void* out, hipStream_t s);

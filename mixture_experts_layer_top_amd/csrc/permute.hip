@@ -162,7 +162,7 @@ __global__ __launch_bounds__(1024) void front_small_kernel(const float* __restri
   __shared__ int wcnt[16][kMaxE];
   __shared__ int running[kMaxE];
   __shared__ int s_off[kMaxE];
-  __shared__ int scan_lds[16];
+  __shared__ int scan_lds[block_scan_lds(1)];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = T * k;
   for (int t = wv; t < T; t += 16) route_token<VPL>(logits, t, E, k, ids, w, s_ids);

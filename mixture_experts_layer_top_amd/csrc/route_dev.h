@@ -78,38 +78,58 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   }
 }
 
-// Block-wide exclusive scan of NA values per thread (blockDim.x = 64 * NWAVE), with totals.
-// `lds` holds NWAVE * NA ints.  Contains __syncthreads: every thread of the block must call it.
+// Inclusive prefix sum inside each row of 16 lanes (DPP row shifts; lanes shifted in from outside
+// the row read 0).
+__device__ __forceinline__ int row16_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  return x;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront: row scans, then lane 15 is broadcast
+// into rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = row16_incl_scan(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// LDS ints block_scan needs for NA values per thread.
+constexpr int block_scan_lds(int na) { return 33 * na; }
+
+// Block-wide exclusive scan of NA values per thread (blockDim.x = 64 * NWAVE, NWAVE <= 16), with
+// totals.  Wavefront scans, then one 16-lane row scan per value over the wavefront totals.
+// `lds` holds block_scan_lds(NA) ints.  Contains __syncthreads: every thread of the block must
+// call it.
 template <int NA, int NWAVE>
 __device__ __forceinline__ void block_scan(const int (&v)[NA], int (&excl)[NA], int (&tot)[NA],
                                            int* lds) {
+  static_assert(NWAVE <= 16 && NA * 16 <= 64 * NWAVE, "block_scan shape");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) incl[i] = v[i];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int u = __shfl_up(incl[i], off);
-      if (lane >= off) incl[i] += u;
-    }
-  }
+  for (int i = 0; i < NA; ++i) incl[i] = wave_incl_scan(v[i]);
+  // lds[i * 16 + w]: wavefront totals (rows of waves that do not exist are 0)
   if (lane == 63) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) lds[wv * NA + i] = incl[i];
+    for (int i = 0; i < NA; ++i) lds[i * 16 + wv] = incl[i];
+  }
+  if (NWAVE < 16 && threadIdx.x < NA * 16 && (threadIdx.x & 15) >= NWAVE) lds[threadIdx.x] = 0;
+  __syncthreads();
+  if (threadIdx.x < NA * 16) {  // thread i * 16 + w: value i, wavefront w
+    const int s = lds[threadIdx.x];
+    const int inc = row16_incl_scan(s);
+    lds[NA * 16 + threadIdx.x] = inc - s;
+    if ((threadIdx.x & 15) == 15) lds[2 * NA * 16 + (threadIdx.x >> 4)] = inc;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    int base = 0, all = 0;
-    for (int w = 0; w < NWAVE; ++w) {
-      const int s = lds[w * NA + i];
-      base += (w < wv) ? s : 0;
-      all += s;
-    }
-    excl[i] = base + incl[i] - v[i];
-    tot[i] = all;
+    excl[i] = lds[NA * 16 + i * 16 + wv] + incl[i] - v[i];
+    tot[i] = lds[2 * NA * 16 + i];
   }
   __syncthreads();
 }

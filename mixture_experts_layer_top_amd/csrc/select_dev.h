@@ -27,7 +27,7 @@ __device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
 __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOut& o,
                                              const int* lds_counts = nullptr,
                                              const int* lds_offsets = nullptr) {
-  __shared__ int scan_lds[16 * 16];
+  __shared__ int scan_lds[block_scan_lds(16)];
   const int e = threadIdx.x;
   const int nexp = a.E + (a.has_shared ? 1 : 0);
   int c = 0;
