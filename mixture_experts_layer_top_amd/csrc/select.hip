@@ -13,7 +13,9 @@
 //                 that hold rows, so a light expert's tile streams its weights through LDS once and
 //                 costs MFMA time in proportion to its rows.
 // The streaming family re-reads an expert's rows from L2 for every 16 weight rows, which is what
-// caps it at a few rows per expert.  Block-scaled fp8 experts always take the streaming family (up
+// caps it at a few rows per expert.  For a down GEMM with long K (d_ff >= 4096) an expert whose
+// last 256-row m-tile would hold at most 64 rows sends those rows to the streaming family: such a
+// tile costs nearly a full tile's LDS-load time, and a few of them can add a whole round of tiles.  Block-scaled fp8 experts always take the streaming family (up
 // to 128 rows per pass).  Inside a (GEMM, family) list, experts with several m-tiles come first
 // ("heavy"); the MFMA kernels spread the light tiles evenly between the heavy ones, so HBM-bound
 // and MFMA-bound tiles run side by side.  Experts with no rows get no segment and their weights are

@@ -34,109 +34,134 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   if (e < nexp) c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
-  int fm[2], mt[2], nt[2], tn[2], cls[2];
+  // Up to three segments per expert: gate/up, down, and the down GEMM's tail rows (see below).
+  // Segment j: gemm gj, family fm[j] (-1: none), rows [r0[j], r0[j] + nr[j]) of the expert.
+  constexpr int NS = 3;
+  int fm[NS], r0[NS], nr[NS], mt[NS], nt[NS], tn[NS], cls[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    fm[j] = (j < 2 && e < nexp) ? pick_family(c, g, a.config, a.fp8) : -1;
+    r0[j] = 0;
+    nr[j] = c;
+  }
+  // A down GEMM with long K spends the same LDS load time on a 256-row tile whatever its rows, so
+  // an expert whose last m-tile would hold at most kStreamMaxRows rows hands those rows to the
+  // weight-streaming family (its weights stream once more, at HBM rate) instead of adding one
+  // nearly empty MFMA tile per output tile.
+  if (fm[1] == kFamMfma && a.config < 0 && ffe >= kStreamSplitK && c > kMfmaBM) {
+    const int tail = c - (c - 1) / kMfmaBM * kMfmaBM;
+    if (tail <= kStreamMaxRows) {
+      nr[1] = c - tail;
+      fm[2] = kFamStream;
+      r0[2] = c - tail;
+      nr[2] = tail;
+    }
+  }
   // v: flags [gemm][fam][cls] (8), then tiles [gemm][fam][cls] (8)
   int v[16], ex[16], tot[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = 0;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8) : -1;
-    const bool st = fm[g] == kFamStream;
+  for (int j = 0; j < NS; ++j) {
+    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    const bool st = fm[j] == kFamStream;
     const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
     if (g == kGemmGateUp) {
-      tn[g] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
-      nt[g] = ffe / tn[g];  // f is a multiple of 128
+      tn[j] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
+      nt[j] = ffe / tn[j];  // f is a multiple of 128
     } else {
-      tn[g] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
-      nt[g] = (a.d + tn[g] - 1) / tn[g];  // a down tile of 256 columns may be half full at the edge
+      tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
+      nt[j] = (a.d + tn[j] - 1) / tn[j];  // a down tile of 256 columns may be half full at the edge
     }
-    mt[g] = (c + tm - 1) / tm;
-    cls[g] = mt[g] >= 2 ? 0 : 1;
+    mt[j] = (nr[j] + tm - 1) / tm;
+    cls[j] = mt[j] >= 2 ? 0 : 1;
     // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (fm[g] >= 0 && i == (g * 2 + fm[g]) * 2 + cls[g]) {
-        v[i] = 1;
-        v[8 + i] = mt[g] * nt[g];
+      if (fm[j] >= 0 && i == (g * 2 + fm[j]) * 2 + cls[j]) {
+        v[i] += 1;
+        v[8 + i] += mt[j] * nt[j];
       }
   }
   block_scan<16, 16>(v, ex, tot, scan_lds);
-  int rank[2], tbase[2];
+  // a down tail segment shares its (gemm, family, class) list with no other segment of the expert:
+  // the main down segment is MFMA, the gate/up one belongs to the other gemm
+  int rank[NS], tbase[NS];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    rank[g] = tbase[g] = 0;
+  for (int j = 0; j < NS; ++j) {
+    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    rank[j] = tbase[j] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (fm[g] >= 0 && i == (g * 2 + fm[g]) * 2 + cls[g]) {
+      if (fm[j] >= 0 && i == (g * 2 + fm[j]) * 2 + cls[j]) {
         // light experts follow all heavy ones of their list
-        rank[g] = ((i & 1) ? tot[i - 1] : 0) + ex[i];
-        tbase[g] = ((i & 1) ? tot[8 + i - 1] : 0) + ex[8 + i];
+        rank[j] = ((i & 1) ? tot[i - 1] : 0) + ex[i];
+        tbase[j] = ((i & 1) ? tot[8 + i - 1] : 0) + ex[8 + i];
       }
   }
 
   const size_t wb = a.fp8 ? 1 : 2;
   const int kb_d = a.d / 128, kb_f = ffe / 128;
   const int row0 = (e < nexp && !shared) ? (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e)) : 0;
-  {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if (fm[g] < 0) continue;
-      Seg sg;
-      sg.row0 = row0;
-      sg.rows = c;
-      sg.mtiles = mt[g];
-      sg.expert = e;
-      sg.tile_base = tbase[g];
-      sg.tn = tn[g];
-      if (g == kGemmGateUp) {
-        sg.N = ffe;
-        sg.K = a.d;
-        sg.ntiles = nt[g];
-        sg.a = a.x;
-        sg.as = a.xs;
-        sg.tok = shared ? nullptr : a.tok;
-        if (shared) {
-          sg.w0 = a.sh_gate;
-          sg.w1 = a.sh_up;
-          sg.s0 = a.s_sh_gate;
-          sg.s1 = a.s_sh_up;
-          sg.out = a.h_sh;
-          sg.outs = a.hs_sh;
-        } else {
-          const size_t wo = (size_t)e * ffe * a.d * wb;
-          const size_t so = (size_t)e * kb_f * kb_d;
-          sg.w0 = static_cast<const uint8_t*>(a.w_gate) + wo;
-          sg.w1 = static_cast<const uint8_t*>(a.w_up) + wo;
-          sg.s0 = a.s_gate ? a.s_gate + so : nullptr;
-          sg.s1 = a.s_up ? a.s_up + so : nullptr;
-          sg.out = a.h;
-          sg.outs = a.hs;
-        }
+  for (int j = 0; j < NS; ++j) {
+    if (fm[j] < 0) continue;
+    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    Seg sg;
+    sg.row0 = row0 + r0[j];
+    sg.rows = nr[j];
+    sg.mtiles = mt[j];
+    sg.expert = e;
+    sg.tile_base = tbase[j];
+    sg.tn = tn[j];
+    if (g == kGemmGateUp) {
+      sg.N = ffe;
+      sg.K = a.d;
+      sg.ntiles = nt[j];
+      sg.a = a.x;
+      sg.as = a.xs;
+      sg.tok = shared ? nullptr : a.tok;
+      if (shared) {
+        sg.w0 = a.sh_gate;
+        sg.w1 = a.sh_up;
+        sg.s0 = a.s_sh_gate;
+        sg.s1 = a.s_sh_up;
+        sg.out = a.h_sh;
+        sg.outs = a.hs_sh;
       } else {
-        sg.N = a.d;
-        sg.K = ffe;
-        sg.ntiles = nt[g];
-        sg.tok = nullptr;
-        sg.w1 = nullptr;
-        sg.s1 = nullptr;
-        sg.outs = nullptr;
-        if (shared) {
-          sg.a = a.h_sh;
-          sg.as = a.hs_sh;
-          sg.w0 = a.sh_down;
-          sg.s0 = a.s_sh_down;
-          sg.out = a.y_sh;
-        } else {
-          sg.a = a.h;
-          sg.as = a.hs;
-          sg.w0 = static_cast<const uint8_t*>(a.w_down) + (size_t)e * a.d * ffe * wb;
-          sg.s0 = a.s_down ? a.s_down + (size_t)e * kb_d * kb_f : nullptr;
-          sg.out = a.y;
-        }
+        const size_t wo = (size_t)e * ffe * a.d * wb;
+        const size_t so = (size_t)e * kb_f * kb_d;
+        sg.w0 = static_cast<const uint8_t*>(a.w_gate) + wo;
+        sg.w1 = static_cast<const uint8_t*>(a.w_up) + wo;
+        sg.s0 = a.s_gate ? a.s_gate + so : nullptr;
+        sg.s1 = a.s_up ? a.s_up + so : nullptr;
+        sg.out = a.h;
+        sg.outs = a.hs;
       }
-      o.segs[((size_t)g * kNumFam + fm[g]) * kSelMax + rank[g]] = sg;
+    } else {
+      sg.N = a.d;
+      sg.K = ffe;
+      sg.ntiles = nt[j];
+      sg.tok = nullptr;
+      sg.w1 = nullptr;
+      sg.s1 = nullptr;
+      sg.outs = nullptr;
+      if (shared) {
+        sg.a = a.h_sh;
+        sg.as = a.hs_sh;
+        sg.w0 = a.sh_down;
+        sg.s0 = a.s_sh_down;
+        sg.out = a.y_sh;
+      } else {
+        sg.a = a.h;
+        sg.as = a.hs;
+        sg.w0 = static_cast<const uint8_t*>(a.w_down) + (size_t)e * a.d * ffe * wb;
+        sg.s0 = a.s_down ? a.s_down + (size_t)e * kb_d * kb_f : nullptr;
+        sg.out = a.y;
+      }
     }
+    o.segs[((size_t)g * kNumFam + fm[j]) * kSelMax + rank[j]] = sg;
   }
   // per (gemm, family): segment count, tile count, zeroed queues, heavy tile count
   if (e < 2 * kNumFam) {  // e = gemm * kNumFam + family; its flags and tiles sit at 2e, 2e + 1
