@@ -5,15 +5,16 @@
 // SwiGLU).  Down: y[row][n] = sum_k h[row][k] Wd[n][k].  Shapes follow the live routing histogram
 // ("Decoding the Skew ...", Abstract: sparse expert GEMMs whose shapes vary with routing).
 //
-// Two tile families, chosen per expert on the device (select.hip):
-//  * stream: one workgroup = 4 wavefronts x 16 weight rows, all (<= 64) of an expert's rows.
-//    Operand roles are swapped so the weight rows sit on the MFMA's 16-wide row side and the few
-//    tokens on the column side (the same idea as GC-MoE's operand-swapped MMA); weights go straight
-//    from HBM into MFMA registers, each element used once, 64 contiguous bytes per row per load.
-//  * mfma: 128x128 output tiles, K-steps of 64 staged through double-buffered LDS with an XOR
-//    swizzle (conflict-free ds_read_b128), 2x2 wavefronts of 64x64 (x2 for gate and up), MFMA
-//    32x32x16.
-// Both are persistent: a fixed grid pops tiles from a device queue (zeroed by the selection
+// Two tile families, chosen per expert and GEMM on the device (select.hip):
+//  * stream: one workgroup = 4 wavefronts x 16 weight rows (or 16 each), up to 64 of an expert's
+//    rows per pass.  Operand roles are swapped so the weight rows sit on the MFMA's 16-wide row
+//    side and the few tokens on the column side (the same idea as GC-MoE's operand-swapped MMA);
+//    weights go straight from HBM into MFMA registers, each element used once, 64 contiguous bytes
+//    per row per load.
+//  * mfma: 256 token rows x 256 weight rows per tile, K-steps of 64 staged through two LDS stages
+//    by direct global->LDS loads with an XOR swizzle (conflict-free ds_read_b128), 2x2 wavefronts
+//    of 128x128, MFMA 32x32x16.
+// Both are persistent: a fixed grid pops tiles from device queues (zeroed by the selection
 // kernel), heaviest experts first, m-tiles of one weight tile adjacent in the queue.
 #include "common.h"
 #include "kernels.h"
@@ -42,7 +43,7 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // ------------------------------------------------------------------------------------------------
 // weight-streaming family
 //
-// One workgroup = 16 weight rows (gate/up: 16 gate + 16 up) and all (<= 64) rows of an expert's
+// One workgroup = 16 weight rows (gate/up: 16 gate + 16 up) and up to 64 rows of an expert's
 // segment; its 4 wavefronts split K in quarters and their partial sums meet in LDS (added in a
 // fixed order, so results are deterministic).  Small tiles give decode-sized layers enough
 // workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its quarter of

@@ -7,9 +7,10 @@
 //   acc[row][n] += P * (s_w[n/128][kb] * s_x[row][kb])
 // with s_w the weight's 128x128 block scale and s_x the row's 1x128 activation scale.
 //
-// One workgroup = 4 wavefronts; weight rows on the MFMA's 16-wide row side, up to 128 token rows
+// One workgroup = 4 wavefronts; weight rows on the MFMA's 16-wide row side, up to 32 token rows
 // per pass on the column side (operand-swapped as in the bf16 streaming family); weights stream
-// straight from HBM into MFMA registers (32 contiguous bytes per lane per 128-wide block).
+// straight from HBM into MFMA registers (32 contiguous bytes per lane per 128-wide block), the
+// next block's loads in flight while the current one is computed.
 //   gate/up: 128 weight rows per workgroup (2 row groups of 16 per wavefront, gate and up), so the
 //            workgroup owns one whole 128-column block of h: h = SiLU(g) * u is requantised per row
 //            over that block (s = amax / 448, q = e4m3(h / s)) for the fp8 down GEMM.
@@ -22,7 +23,7 @@
 
 namespace moe {
 
-constexpr int kFp8Rows = kStreamMaxRows8;  // token rows per pass (8 groups of 16)
+constexpr int kFp8Rows = kStreamMaxRows8;  // token rows per pass (2 groups of 16)
 
 __device__ __forceinline__ i32x8 as_i32x8(const uint4& lo, const uint4& hi) {
   i32x8 r;
@@ -39,6 +40,31 @@ __device__ __forceinline__ int find_seg8(const Seg* __restrict__ segs, int nseg,
     else hi = mid - 1;
   }
   return lo;
+}
+
+// Runs compute over the nkb K blocks.  Pipelined: the loads of block kb + 1 are issued before block
+// kb is computed (two register buffers, unrolled by two so no buffer is copied); otherwise each
+// block's loads are waited for before its MFMAs.
+template <bool PIPE, class Blk, class Load, class Compute>
+__device__ __forceinline__ void k_blocks_pipelined(int nkb, Load& load, Compute& compute) {
+  if (PIPE) {
+    Blk b0, b1;
+    load(b0, 0);
+    int kb = 0;
+    for (; kb + 1 < nkb; kb += 2) {
+      load(b1, kb + 1);
+      compute(b0);
+      if (kb + 2 < nkb) load(b0, kb + 2);
+      compute(b1);
+    }
+    if (kb < nkb) compute(b0);  // odd nkb: the last block sits in b0
+  } else {
+    for (int kb = 0; kb < nkb; ++kb) {
+      Blk b;
+      load(b, kb);
+      compute(b);
+    }
+  }
 }
 
 // Gate/up tile: rows [m0, m0+rows) of segment sg (rows <= 16*MQ), weight rows n0 .. n0+127.
@@ -72,26 +98,30 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
       au[g][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < nkb; ++kb) {
+  // one 128-wide K block: weights, activations and their scales
+  struct Blk { i32x8 wg[2], wu[2], xb[MQ]; float swg, swu, sx[MQ]; };
+  auto load = [&](Blk& b, int kb) {
     const uint32_t ko = (uint32_t)kb * 128;
-    i32x8 wg[2], wu[2], xb[MQ];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      wg[g] = as_i32x8(gload16(sg.w0, woff[g] + ko), gload16(sg.w0, woff[g] + ko + 16));
-      wu[g] = as_i32x8(gload16(sg.w1, woff[g] + ko), gload16(sg.w1, woff[g] + ko + 16));
+      b.wg[g] = as_i32x8(gload16(sg.w0, woff[g] + ko), gload16(sg.w0, woff[g] + ko + 16));
+      b.wu[g] = as_i32x8(gload16(sg.w1, woff[g] + ko), gload16(sg.w1, woff[g] + ko + 16));
     }
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
-    const float swg = gload_f32(sg.s0, nb * nkb + kb);
-    const float swu = gload_f32(sg.s1, nb * nkb + kb);
+    for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
+    b.swg = gload_f32(sg.s0, nb * nkb + kb);
+    b.swu = gload_f32(sg.s1, nb * nkb + kb);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) b.sx[q] = gload_f32(sg.as, srow[q] * nkb + kb);
+  };
+  auto compute = [&](const Blk& b) {
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
-      const float sx = gload_f32(sg.as, srow[q] * nkb + kb);
-      const float cg = swg * sx, cu = swu * sx;
+      const float cg = b.swg * b.sx[q], cu = b.swu * b.sx[q];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const f32x4 pg = mfma16_fp8(wg[g], xb[q], zero);
-        const f32x4 pu = mfma16_fp8(wu[g], xb[q], zero);
+        const f32x4 pg = mfma16_fp8(b.wg[g], b.xb[q], zero);
+        const f32x4 pu = mfma16_fp8(b.wu[g], b.xb[q], zero);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ag[g][q][i] = fmaf(pg[i], cg, ag[g][q][i]);
@@ -99,7 +129,8 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
         }
       }
     }
-  }
+  };
+  k_blocks_pipelined<true, Blk>(nkb, load, compute);
   // SwiGLU, then per-row requantisation over this workgroup's 128 columns.
   // lane holds C[i = 4*kg + r][j = r16]: weight row n0 + wv*32 + g*16 + 4*kg + r, token column j.
   float h[2][MQ][4];
@@ -166,21 +197,26 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
 #pragma unroll
   for (int q = 0; q < MQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < nkb; ++kb) {
+  struct Blk { i32x8 w, xb[MQ]; float sw, sx[MQ]; };
+  auto load = [&](Blk& b, int kb) {
     const uint32_t ko = (uint32_t)kb * 128;
-    const i32x8 w = as_i32x8(gload16(sg.w0, woff + ko), gload16(sg.w0, woff + ko + 16));
-    i32x8 xb[MQ];
+    b.w = as_i32x8(gload16(sg.w0, woff + ko), gload16(sg.w0, woff + ko + 16));
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
-    const float sw = gload_f32(sg.s0, nb * nkb + kb);
+    for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
+    b.sw = gload_f32(sg.s0, nb * nkb + kb);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) b.sx[q] = gload_f32(sg.as, srow[q] * nkb + kb);
+  };
+  auto compute = [&](const Blk& b) {
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
-      const float c = sw * gload_f32(sg.as, srow[q] * nkb + kb);
-      const f32x4 p = mfma16_fp8(w, xb[q], zero);
+      const float c = b.sw * b.sx[q];
+      const f32x4 p = mfma16_fp8(b.w, b.xb[q], zero);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[q][i] = fmaf(p[i], c, acc[q][i]);
     }
-  }
+  };
+  k_blocks_pipelined<true, Blk>(nkb, load, compute);
   uint16_t* out = static_cast<uint16_t*>(sg.out);
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
@@ -212,18 +248,15 @@ __global__ __launch_bounds__(256) void gemm_stream_fp8(const Seg* __restrict__ s
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     const int m0 = mt * kFp8Rows;
     const int rows = min(kFp8Rows, sg.rows - m0);
+    static_assert(kFp8Rows == 32, "token groups per pass");
     if (GU) {
       const int n0 = nt * kStream8BNGateUp;
       if (rows <= 16) fp8_gateup_tile<1>(sg, m0, rows, n0, red);
-      else if (rows <= 32) fp8_gateup_tile<2>(sg, m0, rows, n0, red);
-      else if (rows <= 64) fp8_gateup_tile<4>(sg, m0, rows, n0, red);
-      else fp8_gateup_tile<8>(sg, m0, rows, n0, red);
+      else fp8_gateup_tile<2>(sg, m0, rows, n0, red);
     } else {
       const int n0 = nt * kStream8BNDown;
       if (rows <= 16) fp8_down_tile<1>(sg, m0, rows, n0);
-      else if (rows <= 32) fp8_down_tile<2>(sg, m0, rows, n0);
-      else if (rows <= 64) fp8_down_tile<4>(sg, m0, rows, n0);
-      else fp8_down_tile<8>(sg, m0, rows, n0);
+      else fp8_down_tile<2>(sg, m0, rows, n0);
     }
   }
 }

@@ -10,11 +10,14 @@ namespace moe {
 enum Family { kFamStream = 0, kFamMfma = 1, kNumFam = 2 };
 enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
 
-constexpr int kStreamMaxRows = 64;  // rows per weight-streaming tile
+constexpr int kStreamMaxRows = 64;  // rows per weight-streaming pass
 // Automatic selection: an expert takes the weight-streaming family for a GEMM while its row
 // count is at most this, the LDS-tiled MFMA family above it.
 constexpr int kStreamRowsGateUp = 8;
 constexpr int kStreamRowsDown = 16;
+// Down GEMM with d_ff >= kStreamSplitK: the last MFMA m-tile of an expert moves to the streaming
+// family when it would hold at most this many rows.
+constexpr int kDownTailRows = 64;
 constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
@@ -24,9 +27,11 @@ constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 constexpr int kStreamSplitK = 4096;
 __host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 64; }
 constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
-// fp8 weights (streaming family only): rows per pass, h columns per gate/up tile (one whole
-// 128-column requantisation block), y columns per down tile
-constexpr int kStreamMaxRows8 = 128;
+// fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
+// the weights from L2; 32 keeps the kernels' registers low enough for 3 or more wavefronts per
+// SIMD), h columns per gate/up tile (one whole 128-column requantisation block), y columns per
+// down tile
+constexpr int kStreamMaxRows8 = 32;
 constexpr int kStream8BNGateUp = 128;
 constexpr int kStream8BNDown = 64;
 

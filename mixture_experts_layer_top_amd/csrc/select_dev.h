@@ -46,12 +46,12 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     nr[j] = c;
   }
   // A down GEMM with long K spends the same LDS load time on a 256-row tile whatever its rows, so
-  // an expert whose last m-tile would hold at most kStreamMaxRows rows hands those rows to the
+  // an expert whose last m-tile would hold at most kDownTailRows rows hands those rows to the
   // weight-streaming family (its weights stream once more, at HBM rate) instead of adding one
   // nearly empty MFMA tile per output tile.
   if (fm[1] == kFamMfma && a.config < 0 && ffe >= kStreamSplitK && c > kMfmaBM) {
     const int tail = c - (c - 1) / kMfmaBM * kMfmaBM;
-    if (tail <= kStreamMaxRows) {
+    if (tail <= kDownTailRows) {
       nr[1] = c - tail;
       fm[2] = kFamStream;
       r0[2] = c - tail;
