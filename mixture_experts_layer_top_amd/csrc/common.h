@@ -72,6 +72,19 @@ __device__ __forceinline__ int32_t gload_i32(const int32_t* p, int i) {
 __device__ __forceinline__ float gload_f32(const float* p, int i) {
   return reinterpret_cast<__attribute__((address_space(1))) const float*>((gchar*)p)[i];
 }
+// Vector stores through the global address space (a flat store would also count against the LDS
+// wait counter, out of order, and force full waits on every LDS read behind it); off in bytes.
+typedef __attribute__((address_space(1))) char gwchar;
+__device__ __forceinline__ void gstore8(void* base, size_t off, uint2 v) {
+  *reinterpret_cast<__attribute__((address_space(1))) u32x2*>((gwchar*)base + off) =
+      __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ void gstore4(void* base, size_t off, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>((gwchar*)base + off) = v;
+}
+__device__ __forceinline__ void gstore_f32(float* p, size_t i, float v) {
+  reinterpret_cast<__attribute__((address_space(1))) float*>((gwchar*)p)[i] = v;
+}
 
 
 }  // namespace moe

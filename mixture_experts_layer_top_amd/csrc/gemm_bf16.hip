@@ -151,7 +151,6 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       }
   }
   // C[i][j]: i = weight row 4*kg + r, j = token r16 of group q
-  uint16_t* out = static_cast<uint16_t*>(sg.out);
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
     const int r = q * 16 + r16;
@@ -162,7 +161,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       uint2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
       pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(out + (size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) = pk;
+      gstore8(sg.out, ((size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) * 2, pk);
     }
   }
 }
@@ -228,13 +227,12 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
     const int wm = wv & 1, wn = wv >> 1;
     const int l32 = lane & 31, khalf = lane >> 5;
     const int N = sg.N;
-    uint16_t* out = static_cast<uint16_t*>(sg.out);
     // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = wm * 128 + b * 32 + l32;
       if (r >= rows) continue;
-      uint16_t* orow = out + (size_t)(sg.row0 + m0 + r) * N;
+      const size_t orow = (size_t)(sg.row0 + m0 + r) * N;  // element offset of the output row
       if (GU) {
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -247,7 +245,7 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+            gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
           }
         }
       } else {
@@ -261,7 +259,7 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
             uint2 pk;
             pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
             pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(orow + c0 + q * 8) = pk;
+            gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
           }
         }
       }

@@ -153,7 +153,6 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
   for (int q = 0; q < MQ; ++q)
     if (kg == 0) red[wv][q * 16 + r16] = amax[q];
   __syncthreads();
-  uint8_t* hq = static_cast<uint8_t*>(sg.out);
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
     const int r = q * 16 + r16;
@@ -169,9 +168,9 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
         uint32_t pk = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk |= uint32_t(e4m3_encode(h[g][q][i] * inv)) << (8 * i);
-        *reinterpret_cast<uint32_t*>(hq + orow * N + n0 + wv * 32 + g * 16 + kg * 4) = pk;
+        gstore4(sg.out, orow * N + n0 + wv * 32 + g * 16 + kg * 4, pk);
       }
-      if (wv == 0 && kg == 0) sg.outs[orow * (N / 128) + n0 / 128] = s;
+      if (wv == 0 && kg == 0) gstore_f32(sg.outs, orow * (N / 128) + n0 / 128, s);
     }
   }
 }
@@ -217,7 +216,6 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
     }
   };
   k_blocks_pipelined<true, Blk>(nkb, load, compute);
-  uint16_t* out = static_cast<uint16_t*>(sg.out);
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
     const int r = q * 16 + r16;
@@ -225,7 +223,7 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
       uint2 pk;
       pk.x = pack_bf16x2(acc[q][0], acc[q][1]);
       pk.y = pack_bf16x2(acc[q][2], acc[q][3]);
-      *reinterpret_cast<uint2*>(out + (size_t)(sg.row0 + m0 + r) * N + n0 + wv * 16 + kg * 4) = pk;
+      gstore8(sg.out, ((size_t)(sg.row0 + m0 + r) * N + n0 + wv * 16 + kg * 4) * 2, pk);
     }
   }
 }
