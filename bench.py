@@ -160,6 +160,44 @@ def cpu_baseline(p, logits, x, W, sample_tokens: int):
                       f"float64 numpy/OpenBLAS, {dt:.1f} s"}
 
 
+def select_control(args, p, ew, d_logits, d_x, scratch, auto_ms):
+    """Time the layer with every expert forced onto one tile family.  A static rule keyed on the
+    batch alone (average rows per expert T*k/E against the streaming threshold) would pick one of
+    the two for the whole batch; the device-side selection picks per expert and per GEMM."""
+    import torch
+    from mixture_experts_layer_top_amd import moe
+    res = {"auto_ms": round(auto_ms, 4)}
+    n = max(3, args.steps // 2)
+    for name, cfg in (("stream_ms", moe.CONFIG_STREAM), ("mfma_ms", moe.CONFIG_MFMA)):
+        lay = moe.Layer(ew, p.T, p.E, p.k, config=cfg)
+        lay(d_logits, d_x)
+        torch.cuda.synchronize()
+        if args.flush:
+            ts = []
+            for _ in range(n):
+                scratch.fill_(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                lay(d_logits, d_x)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            res[name] = round(statistics.median(ts), 4)
+        else:
+            t0 = time.perf_counter()
+            for _ in range(n):
+                lay(d_logits, d_x)
+            torch.cuda.synchronize()
+            res[name] = round((time.perf_counter() - t0) * 1e3 / n, 4)
+    per_expert = p.T * p.k / p.E
+    static = "stream_ms" if per_expert <= 8 else "mfma_ms"
+    res["static_rule"] = f"T*k/E = {per_expert:g} -> {static[:-3]}"
+    res["static_ms"] = res[static]
+    res["auto_vs_static"] = round(res[static] / auto_ms, 3)
+    res["auto_vs_best_forced"] = round(min(res["stream_ms"], res["mfma_ms"]) / auto_ms, 3)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +215,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM byte-counter calibration)")
+    ap.add_argument("--select-control", action="store_true",
+                    help="also time the layer with every expert forced onto one tile family (the "
+                         "control arms of the device-side selection), same protocol, fewer steps")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -229,21 +270,26 @@ def main() -> int:
         layer(d_logits, d_x, keep={"counts": counts})
         torch.cuda.synchronize()
 
-    # Timed region: K steps.  Only the two events around the dominant kernel (gate/up GEMM) are
-    # recorded per step (plus the step's first and last when flushing), since every timing event
-    # costs GPU time.
-    GU0, GU1 = 4, 5
-    keep_idx = {GU0, GU1} | ({0, moe.TRACE_EVENTS - 1} if args.flush else set())
+    # Timed region: K steps.  Every timing event costs GPU time (a few microseconds, which matters
+    # at decode sizes), so odd steps record only the two events around the dominant kernel (the
+    # gate/up GEMM, for the roofline) and, when flushing, even steps only the layer's first and
+    # last event (for the per-step times); with K = 1 the one step records both.
+    GU0, GU1, LAST = 4, 5, moe.TRACE_EVENTS - 1
+    def keep(i):
+        gu = i % 2 == 1 or K == 1
+        ends = args.flush and (i % 2 == 0)
+        return ({GU0, GU1} if gu else set()) | ({0, LAST} if ends else set())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if scratch is not None:
             scratch.fill_(i & 0xFF)
-        layer.traced(d_logits, d_x, [e if j in keep_idx else None for j, e in enumerate(evs[i])])
+        k_i = keep(i)
+        layer.traced(d_logits, d_x, [e if j in k_i else None for j, e in enumerate(evs[i])])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu_launch_ms = [hip.elapsed_ms(evs[i][GU0], evs[i][GU1]) for i in range(K)]
-    step_ms = ([hip.elapsed_ms(evs[i][0], evs[i][-1]) for i in range(K)] if args.flush else [])
+    gu_launch_ms = [hip.elapsed_ms(evs[i][GU0], evs[i][GU1]) for i in range(K) if GU0 in keep(i)]
+    step_ms = [hip.elapsed_ms(evs[i][0], evs[i][LAST]) for i in range(K) if 0 in keep(i)]
 
     # Phase breakdown (not timed): a few more steps with every phase boundary recorded.
     phases = {name: [] for name in moe.TRACE_PHASES}
@@ -262,10 +308,15 @@ def main() -> int:
     alg = algorithmic(p, n_active)
     if args.flush:
         ms_per_step = statistics.median(step_ms)
-        timing = "median of per-step events around the layer; 512 MiB cache flush before each step"
+        timing = ("median of per-step events around the layer (steps without the gate/up events); "
+                  "512 MiB cache flush before each step")
+        q = statistics.quantiles(step_ms, n=10) if len(step_ms) >= 2 else [step_ms[0]] * 9
+        step_spread = {"p10_ms": round(q[0], 4), "p50_ms": round(ms_per_step, 4), "p90_ms": round(q[8], 4)}
     else:
         ms_per_step = wall * 1e3 / K
-        timing = "wall clock over the timed steps (synchronised before and after)"
+        timing = ("wall clock over the timed steps (synchronised before and after; every second "
+                  "step also records the two gate/up events)")
+        step_spread = None
     value = p.T / (ms_per_step * 1e-3)
 
     peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" else PEAK_BF16_TFLOPS
@@ -313,6 +364,10 @@ def main() -> int:
                                 "timing event adds ~5 us of GPU time)",
                   "timing": timing},
     }
+    if step_spread:
+        out["layer"]["step_ms"] = step_spread
+    if args.select_control and p.wdtype != "fp8":
+        out["select_control"] = select_control(args, p, ew, d_logits, d_x, scratch, ms_per_step)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

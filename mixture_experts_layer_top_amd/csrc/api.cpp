@@ -234,6 +234,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.f = p->d_ff;
   a.has_shared = 0;
   a.config = p->config;
+  a.num_cus = device_cus();
   a.fp8 = fp8;
   a.x = x_perm;
   a.xs = fp8 ? x_perm_scale : nullptr;
@@ -345,6 +346,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.f_sh = p->has_shared ? p->d_ff_shared : 0;
   a.has_shared = p->has_shared;
   a.config = p->config;
+  a.num_cus = device_cus();
   a.fp8 = fp8;
   a.x = fp8 ? static_cast<const void*>(L.xq) : x;
   a.xs = L.xs;

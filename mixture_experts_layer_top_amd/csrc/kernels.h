@@ -63,6 +63,7 @@ struct SelectArgs {
   const int32_t* counts;   // [E]
   const int32_t* offsets;  // [E + 1]
   int E, T, k, d, f, f_sh, has_shared, config, fp8;
+  int num_cus;              // compute units of the device (one MFMA-tile round)
   const void* x;           // gate/up activations (bf16 x, or e4m3 xq)
   const float* xs;         // fp8 activation scales
   const int32_t* tok;      // row -> token, for routed rows (null: rows are already permuted)

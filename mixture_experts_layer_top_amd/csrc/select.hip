@@ -12,6 +12,8 @@
 //   above that -> LDS-tiled MFMA tiles of 256 rows.  A tile runs MFMAs only for its 32-row blocks
 //                 that hold rows, so a light expert's tile streams its weights through LDS once and
 //                 costs MFMA time in proportion to its rows.
+// An MFMA tile costs a whole K loop on one CU however few rows it holds: when a GEMM's MFMA tiles
+// would not fill two rounds of CUs, its experts of up to 64 rows stay on the streaming tiles.
 // The streaming family re-reads an expert's rows from L2 for every 16 weight rows, which is what
 // caps it at a few rows per expert.  For a down GEMM with long K (d_ff >= 4096) an expert whose
 // last 256-row m-tile would hold at most 64 rows sends those rows to the streaming family: such a

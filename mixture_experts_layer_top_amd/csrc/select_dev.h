@@ -45,6 +45,23 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     r0[j] = 0;
     nr[j] = c;
   }
+  // An MFMA tile costs a whole K loop on one CU however few rows it holds, so a GEMM whose MFMA
+  // tiles would not fill two rounds of CUs (the last round is partly idle) keeps its small experts
+  // (<= kStreamMaxRows rows) on the streaming tiles, which spread each expert's weights over many
+  // workgroups.
+  if (a.config < 0 && !a.fp8) {
+    int w[2], wex[2], wtot[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      w[j] = fm[j] == kFamMfma
+                 ? (c + kMfmaBM - 1) / kMfmaBM *
+                       (j == 0 ? ffe / kMfmaBNGateUp : (a.d + kMfmaBNDown - 1) / kMfmaBNDown)
+                 : 0;
+    block_scan<2, 16>(w, wex, wtot, scan_lds);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (fm[j] == kFamMfma && wtot[j] < 2 * a.num_cus && c <= kStreamMaxRows) fm[j] = kFamStream;
+  }
   // A down GEMM with long K spends the same LDS load time on a 256-row tile whatever its rows, so
   // an expert whose last m-tile would hold at most kDownTailRows rows hands those rows to the
   // weight-streaming family (its weights stream once more, at HBM rate) instead of adding one
