@@ -160,7 +160,7 @@ def cpu_baseline(p, logits, x, W, sample_tokens: int):
                       f"float64 numpy/OpenBLAS, {dt:.1f} s"}
 
 
-def select_control(args, p, ew, d_logits, d_x, scratch, auto_ms):
+def select_control(args, p, ew, d_logits, d_x, flush, auto_ms):
     """Time the layer with every expert forced onto one tile family.  A static rule keyed on the
     batch alone (average rows per expert T*k/E against the streaming threshold) would pick one of
     the two for the whole batch; the device-side selection picks per expert and per GEMM."""
@@ -175,7 +175,7 @@ def select_control(args, p, ew, d_logits, d_x, scratch, auto_ms):
         if args.flush:
             ts = []
             for _ in range(n):
-                scratch.fill_(0)
+                flush(0)
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
                 lay(d_logits, d_x)
@@ -209,8 +209,11 @@ def main() -> int:
     ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
     ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
     ap.add_argument("--flush", action="store_true",
-                    help="overwrite a 512 MiB buffer before every step to evict L2 and the MALL; "
+                    help="sweep a 512 MiB buffer before every step to evict L2 and the MALL; "
                          "the value then comes from per-step events around the layer only")
+    ap.add_argument("--flush-mode", choices=["read", "write"], default="read",
+                    help="read: sum the buffer (evicts with clean lines); write: overwrite it (the "
+                         "dirty lines are then written back while the layer runs)")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -261,7 +264,15 @@ def main() -> int:
     hip = HipEvents()
     K, Wm = args.steps, args.warmup
     evs = [hip.create(moe.TRACE_EVENTS) for _ in range(K)]
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+    scratch = torch.ones(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+
+    def flush(i):
+        if scratch is None:
+            return
+        if args.flush_mode == "write":
+            scratch.fill_(i & 0xFF)
+        else:
+            scratch.view(torch.int64).sum()
 
     for i in range(Wm):
         layer(d_logits, d_x, keep={"counts": counts} if i == 0 else None)
@@ -282,8 +293,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)
+        flush(i)
         k_i = keep(i)
         layer.traced(d_logits, d_x, [e if j in k_i else None for j, e in enumerate(evs[i])])
     torch.cuda.synchronize()
@@ -294,8 +304,7 @@ def main() -> int:
     # Phase breakdown (not timed): a few more steps with every phase boundary recorded.
     phases = {name: [] for name in moe.TRACE_PHASES}
     for i in range(min(K, 5)):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)
+        flush(i)
         layer.traced(d_logits, d_x, evs[i])
     torch.cuda.synchronize()
     for i in range(min(K, 5)):
@@ -309,7 +318,7 @@ def main() -> int:
     if args.flush:
         ms_per_step = statistics.median(step_ms)
         timing = ("median of per-step events around the layer (steps without the gate/up events); "
-                  "512 MiB cache flush before each step")
+                  f"512 MiB cache flush ({args.flush_mode}) before each step")
         q = statistics.quantiles(step_ms, n=10) if len(step_ms) >= 2 else [step_ms[0]] * 9
         step_spread = {"p10_ms": round(q[0], 4), "p50_ms": round(ms_per_step, 4), "p90_ms": round(q[8], 4)}
     else:
@@ -367,7 +376,7 @@ def main() -> int:
     if step_spread:
         out["layer"]["step_ms"] = step_spread
     if args.select_control and p.wdtype != "fp8":
-        out["select_control"] = select_control(args, p, ew, d_logits, d_x, scratch, ms_per_step)
+        out["select_control"] = select_control(args, p, ew, d_logits, d_x, flush, ms_per_step)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

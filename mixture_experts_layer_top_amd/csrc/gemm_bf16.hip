@@ -43,11 +43,11 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // ------------------------------------------------------------------------------------------------
 // weight-streaming family
 //
-// One workgroup = 16 weight rows (gate/up: 16 gate + 16 up) and up to 64 rows of an expert's
-// segment; its 4 wavefronts split K in quarters and their partial sums meet in LDS (added in a
-// fixed order, so results are deterministic).  Small tiles give decode-sized layers enough
-// workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its quarter of
-// the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
+// One workgroup = 16 weight rows split four ways in K, or 32 split two ways (gate/up: as many
+// gate and up rows), and up to 64 rows of an expert's segment; the partial sums meet in LDS
+// (added in a fixed order, so results are deterministic).  Small tiles give decode-sized layers
+// enough workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its share
+// of the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
 // ------------------------------------------------------------------------------------------------
 template <int MQ, bool GU, int WK>
 __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0,
@@ -55,9 +55,9 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K, N = sg.N;
-  // WK = 4: the wavefronts split K over the same 16 rows; WK = 1: wavefront wv takes rows 16*wv..
-  const int kw = WK == 4 ? wv : 0;
-  if (WK == 1) n0 += 16 * wv;
+  // WK wavefronts split K over each group of 16 weight rows; the 4 / WK groups are consecutive
+  const int grp = wv / WK, kw = wv % WK;
+  n0 += 16 * grp;
   const int nrow = n0 + r16;  // this lane's weight row (A operand)
   const void* wg = sg.w0;
   const void* wu = GU ? sg.w1 : sg.w0;
@@ -122,11 +122,12 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
   }
-  // split-K reduction: wavefronts 1..3 park their partials, wavefront 0 adds them in order
+  // split-K reduction: in each group, wavefronts kw = 1..WK-1 park their partials and wavefront
+  // kw = 0 adds them in order (slots grp * (WK - 1) + kw - 1, at most 3)
   constexpr int NV = MQ * 4 * (GU ? 2 : 1);  // floats per lane
-  if (WK == 4) __syncthreads();  // red[] may still be read by the previous tile
-  if (WK == 4 && wv > 0) {
-    float* dst = red + ((wv - 1) * NV) * 64 + lane;
+  if (WK > 1) __syncthreads();  // red[] may still be read by the previous tile
+  if (WK > 1 && kw > 0) {
+    float* dst = red + ((grp * (WK - 1) + kw - 1) * NV) * 64 + lane;
 #pragma unroll
     for (int q = 0; q < MQ; ++q)
 #pragma unroll
@@ -135,13 +136,13 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
         if (GU) dst[(MQ * 4 + q * 4 + i) * 64] = acc1[q][i];
       }
   }
-  if (WK == 4) {
+  if (WK > 1) {
     __syncthreads();
-    if (wv != 0) return;
+    if (kw != 0) return;
   }
 #pragma unroll
-  for (int w = 0; w < (WK == 4 ? 3 : 0); ++w) {
-    const float* src = red + (w * NV) * 64 + lane;
+  for (int w = 0; w < WK - 1; ++w) {
+    const float* src = red + ((grp * (WK - 1) + w) * NV) * 64 + lane;
 #pragma unroll
     for (int q = 0; q < MQ; ++q)
 #pragma unroll
@@ -183,14 +184,14 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
     const int m0 = mt * kStreamMaxRows;
     const int rows = min(kStreamMaxRows, sg.rows - m0);
     const int n0 = nt * sg.tn;
-    if (sg.tn == 16) {  // long K: split across the wavefronts
+    if (sg.tn == 16) {  // long K: split across the 4 wavefronts
       if (rows <= 16) stream_tile_bf16<1, GU, 4>(sg, m0, rows, n0, red);
       else if (rows <= 32) stream_tile_bf16<2, GU, 4>(sg, m0, rows, n0, red);
       else stream_tile_bf16<4, GU, 4>(sg, m0, rows, n0, red);
-    } else {
-      if (rows <= 16) stream_tile_bf16<1, GU, 1>(sg, m0, rows, n0, red);
-      else if (rows <= 32) stream_tile_bf16<2, GU, 1>(sg, m0, rows, n0, red);
-      else stream_tile_bf16<4, GU, 1>(sg, m0, rows, n0, red);
+    } else {  // 32 columns: split across pairs of wavefronts
+      if (rows <= 16) stream_tile_bf16<1, GU, 2>(sg, m0, rows, n0, red);
+      else if (rows <= 32) stream_tile_bf16<2, GU, 2>(sg, m0, rows, n0, red);
+      else stream_tile_bf16<4, GU, 2>(sg, m0, rows, n0, red);
     }
   }
 }

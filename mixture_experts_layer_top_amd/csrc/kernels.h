@@ -22,10 +22,11 @@ constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
 constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
-// Weight-streaming tiles: the 4 wavefronts split K when K is long (16 output columns per tile),
-// otherwise each takes 16 of 64 output columns over the whole K.
+// Weight-streaming tiles: the 4 wavefronts split K four ways when K is long (16 output columns
+// per tile), otherwise two ways (32 output columns, 16 per pair of wavefronts).  Measured: one
+// wavefront per 16 columns over the whole K, or a four-way split of a short K, streams slower.
 constexpr int kStreamSplitK = 4096;
-__host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 64; }
+__host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 32; }
 constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
 // fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
 // the weights from L2; 32 keeps the kernels' registers low enough for 3 or more wavefronts per
