@@ -199,12 +199,20 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // ------------------------------------------------------------------------------------------------
 // LDS-tiled MFMA family
 //
-// Tile: 256 token rows x 256 weight rows (gate/up: 128 gate + 128 up rows -> 128 h columns; down:
-// 256 y columns).  4 wavefronts as 2 (tokens) x 2 (weights), each 128 x 128 with MFMA 32x32x16:
-// 16 accumulator blocks, 4 A and 4 B fragments per k-substep, every fragment reused 4 times.  A tile
-// runs every MFMA whatever its rows (skipping the empty token blocks of partly filled tiles was
-// measured: it gained ~3% on many-expert prefill, lost ~2% on 8-expert prefill and raised the
-// gate/up L2 miss traffic by ~40%).
+// A tile is 256 weight rows (gate/up: 128 gate + 128 up rows -> 128 h columns; down: 256 y columns)
+// by a tile height of token rows chosen from the rows the tile holds: 256 (full), 128 or 64.  The
+// last m-tile of an expert and every expert with at most 128 rows take the shortest height that
+// holds their rows, so a 40-row expert runs a quarter of the MFMAs of a full tile and its weights
+// stream at the rate of the loads instead of the MFMAs.
+//  * full: 4 wavefronts as 2 (tokens) x 2 (weights), each 128 x 128 with MFMA 32x32x16: 16
+//    accumulator blocks, 4 A and 4 B fragments per k-substep, every fragment reused 4 times; two
+//    LDS stages of 64 KB.
+//  * short (128 or 64 rows): the 4 wavefronts split the weight rows (gate/up: 32 gate + 32 up rows
+//    each, down: 64 rows each) and each covers every token row; three LDS stages of 48 or 40 KB,
+//    since these tiles wait on the weight stream rather than on the MFMAs.
+// Within a tile every MFMA runs whatever its rows (skipping empty 32-row token blocks inside a full
+// tile was measured: ~3% on many-expert prefill, -2% on 8-expert prefill and ~40% more gate/up L2
+// miss traffic).
 //
 // Scheduling: one persistent workgroup per CU.  The tile order puts the m-tiles of one weight tile
 // next to each other; consecutive runs of (CUs per XCD) tiles go to one XCD, so tiles that share
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // ------------------------------------------------------------------------------------------------
 constexpr int BM = kMfmaBM;
 constexpr int BNW = 256;                  // weight rows per tile
-constexpr int LROWS = BM + BNW;           // LDS rows per stage
+constexpr int LROWS = BM + BNW;           // LDS rows per stage of a full tile
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -267,47 +275,119 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
     }
   }
 
+// Short tiles of TB * 32 token rows: wavefront wn holds weight blocks acc[0..1][*] (gate/up: its 32
+// gate rows in block 0 and the matching 32 up rows in block 1 -> h columns [32 wn, +32); down: y
+// columns [64 wn, +64)) for token blocks acc[*][0..TB).
+template <bool GU, int TB>
+__device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], const Seg& sg,
+                                                   int m0, int rows, int n0) {
+  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int N = sg.N;
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    const int r = b * 32 + l32;
+    if (r >= rows) continue;
+    const size_t orow = (size_t)(sg.row0 + m0 + r) * N;
+    if (GU) {
+      const int c0 = n0 + wn * 32 + khalf * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[0][b][q * 4 + s], acc[1][b][q * 4 + s]);
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int cb = n0 + wn * 64 + a * 32;
+        if (cb >= N) continue;
+        const int c0 = cb + khalf * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
+          pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
+          gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
-// Memory pipeline: K-steps of 64 through two LDS stages of 64 KB (512 rows of 128 B).  Global data
-// goes straight into LDS (global_load_lds_dwordx4, no staging registers), every instruction moving
-// 8 whole 128-byte lines.  Rows keep 8 chunks of 16 B XOR-swizzled by (row >> 1) & 7, so the 16
-// lanes a ds_read_b128 serves together (16 rows, one chunk index) cover all 64 banks.  The stages
-// are distinct LDS arrays so the compiler can tell the asynchronous LDS writes from the reads, and
-// waits are explicit (vmcnt) around a plain barrier so prefetches stay in flight.
-// Step kt on stage S: substeps 0..2 run while substeps 1..3 are read; wait until this wavefront's
-// reads are done and every load it issued has landed; barrier (stage S^1 complete, stage S free);
-// loads for step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
+// Memory pipeline: K-steps of 64 (128-byte LDS rows) through a ring of stages; each stage holds the
+// tile's token rows, then its 256 weight rows.  Global data goes straight into LDS
+// (global_load_lds_dwordx4, no staging registers), every instruction moving 8 whole 128-byte lines.
+// Rows keep 8 chunks of 16 B XOR-swizzled by (row >> 1) & 7, so the 16 lanes a ds_read_b128 serves
+// together (16 rows, one chunk index) cover all 64 banks.
+//
+// Full tiles: two stages of 64 KB.  Waits are explicit (vmcnt) around a plain barrier so prefetches
+// stay in flight.  Step kt
+// on stage S: substeps 0..2 run while substeps 1..3 are read; wait until this wavefront's reads are
+// done and every load it issued has landed; barrier (stage S^1 complete, stage S free); loads for
+// step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
+//
+// Short tiles: three stages at a run-time stage index, so that two steps of loads stay in flight
+// while one stage is read.  Step kt reads stage kt % 3; before the
+// barrier it waits until the loads of step kt+1 have landed (those of kt+2 may still fly), then
+// loads step kt+3 into the stage it just finished.
 // ------------------------------------------------------------------------------------------------
 constexpr int BK64 = 64;
 constexpr int ROWB64 = 128;
 constexpr int STAGE64 = LROWS * ROWB64;            // 64 KB
 constexpr int DMA64 = STAGE64 / (256 * 16);        // 16 loads per thread per stage
-__shared__ __attribute__((aligned(1024))) uint8_t g_bs0[STAGE64];
-__shared__ __attribute__((aligned(1024))) uint8_t g_bs1[STAGE64];
-template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return S == 0 ? g_bs0 : g_bs1; }
+constexpr int kShortStages = 3;
+constexpr int kRingBytes = kShortStages * (128 + BNW) * ROWB64;  // 144 KB (>= 2 full stages)
+static_assert(kRingBytes >= 2 * STAGE64, "ring holds two full-tile stages");
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring[kRingBytes];
+template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return g_ring + S * STAGE64; }
 
 __device__ __forceinline__ int lds_off64(int r, int c) { return r * ROWB64 + ((c ^ ((r >> 1) & 7)) << 4); }
 
+// One global->LDS load of 16 bytes per lane: lane i's bytes land at dst + 16 * i (dst uniform).
+// Written as asm because the compiler cannot tell which LDS bytes its LDS-load builtin writes: it
+// waits for every such load (vmcnt(0)) before any LDS read that might overlap, which within one
+// ring array means right after each prefetch is issued, and it also drains them at loop heads.  Hidden from the compiler, the loads still count in vmcnt in hardware, and vector
+// memory operations of a wavefront complete in order; the short-tile pipeline waits for them
+// explicitly, and any vmcnt wait the compiler emits for its own loads can only be stronger than
+// needed.  No output registers: the data goes to LDS only.
+__device__ __forceinline__ void dma16(gchar* src, lds_void* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
 template <bool GU>
-struct MfmaTile64 {
-  // Load slot j of wavefront wv fills LDS rows [32*j + 8*wv, +8): slots 0..7 token rows,
-  // 8..15 weight rows (gate/up: 8..11 gate rows 0..127, 12..15 up rows 0..127).
+struct MfmaTile {
+  // Load slot j of wavefront wv fills LDS rows [32*j + 8*wv, +8) of a stage: slots [0, NTS) token
+  // rows, then 8 slots of weight rows (gate/up: 4 of gate rows 0..127, 4 of up rows 0..127), with
+  // NTS = tile height / 32.
   const char* abase;
   const char* wbase0;
   const char* wbase1;
   uint32_t off[DMA64];
   int wvu;
+  int bm;  // tile height: 256, 128 or 64 token rows
   int arow[4], brow[4];
   f32x16 acc[4][4];
 
+  template <int NTS>
   __device__ __forceinline__ const char* slot_base(int j) const {
-    return j < 8 ? abase : ((!GU || j < 12) ? wbase0 : wbase1);
+    return j < NTS ? abase : ((!GU || j < NTS + 4) ? wbase0 : wbase1);
   }
 
   __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0) {
     const int lane = threadIdx.x & 63;
     wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wvu & 1, wn = wvu >> 1;
+    bm = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
+    const int nts = bm >> 5;
     const uint32_t rowbytes = (uint32_t)sg.K * 2;
     abase = static_cast<const char*>(sg.a);
     wbase0 = static_cast<const char*>(sg.w0);
@@ -316,36 +396,50 @@ struct MfmaTile64 {
     for (int j = 0; j < DMA64; ++j) {
       const int r = 32 * j + 8 * wvu + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
-      if (j < 8) {
+      if (j < nts) {
         // padded rows (r >= rows) all read the first row's first 16 bytes: one coalesced request
         // per instruction instead of eight lines; their LDS rows are never stored
         const int gr = sg.row0 + m0 + (r < rows ? r : 0);
         const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
         off[j] = (uint32_t)src * rowbytes + (r < rows ? c * 16 : 0);
       } else {
-        int wr = GU ? n0 + ((r - BM) & 127) : n0 + (r - BM);
+        // (slots past the tile's last weight slot are never issued)
+        int wr = GU ? n0 + ((r - bm) & 127) : n0 + (r - bm);
         wr = wr < sg.N ? wr : sg.N - 1;
         off[j] = (uint32_t)wr * rowbytes + c * 16;
       }
     }
     const int l32 = lane & 31;
+    if (bm == BM) {
+      const int wm = wvu & 1, wn = wvu >> 1;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
-                   : (BM + wn * 128 + a * 32 + l32);
+      for (int a = 0; a < 4; ++a)
+        arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
+                     : (BM + wn * 128 + a * 32 + l32);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
+      for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
+    } else {
+      const int wn = wvu;
+      arow[0] = GU ? bm + wn * 32 + l32 : bm + wn * 64 + l32;
+      arow[1] = GU ? bm + 128 + wn * 32 + l32 : bm + wn * 64 + 32 + l32;
+      arow[2] = arow[3] = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) brow[b] = b * 32 + l32;
+    }
+  }
+
+  // ---- full tiles ----
+  template <int S>
+  __device__ __forceinline__ void issue_one(int j, uint32_t ko) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t* st = stage64_ptr<S>() + wv * 8 * ROWB64;
+    dma16((gchar*)slot_base<8>(j) + off[j] + ko, (lds_void*)(st + j * 32 * ROWB64));
   }
 
   template <int S>
   __device__ __forceinline__ void issue(int kt) {
-    uint8_t* st = stage64_ptr<S>() + wvu * 8 * ROWB64;
-    const uint32_t ko = (uint32_t)kt * ROWB64;
 #pragma unroll
-    for (int j = 0; j < DMA64; ++j)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<__attribute__((address_space(1))) const void*>((gchar*)slot_base(j) + off[j] + ko),
-          (lds_void*)(st + j * 32 * ROWB64), 16, 0, 0);
+    for (int j = 0; j < DMA64; ++j) issue_one<S>(j, (uint32_t)kt * ROWB64);
   }
 
   template <int S>
@@ -387,24 +481,28 @@ struct MfmaTile64 {
     sub<S>(3, f0, f1);
     MOE_WAITCNT(0, 0);
     __builtin_amdgcn_s_barrier();
-    issue<S>(min(kt + 2, nk - 1));
-    read_frags<S ^ 1>(0, f0);
-    mfmas(f1);
+    // one load for step kt+2 per MFMA of substep 3 (the scheduler cannot see the asm loads, so the
+    // interleave is fixed by hand), with substep 0 of stage S^1 read behind the first eight
+    const uint32_t ko = (uint32_t)min(kt + 2, nk - 1) * ROWB64;
+    const uint8_t* rd = stage64_ptr<S ^ 1>();
+    const int c = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_one<S>(i, ko);
+      acc[i >> 2][i & 3] = mfma32(f1[i >> 2], f1[4 + (i & 3)], acc[i >> 2][i & 3]);
+      if (i < 8)
+        f0[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rd + lds_off64(i < 4 ? arow[i] : brow[i - 4], c)));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  __device__ __forceinline__ void prologue() {
+  __device__ __forceinline__ void prologue_full() {
     issue<0>(0);
     issue<1>(1);
   }
 
-  __device__ __forceinline__ void run(int K) {
+  __device__ __forceinline__ void run_full(int K) {
     const int nk = K / BK64;  // K is a multiple of 128, so nk is even
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -424,8 +522,108 @@ struct MfmaTile64 {
     __builtin_amdgcn_s_barrier();
   }
 
-  __device__ __forceinline__ void store(const Seg& sg, int m0, int rows, int n0) {
-    MfmaTileStore<GU>(acc, sg, m0, rows, n0);
+  // ---- short tiles (TB = tile height / 32 token blocks) ----
+  template <int TB>
+  __device__ __forceinline__ void issue_short_one(int stage, int j, uint32_t ko) {
+    constexpr int kStage = (TB * 32 + BNW) * ROWB64;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t* st = g_ring + stage * kStage + wv * 8 * ROWB64;
+    dma16((gchar*)slot_base<TB>(j) + off[j] + ko, (lds_void*)(st + j * 32 * ROWB64));
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void issue_short(int stage, int kt) {
+#pragma unroll
+    for (int j = 0; j < TB + 8; ++j) issue_short_one<TB>(stage, j, (uint32_t)kt * ROWB64);
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void read_frags_short(const uint8_t* st, int kk, bf16x8 (&f)[2 + TB]) const {
+    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(arow[a], c)));
+#pragma unroll
+    for (int b = 0; b < TB; ++b) f[2 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(brow[b], c)));
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void mfmas_short(const bf16x8 (&f)[2 + TB]) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) acc[a][b] = mfma32(f[a], f[2 + b], acc[a][b]);
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void sub_short(const uint8_t* st, int kk, const bf16x8 (&cur)[2 + TB],
+                                            bf16x8 (&nxt)[2 + TB]) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags_short<TB>(st, kk, nxt);
+    mfmas_short<TB>(cur);
+#pragma unroll
+    for (int i = 0; i < 2 + TB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (TB > 2) __builtin_amdgcn_sched_group_barrier(0x008, TB - 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void prologue_short(int nk) {
+#pragma unroll
+    for (int s = 0; s < kShortStages; ++s) issue_short<TB>(s, min(s, nk - 1));
+  }
+
+  template <int TB>
+  __device__ __forceinline__ void run_short(int K) {
+    constexpr int kStage = (TB * 32 + BNW) * ROWB64;
+    constexpr int D = TB + 8;  // loads per thread per stage
+    const int nk = K / BK64;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    MOE_WAITCNT((kShortStages - 1) * D, 15);  // stage 0 (the oldest loads) has landed
+    __builtin_amdgcn_s_barrier();
+    bf16x8 f0[2 + TB], f1[2 + TB];
+    read_frags_short<TB>(g_ring, 0, f0);
+    int s = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint8_t* st = g_ring + s * kStage;
+      sub_short<TB>(st, 1, f0, f1);
+      sub_short<TB>(st, 2, f1, f0);
+      sub_short<TB>(st, 3, f0, f1);
+      // this wavefront's reads of stage s are done and its loads for step kt+1 have landed
+      MOE_WAITCNT((kShortStages - 2) * D, 0);
+      __builtin_amdgcn_s_barrier();
+      // the loads for step kt+3 into stage s, interleaved with the MFMAs of substep 3 and the
+      // reads of substep 0 of the next stage
+      const uint32_t ko = (uint32_t)min(kt + kShortStages, nk - 1) * ROWB64;
+      const int sn = s == kShortStages - 1 ? 0 : s + 1;
+      const uint8_t* rd = g_ring + sn * kStage;
+      const int c = (threadIdx.x & 63) >> 5;
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_short_one<TB>(s, i, ko);
+        if (i < 2 * TB) acc[i / TB][i % TB] = mfma32(f1[i / TB], f1[2 + i % TB], acc[i / TB][i % TB]);
+        if (i < 2 + TB)
+          f0[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rd + lds_off64(i < 2 ? arow[i] : brow[i - 2], c)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s = sn;
+    }
+    MOE_WAITCNT(0, 0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  __device__ __forceinline__ void prologue(int K) {
+    if (bm == BM) prologue_full();
+    else if (bm == 128) prologue_short<4>(K / BK64);
+    else prologue_short<2>(K / BK64);
   }
 };
 
@@ -466,8 +664,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   if (ntiles == 0) return;
   const int chunk = max(1, (int)gridDim.x / kXcds);
   int q = 0;
-  MfmaTile64<GU> tile;
-  struct Cur { int si, m0, rows, n0; };
+  MfmaTile<GU> tile;
+  struct Cur { int si, m0, rows, n0, h; };
   auto claim = [&](Cur& c) -> bool {
     const int pos = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);
     if (pos < 0) return false;
@@ -480,17 +678,31 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
     c.rows = min(BM, sg.rows - c.m0);
     c.n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
     tile.setup(sg, c.m0, c.rows, c.n0);
-    tile.prologue();
+    c.h = __builtin_amdgcn_readfirstlane(tile.bm);
+    tile.prologue(sg.K);
     return true;
   };
   Cur cur;
   if (!claim(cur)) return;
   for (;;) {
-    tile.run(segs[cur.si].K);
-    // start the next tile's loads before this tile's epilogue
+    // run, then start the next tile's loads before this tile's epilogue; each height has its own
+    // branch so the accumulators a shorter tile leaves unused are dead around the loop
+    const Seg& sg = segs[cur.si];
     Cur nxt;
-    const bool more = claim(nxt);
-    tile.store(segs[cur.si], cur.m0, cur.rows, cur.n0);
+    bool more;
+    if (cur.h == BM) {
+      tile.run_full(sg.K);
+      more = claim(nxt);
+      MfmaTileStore<GU>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+    } else if (cur.h == 128) {
+      tile.template run_short<4>(sg.K);
+      more = claim(nxt);
+      MfmaTileStoreShort<GU, 4>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+    } else {
+      tile.template run_short<2>(sg.K);
+      more = claim(nxt);
+      MfmaTileStoreShort<GU, 2>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+    }
     if (!more) break;
     cur = nxt;
   }

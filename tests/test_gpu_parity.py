@@ -190,6 +190,30 @@ def test_layer_matches_oracle(moe, p, config):
     _check_layer(moe, Inputs(p), config=config, runs=2)
 
 
+# MFMA tiles take a height of 64, 128 or 256 token rows from the rows they hold; one expert whose
+# row count sits at each boundary, with K of 2 K-steps (the three-stage ring of the short tiles
+# then reloads its last step) and of 6.
+TILE_HEIGHTS = [
+    _small(f"heights_T{T}_d{d}", T=T, d=d, f=f, E=1, k=1, cfg_index=120 + i)
+    for i, (T, d, f) in enumerate(
+        [(T, 128, 384) for T in (1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 385)]
+        + [(T, 384, 128) for T in (40, 100, 300)])
+]
+
+
+@pytest.mark.parametrize("p", TILE_HEIGHTS, ids=lambda p: p.name)
+def test_mfma_tile_heights(moe, p):
+    _check_layer(moe, Inputs(p), config=1)
+
+
+# More tiles than workgroups, so one persistent workgroup runs tiles of different heights in turn.
+def test_mfma_mixed_heights_persistent(moe):
+    p = _small("heights_mixed", T=2000, d=256, f=2048, E=8, k=2, routing="dirichlet", alpha=1.0,
+               cfg_index=140)
+    for config in (1, -1):
+        _check_layer(moe, Inputs(p), config=config, runs=2)
+
+
 def test_generator_device_independent(moe):
     for p, which, e in ((I.TINY, "gate", 3), (I.DSV3, "down", 200), (I.FP8, "up", 7)):
         a = I.gen_expert_weight(p, which, e, "cpu")
