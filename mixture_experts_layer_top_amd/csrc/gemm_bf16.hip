@@ -229,19 +229,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define MOE_WAITCNT(vm, lg) \
   __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | 0x70 | (((lg) & 15) << 8))
 
+// Epilogue of one tile: out is the GEMM's output base ([.][N] bf16), row0 + m0 its first row.
 template <bool GU>
-__device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const Seg& sg, int m0,
-                                              int rows, int n0) {
+__device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], void* out, int N, int row0,
+                                              int m0, int rows, int n0) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wm = wv & 1, wn = wv >> 1;
     const int l32 = lane & 31, khalf = lane >> 5;
-    const int N = sg.N;
     // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = wm * 128 + b * 32 + l32;
       if (r >= rows) continue;
-      const size_t orow = (size_t)(sg.row0 + m0 + r) * N;  // element offset of the output row
+      const size_t orow = (size_t)(row0 + m0 + r) * N;  // element offset of the output row
       if (GU) {
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -254,7 +254,7 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
             uint2 pk;
             pk.x = pack_bf16x2(v[0], v[1]);
             pk.y = pack_bf16x2(v[2], v[3]);
-            gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+            gstore8(out, (orow + c0 + q * 8) * 2, pk);
           }
         }
       } else {
@@ -268,7 +268,7 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
             uint2 pk;
             pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
             pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
-            gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+            gstore8(out, (orow + c0 + q * 8) * 2, pk);
           }
         }
       }
@@ -279,16 +279,15 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], const S
 // gate rows in block 0 and the matching 32 up rows in block 1 -> h columns [32 wn, +32); down: y
 // columns [64 wn, +64)) for token blocks acc[*][0..TB).
 template <bool GU, int TB>
-__device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], const Seg& sg,
-                                                   int m0, int rows, int n0) {
+__device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], void* out, int N,
+                                                   int row0, int m0, int rows, int n0) {
   const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int N = sg.N;
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     const int r = b * 32 + l32;
     if (r >= rows) continue;
-    const size_t orow = (size_t)(sg.row0 + m0 + r) * N;
+    const size_t orow = (size_t)(row0 + m0 + r) * N;
     if (GU) {
       const int c0 = n0 + wn * 32 + khalf * 4;
 #pragma unroll
@@ -299,7 +298,7 @@ __device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], co
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
-        gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+        gstore8(out, (orow + c0 + q * 8) * 2, pk);
       }
     } else {
 #pragma unroll
@@ -312,7 +311,7 @@ __device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], co
           uint2 pk;
           pk.x = pack_bf16x2(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1]);
           pk.y = pack_bf16x2(acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
-          gstore8(sg.out, (orow + c0 + q * 8) * 2, pk);
+          gstore8(out, (orow + c0 + q * 8) * 2, pk);
         }
       }
     }
@@ -349,6 +348,21 @@ template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return g_ri
 
 __device__ __forceinline__ int lds_off64(int r, int c) { return r * ROWB64 + ((c ^ ((r >> 1) & 7)) << 4); }
 
+// Fragment reads: a wavefront's A (weight) and B (token) fragments sit in 32-row blocks starting at
+// multiples of 32 rows, so a lane's swizzle (row >> 1) & 7 = (lane % 32 >> 1) & 7 is the same in
+// every block.  Each read address is then a per-lane base for the k-substep (row 32*blk + lane%32,
+// chunk 2*kk + lane/32) plus a block offset that is a compile-time constant, which the LDS read
+// instruction carries as its immediate: 4 bases per operand instead of one register per fragment.
+__device__ __forceinline__ int frag_lane_off(int kk) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
+  return l32 * ROWB64 + (((kk * 2 + (lane >> 5)) ^ ((l32 >> 1) & 7)) << 4);
+}
+// byte offset of weight block a of a full tile (gate/up: gate blocks 0, 1 then up blocks 2, 3)
+template <bool GU>
+__device__ __forceinline__ constexpr int full_a_blk(int a) {
+  return GU ? ((a & 1) * 32 + (a >> 1) * 128) * ROWB64 : a * 32 * ROWB64;
+}
+
 // One global->LDS load of 16 bytes per lane: lane i's bytes land at dst + 16 * i (dst uniform).
 // Written as asm because the compiler cannot tell which LDS bytes its LDS-load builtin writes: it
 // waits for every such load (vmcnt(0)) before any LDS read that might overlap, which within one
@@ -375,7 +389,7 @@ struct MfmaTile {
   uint32_t off[DMA64];
   int wvu;
   int bm;  // tile height: 256, 128 or 64 token rows
-  int arow[4], brow[4];
+  int arow0, brow0;  // LDS byte offsets of the wavefront's first weight and token rows
   f32x16 acc[4][4];
 
   template <int NTS>
@@ -392,39 +406,45 @@ struct MfmaTile {
     abase = static_cast<const char*>(sg.a);
     wbase0 = static_cast<const char*>(sg.w0);
     wbase1 = static_cast<const char*>(GU ? sg.w1 : sg.w0);
+    // Token rows of slots 0..7, fetched together whatever the tile height (slots at or past NTS
+    // are weight slots and drop theirs).  Padded rows (r >= rows) all read the first row's first 16
+    // bytes: one coalesced request per instruction instead of eight lines; their LDS rows are never
+    // stored.
+    int src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 32 * j + 8 * wvu + (lane >> 3);
+      src[j] = sg.row0 + m0 + (r < rows ? r : 0);
+    }
+    if (sg.tok) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) src[j] = gload_i32(sg.tok, src[j]);
+    }
 #pragma unroll
     for (int j = 0; j < DMA64; ++j) {
       const int r = 32 * j + 8 * wvu + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
-      if (j < nts) {
-        // padded rows (r >= rows) all read the first row's first 16 bytes: one coalesced request
-        // per instruction instead of eight lines; their LDS rows are never stored
-        const int gr = sg.row0 + m0 + (r < rows ? r : 0);
-        const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-        off[j] = (uint32_t)src * rowbytes + (r < rows ? c * 16 : 0);
+      // as a weight slot, LDS row r holds the tile's weight row r - bm (slots past the tile's last
+      // weight slot are never issued)
+      int wr = GU ? n0 + ((r - bm) & 127) : n0 + (r - bm);
+      wr = wr < sg.N ? wr : sg.N - 1;
+      const uint32_t woff = (uint32_t)wr * rowbytes + c * 16;
+      if (j < 8) {
+        const int rr = 32 * j + 8 * wvu + (lane >> 3);
+        const uint32_t toff = (uint32_t)src[j] * rowbytes + (rr < rows ? c * 16 : 0);
+        off[j] = j < nts ? toff : woff;
       } else {
-        // (slots past the tile's last weight slot are never issued)
-        int wr = GU ? n0 + ((r - bm) & 127) : n0 + (r - bm);
-        wr = wr < sg.N ? wr : sg.N - 1;
-        off[j] = (uint32_t)wr * rowbytes + c * 16;
+        off[j] = woff;
       }
     }
-    const int l32 = lane & 31;
     if (bm == BM) {
       const int wm = wvu & 1, wn = wvu >> 1;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        arow[a] = GU ? (BM + (a < 2 ? 0 : 128) + wn * 64 + (a & 1) * 32 + l32)
-                     : (BM + wn * 128 + a * 32 + l32);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) brow[b] = wm * 128 + b * 32 + l32;
+      arow0 = (BM + (GU ? wn * 64 : wn * 128)) * ROWB64;
+      brow0 = wm * 128 * ROWB64;
     } else {
       const int wn = wvu;
-      arow[0] = GU ? bm + wn * 32 + l32 : bm + wn * 64 + l32;
-      arow[1] = GU ? bm + 128 + wn * 32 + l32 : bm + wn * 64 + 32 + l32;
-      arow[2] = arow[3] = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) brow[b] = b * 32 + l32;
+      arow0 = (bm + (GU ? wn * 32 : wn * 64)) * ROWB64;
+      brow0 = 0;
     }
   }
 
@@ -442,14 +462,18 @@ struct MfmaTile {
     for (int j = 0; j < DMA64; ++j) issue_one<S>(j, (uint32_t)kt * ROWB64);
   }
 
+  // fragment i of a full tile's k-substep (0..3: weight blocks, 4..7: token blocks)
+  __device__ __forceinline__ bf16x8 frag_full(const uint8_t* st, int va, int vb, int i) const {
+    const uint8_t* p = i < 4 ? st + va + full_a_blk<GU>(i) : st + vb + (i - 4) * 32 * ROWB64;
+    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+  }
+
   template <int S>
   __device__ __forceinline__ void read_frags(int kk, bf16x8 (&f)[8]) const {
     const uint8_t* st = stage64_ptr<S>();
-    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
+    const int lo = frag_lane_off(kk), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(arow[a], c)));
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[4 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(brow[b], c)));
+    for (int i = 0; i < 8; ++i) f[i] = frag_full(st, va, vb, i);
   }
 
   __device__ __forceinline__ void mfmas(const bf16x8 (&f)[8]) {
@@ -485,14 +509,13 @@ struct MfmaTile {
     // interleave is fixed by hand), with substep 0 of stage S^1 read behind the first eight
     const uint32_t ko = (uint32_t)min(kt + 2, nk - 1) * ROWB64;
     const uint8_t* rd = stage64_ptr<S ^ 1>();
-    const int c = (threadIdx.x & 63) >> 5;
+    const int lo = frag_lane_off(0), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       issue_one<S>(i, ko);
       acc[i >> 2][i & 3] = mfma32(f1[i >> 2], f1[4 + (i & 3)], acc[i >> 2][i & 3]);
-      if (i < 8)
-        f0[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rd + lds_off64(i < 4 ? arow[i] : brow[i - 4], c)));
+      if (i < 8) f0[i] = frag_full(rd, va, vb, i);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -537,13 +560,19 @@ struct MfmaTile {
     for (int j = 0; j < TB + 8; ++j) issue_short_one<TB>(stage, j, (uint32_t)kt * ROWB64);
   }
 
+  // fragment i of a short tile's k-substep (0, 1: weight blocks -- gate/up: 32 gate rows, then the
+  // matching up rows 128 further; down: two consecutive blocks -- 2..: token blocks)
+  template <int TB>
+  __device__ __forceinline__ bf16x8 frag_short(const uint8_t* st, int va, int vb, int i) const {
+    const uint8_t* p = i < 2 ? st + va + i * (GU ? 128 : 32) * ROWB64 : st + vb + (i - 2) * 32 * ROWB64;
+    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+  }
+
   template <int TB>
   __device__ __forceinline__ void read_frags_short(const uint8_t* st, int kk, bf16x8 (&f)[2 + TB]) const {
-    const int c = kk * 2 + ((threadIdx.x & 63) >> 5);
+    const int lo = frag_lane_off(kk), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) f[a] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(arow[a], c)));
-#pragma unroll
-    for (int b = 0; b < TB; ++b) f[2 + b] = as_bf16x8(*reinterpret_cast<const uint4*>(st + lds_off64(brow[b], c)));
+    for (int i = 0; i < 2 + TB; ++i) f[i] = frag_short<TB>(st, va, vb, i);
   }
 
   template <int TB>
@@ -604,14 +633,13 @@ struct MfmaTile {
       const uint32_t ko = (uint32_t)min(kt + kShortStages, nk - 1) * ROWB64;
       const int sn = s == kShortStages - 1 ? 0 : s + 1;
       const uint8_t* rd = g_ring + sn * kStage;
-      const int c = (threadIdx.x & 63) >> 5;
+      const int lo = frag_lane_off(0), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
       for (int i = 0; i < D; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         issue_short_one<TB>(s, i, ko);
         if (i < 2 * TB) acc[i / TB][i % TB] = mfma32(f1[i / TB], f1[2 + i % TB], acc[i / TB][i % TB]);
-        if (i < 2 + TB)
-          f0[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rd + lds_off64(i < 2 ? arow[i] : brow[i - 2], c)));
+        if (i < 2 + TB) f0[i] = frag_short<TB>(rd, va, vb, i);
       }
       __builtin_amdgcn_sched_barrier(0);
       s = sn;
@@ -649,34 +677,60 @@ __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chu
 
 // Queue position -> tile index, with the L light tiles spread evenly between the H heavy ones
 // (heavy tiles are [0, H) in tile order, light ones [H, H + L)): among the first p positions,
-// floor(p * H / (H + L)) are heavy.
+// floor(p * H / (H + L)) are heavy.  (32-bit products while they fit.)
 __device__ __forceinline__ int interleave_tile(int p, int heavy, int ntiles) {
-  const int h0 = (int)(((long long)p * heavy) / ntiles);
-  const int h1 = (int)(((long long)(p + 1) * heavy) / ntiles);
+  int h0, h1;
+  if (ntiles < 65536) {
+    h0 = (int)((uint32_t)p * (uint32_t)heavy / (uint32_t)ntiles);
+    h1 = (int)((uint32_t)(p + 1) * (uint32_t)heavy / (uint32_t)ntiles);
+  } else {
+    h0 = (int)(((long long)p * heavy) / ntiles);
+    h1 = (int)(((long long)(p + 1) * heavy) / ntiles);
+  }
   return h1 > h0 ? h0 : heavy + (p - h0);
+}
+
+// Segment holding tile t, by binary search over the segments' first tiles cached in LDS.
+__device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 template <bool GU>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__ segs,
                                                           int32_t* __restrict__ meta) {
   __shared__ int slot;
+  __shared__ int seg_base[kSegCap];  // first tile of each segment
   const int nseg = meta[0], ntiles = meta[1], heavy = meta[kMetaHeavy];
   if (ntiles == 0) return;
+  for (int i = threadIdx.x; i < nseg; i += blockDim.x) seg_base[i] = segs[i].tile_base;
+  __syncthreads();
   const int chunk = max(1, (int)gridDim.x / kXcds);
   int q = 0;
   MfmaTile<GU> tile;
-  struct Cur { int si, m0, rows, n0, h; };
+  // the claimed tile; the epilogue's fields are copied here so that it reads no Seg memory after
+  // the next tile's loads were issued (a vector load would wait for them)
+  struct Cur { int m0, rows, n0, h, K, N, row0; void* out; };
   auto claim = [&](Cur& c) -> bool {
     const int pos = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);
     if (pos < 0) return false;
     const int t = interleave_tile(pos, heavy, ntiles);
-    c.si = __builtin_amdgcn_readfirstlane(find_seg(segs, nseg, t));
-    const Seg& sg = segs[c.si];
+    const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(seg_base, nseg, t));
+    const Seg& sg = segs[si];
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     c.m0 = mt * BM;
     c.rows = min(BM, sg.rows - c.m0);
     c.n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
+    c.K = sg.K;
+    c.N = sg.N;
+    c.row0 = sg.row0;
+    c.out = sg.out;
     tile.setup(sg, c.m0, c.rows, c.n0);
     c.h = __builtin_amdgcn_readfirstlane(tile.bm);
     tile.prologue(sg.K);
@@ -687,24 +741,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   for (;;) {
     // run, then start the next tile's loads before this tile's epilogue; each height has its own
     // branch so the accumulators a shorter tile leaves unused are dead around the loop
-    const Seg& sg = segs[cur.si];
-    Cur nxt;
-    bool more;
     if (cur.h == BM) {
-      tile.run_full(sg.K);
-      more = claim(nxt);
-      MfmaTileStore<GU>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+      tile.run_full(cur.K);
+      MfmaTileStore<GU>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     } else if (cur.h == 128) {
-      tile.template run_short<4>(sg.K);
-      more = claim(nxt);
-      MfmaTileStoreShort<GU, 4>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+      tile.template run_short<4>(cur.K);
+      MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     } else {
-      tile.template run_short<2>(sg.K);
-      more = claim(nxt);
-      MfmaTileStoreShort<GU, 2>(tile.acc, sg, cur.m0, cur.rows, cur.n0);
+      tile.template run_short<2>(cur.K);
+      MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     }
-    if (!more) break;
-    cur = nxt;
+    if (!claim(cur)) break;
   }
 }
 
