@@ -12,13 +12,11 @@ enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
 
 constexpr int kStreamMaxRows = 64;  // rows per weight-streaming pass
 // Automatic selection: an expert takes the weight-streaming family for a GEMM while its row
-// count is at most this, the LDS-tiled MFMA family above it.
-constexpr int kStreamRowsGateUp = 8;
-constexpr int kStreamRowsDown = 16;
-// Down GEMM with d_ff >= kStreamSplitK: the last MFMA m-tile of an expert moves to the streaming
-// family when it would hold at most this many rows.
-constexpr int kDownTailRows = 64;
-constexpr int kMfmaBM = 256;        // rows per LDS-tiled MFMA tile
+// count is at most this, the LDS-tiled MFMA family above it (whose short tiles stream the
+// weights of even a one-row gate/up expert faster, given enough tiles; see select.hip).
+constexpr int kStreamRowsGateUp = 0;
+constexpr int kStreamRowsDown = 8;
+constexpr int kMfmaBM = 256;        // rows per full LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile
 constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2

@@ -34,17 +34,11 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   if (e < nexp) c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
-  // Up to three segments per expert: gate/up, down, and the down GEMM's tail rows (see below).
-  // Segment j: gemm gj, family fm[j] (-1: none), rows [r0[j], r0[j] + nr[j]) of the expert.
-  constexpr int NS = 3;
-  int fm[NS], r0[NS], nr[NS], mt[NS], nt[NS], tn[NS], cls[NS];
+  // One segment per expert and GEMM: segment j is GEMM j (gate/up, down), family fm[j] (-1: none).
+  constexpr int NS = 2;
+  int fm[NS], mt[NS], nt[NS], tn[NS], cls[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int g = j == 0 ? kGemmGateUp : kGemmDown;
-    fm[j] = (j < 2 && e < nexp) ? pick_family(c, g, a.config, a.fp8) : -1;
-    r0[j] = 0;
-    nr[j] = c;
-  }
+  for (int j = 0; j < NS; ++j) fm[j] = e < nexp ? pick_family(c, j, a.config, a.fp8) : -1;
   // An MFMA tile costs a whole K loop on one CU however few rows it holds, so a GEMM whose MFMA
   // tiles would not fill two rounds of CUs (the last round is partly idle) keeps its small experts
   // (<= kStreamMaxRows rows) on the streaming tiles, which spread each expert's weights over many
@@ -62,26 +56,13 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     for (int j = 0; j < 2; ++j)
       if (fm[j] == kFamMfma && wtot[j] < 2 * a.num_cus && c <= kStreamMaxRows) fm[j] = kFamStream;
   }
-  // A down GEMM with long K spends the same LDS load time on a 256-row tile whatever its rows, so
-  // an expert whose last m-tile would hold at most kDownTailRows rows hands those rows to the
-  // weight-streaming family (its weights stream once more, at HBM rate) instead of adding one
-  // nearly empty MFMA tile per output tile.
-  if (fm[1] == kFamMfma && a.config < 0 && ffe >= kStreamSplitK && c > kMfmaBM) {
-    const int tail = c - (c - 1) / kMfmaBM * kMfmaBM;
-    if (tail <= kDownTailRows) {
-      nr[1] = c - tail;
-      fm[2] = kFamStream;
-      r0[2] = c - tail;
-      nr[2] = tail;
-    }
-  }
   // v: flags [gemm][fam][cls] (8), then tiles [gemm][fam][cls] (8)
   int v[16], ex[16], tot[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    const int g = j;
     const bool st = fm[j] == kFamStream;
     const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
     if (g == kGemmGateUp) {
@@ -91,7 +72,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
       nt[j] = (a.d + tn[j] - 1) / tn[j];  // a down tile of 256 columns may be half full at the edge
     }
-    mt[j] = (nr[j] + tm - 1) / tm;
+    mt[j] = (c + tm - 1) / tm;
     cls[j] = mt[j] >= 2 ? 0 : 1;
     // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
@@ -102,12 +83,10 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       }
   }
   block_scan<16, 16>(v, ex, tot, scan_lds);
-  // a down tail segment shares its (gemm, family, class) list with no other segment of the expert:
-  // the main down segment is MFMA, the gate/up one belongs to the other gemm
   int rank[NS], tbase[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    const int g = j;
     rank[j] = tbase[j] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -124,10 +103,10 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     if (fm[j] < 0) continue;
-    const int g = j == 0 ? kGemmGateUp : kGemmDown;
+    const int g = j;
     Seg sg;
-    sg.row0 = row0 + r0[j];
-    sg.rows = nr[j];
+    sg.row0 = row0;
+    sg.rows = c;
     sg.mtiles = mt[j];
     sg.expert = e;
     sg.tile_base = tbase[j];

@@ -156,8 +156,8 @@ LAYER = [
     _small("layer_T1", T=1, d=512, f=256, E=16, k=4, routing="dirichlet", alpha=1.0, cfg_index=107),
     _small("layer_big_expert", T=700, d=128, f=256, E=4, k=1, routing="dirichlet", alpha=0.1,
            cfg_index=108),
-    # d_ff >= 4096: an expert whose last 256-row tile holds <= 64 rows hands them to the streaming
-    # tiles in the down GEMM (320 rows: a 64-row tail, the largest that moves; 560 over 2 experts)
+    # long-K down GEMMs (d_ff = 4096) whose experts end in a short MFMA tile of 64 rows (320 rows),
+    # of 65 rows -> a 128-row tile (321), and two experts with different tails (560 over 2)
     _small("layer_down_tail64", T=320, d=128, f=4096, E=1, k=1, cfg_index=113),
     _small("layer_down_tail65", T=321, d=128, f=4096, E=1, k=1, cfg_index=114),
     _small("layer_down_tail2e", T=560, d=128, f=4096, E=2, k=1, cfg_index=115),
