@@ -88,10 +88,13 @@ int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Workspace of the grouped GEMMs: segment lists, queue counters and the SwiGLU output.
+// Workspace of the grouped GEMMs: segment lists, queue counters, the SwiGLU output and (bf16) the
+// last-round split-K counters and partial sums.
 struct FfnWs {
   Seg* segs;
   int32_t* meta;
+  int32_t* split_cnt;
+  float* split_part;
   void* h;
   float* hs;
   void* h_sh;
@@ -104,6 +107,12 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
   const size_t wb = p->wdtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
   f.segs = c.take<Seg>((size_t)2 * kNumFam * kSegCap);
   f.meta = c.take<int32_t>(2 * kNumFam * kMetaStride);
+  f.split_cnt = nullptr;
+  f.split_part = nullptr;
+  if (wb == 2) {
+    f.split_cnt = c.take<int32_t>((size_t)2 * kSplitMaxPieces);
+    f.split_part = c.take<float>((size_t)kSplitMaxPieces * kSplitSlotFloats);
+  }
   f.h = c.take<uint8_t>(n * p->d_ff * wb);
   f.hs = wb == 1 ? c.take<float>(n * (p->d_ff / 128)) : nullptr;
   f.h_sh = f.hs_sh = nullptr;
@@ -243,7 +252,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
   a.h = f.h; a.hs = f.hs;
   a.y = y_perm;
-  SelectOut o{f.segs, f.meta};
+  SelectOut o{f.segs, f.meta, f.split_cnt, f.split_part};
   hipError_t e = launch_select(a, o, stream);
   const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
   if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, p->config, n, stream);
@@ -358,7 +367,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.h = L.ffn.h; a.hs = L.ffn.hs;
   a.h_sh = L.ffn.h_sh; a.hs_sh = L.ffn.hs_sh;
   a.y = L.y; a.y_sh = L.ffn.y_sh;
-  SelectOut o{L.ffn.segs, L.ffn.meta};
+  SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_cnt, L.ffn.split_part};
 
   hipError_t e = mark(0);
   if (front_small_fits(T, k)) {

@@ -79,6 +79,10 @@ __device__ __forceinline__ void gstore8(void* base, size_t off, uint2 v) {
   *reinterpret_cast<__attribute__((address_space(1))) u32x2*>((gwchar*)base + off) =
       __builtin_bit_cast(u32x2, v);
 }
+__device__ __forceinline__ void gstore16(void* base, size_t off, uint4 v) {
+  *reinterpret_cast<__attribute__((address_space(1))) u32x4*>((gwchar*)base + off) =
+      __builtin_bit_cast(u32x4, v);
+}
 __device__ __forceinline__ void gstore4(void* base, size_t off, uint32_t v) {
   *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>((gwchar*)base + off) = v;
 }

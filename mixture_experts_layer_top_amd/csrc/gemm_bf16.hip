@@ -214,10 +214,13 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // tile was measured: ~3% on many-expert prefill, -2% on 8-expert prefill and ~40% more gate/up L2
 // miss traffic).
 //
-// Scheduling: one persistent workgroup per CU.  The tile order puts the m-tiles of one weight tile
-// next to each other; consecutive runs of (CUs per XCD) tiles go to one XCD, so tiles that share
-// weight and activation tiles run side by side on the same L2.  Each XCD has its own queue; a
-// workgroup whose queue is empty takes work from the other XCDs' queues.
+// Scheduling: one persistent workgroup per CU.  Tiles are handed out in one of two orders chosen by
+// the selection kernel (select_dev.h): class-1 (light) tiles spread evenly between class-0 ones, or,
+// for GEMMs of few rounds, longest first.  Within a segment the m-tiles of one weight tile are next
+// to each other; consecutive runs of (CUs per XCD) tiles go to
+// one XCD, so tiles that share weight and activation tiles run side by side on the same L2.  Each
+// XCD has its own queue; a workgroup whose queue is empty takes work from the other XCDs' queues.
+// Tiles past the last whole round of CUs may be split in K (see kernels.h).
 // ------------------------------------------------------------------------------------------------
 constexpr int BM = kMfmaBM;
 constexpr int BNW = 256;                  // weight rows per tile
@@ -397,7 +400,8 @@ struct MfmaTile {
     return j < NTS ? abase : ((!GU || j < NTS + 4) ? wbase0 : wbase1);
   }
 
-  __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0) {
+  // kt0: first 64-wide K-step of the tile's K range (a piece of a split tile starts past 0)
+  __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0, int kt0) {
     const int lane = threadIdx.x & 63;
     wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     bm = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
@@ -428,10 +432,11 @@ struct MfmaTile {
       // weight slot are never issued)
       int wr = GU ? n0 + ((r - bm) & 127) : n0 + (r - bm);
       wr = wr < sg.N ? wr : sg.N - 1;
-      const uint32_t woff = (uint32_t)wr * rowbytes + c * 16;
+      const uint32_t woff = (uint32_t)wr * rowbytes + c * 16 + (uint32_t)kt0 * ROWB64;
       if (j < 8) {
         const int rr = 32 * j + 8 * wvu + (lane >> 3);
-        const uint32_t toff = (uint32_t)src[j] * rowbytes + (rr < rows ? c * 16 : 0);
+        const uint32_t toff =
+            (uint32_t)src[j] * rowbytes + (rr < rows ? c * 16 + (uint32_t)kt0 * ROWB64 : 0);
         off[j] = j < nts ? toff : woff;
       } else {
         off[j] = woff;
@@ -525,8 +530,8 @@ struct MfmaTile {
     issue<1>(1);
   }
 
-  __device__ __forceinline__ void run_full(int K) {
-    const int nk = K / BK64;  // K is a multiple of 128, so nk is even
+  // nk: K-steps of the tile's K range (even)
+  __device__ __forceinline__ void run_full(int nk) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -605,10 +610,9 @@ struct MfmaTile {
   }
 
   template <int TB>
-  __device__ __forceinline__ void run_short(int K) {
+  __device__ __forceinline__ void run_short(int nk) {
     constexpr int kStage = (TB * 32 + BNW) * ROWB64;
     constexpr int D = TB + 8;  // loads per thread per stage
-    const int nk = K / BK64;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -648,10 +652,10 @@ struct MfmaTile {
     __builtin_amdgcn_s_barrier();
   }
 
-  __device__ __forceinline__ void prologue(int K) {
+  __device__ __forceinline__ void prologue(int nk) {
     if (bm == BM) prologue_full();
-    else if (bm == 128) prologue_short<4>(K / BK64);
-    else prologue_short<2>(K / BK64);
+    else if (bm == 128) prologue_short<4>(nk);
+    else prologue_short<2>(nk);
   }
 };
 
@@ -675,9 +679,9 @@ __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chu
   return -1;
 }
 
-// Queue position -> tile index, with the L light tiles spread evenly between the H heavy ones
-// (heavy tiles are [0, H) in tile order, light ones [H, H + L)): among the first p positions,
-// floor(p * H / (H + L)) are heavy.  (32-bit products while they fit.)
+// Queue position -> tile index, with the L class-1 tiles spread evenly between the H class-0 ones
+// (class-0 tiles are [0, H) in tile order, class-1 ones [H, H + L)): among the first p positions,
+// floor(p * H / (H + L)) are class 0.  (32-bit products while they fit.)
 __device__ __forceinline__ int interleave_tile(int p, int heavy, int ntiles) {
   int h0, h1;
   if (ntiles < 65536) {
@@ -701,58 +705,175 @@ __device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
   return lo;
 }
 
-template <bool GU>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__ segs,
-                                                          int32_t* __restrict__ meta) {
-  __shared__ int slot;
-  __shared__ int seg_base[kSegCap];  // first tile of each segment
-  const int nseg = meta[0], ntiles = meta[1], heavy = meta[kMetaHeavy];
-  if (ntiles == 0) return;
-  for (int i = threadIdx.x; i < nseg; i += blockDim.x) seg_base[i] = segs[i].tile_base;
+// A piece of a split tile (accumulator blocks a < NA, b < NB): writes its partial sums to its slot
+// of the tile's S slots, then counts itself done; the piece that finds the other S - 1 done adds
+// the S slots in piece order into acc (its own from registers, bit-identical to its slot) and
+// returns true, and only it runs the epilogue.  Release fence before the count, acquire fence
+// after it: the slots are written and read by CUs of different XCDs (different L2s).
+template <int NA, int NB>
+__device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* tile_part, int32_t* cnt,
+                                             int S, int piece, int* lds) {
+  // slot layout: 4 accumulators (16 B) per thread, threads adjacent, so each store is one
+  // contiguous kilobyte per wavefront; group (a, b, q) of a slot starts at float (a*16+b*4+q)*1024.
+  // Group bases are uniform; the lane's offset is one register, produced by asm so that the
+  // compiler cannot fold it into 64 per-group addresses hoisted out of the tile loop (they would
+  // not fit in registers).
+  uint32_t lane_off;
+  asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(lane_off) : "v"((uint32_t)threadIdx.x));
+  float* mine = tile_part + (size_t)piece * kSplitSlotFloats;
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint4 v;
+        v.x = __float_as_uint(acc[a][b][q * 4 + 0]);
+        v.y = __float_as_uint(acc[a][b][q * 4 + 1]);
+        v.z = __float_as_uint(acc[a][b][q * 4 + 2]);
+        v.w = __float_as_uint(acc[a][b][q * 4 + 3]);
+        gstore16(mine + ((a * 4 + b) * 4 + q) * 1024, lane_off, v);
+      }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  const int chunk = max(1, (int)gridDim.x / kXcds);
+  if (threadIdx.x == 0)
+    *lds = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int done = __builtin_amdgcn_readfirstlane(*lds);
+  __syncthreads();  // (the next tile's queue pop reuses *lds)
+  if (done != S - 1) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_barrier(0);  // one group's loads at a time (bounded registers)
+        const float* gb = tile_part + ((a * 4 + b) * 4 + q) * 1024;
+        float t[4];
+        for (int p = 0; p < S; ++p) {
+          float v[4];
+          if (p == piece) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[a][b][q * 4 + i];
+          } else {
+            const uint4 w = gload16(gb + (size_t)p * kSplitSlotFloats, lane_off);
+            v[0] = __uint_as_float(w.x);
+            v[1] = __uint_as_float(w.y);
+            v[2] = __uint_as_float(w.z);
+            v[3] = __uint_as_float(w.w);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = p == 0 ? v[i] : t[i] + v[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][b][q * 4 + i] = t[i];
+      }
+  return true;
+}
+
+// The claimed tile.  The epilogue's fields are copied here so that it reads no Seg memory after
+// the next tile's loads were issued (a vector load would wait for them).  piece: -1 for a whole
+// tile, else the piece of split tile u, covering K-steps [piece * nk, (piece + 1) * nk).
+struct MfmaCur { int m0, rows, n0, h, nk, N, row0, piece, u; void* out; };
+
+// One MFMA list's queue as the persistent loop sees it (positions: [0, sbase) whole tiles, then S
+// pieces for each tile of [sbase, ntiles)).
+struct MfmaQueue {
+  const Seg* segs;
+  int32_t* queues;
+  const int* seg_base;  // LDS: first tile of each segment
+  int nseg, ntiles, ntiles0, sbase, S, nq, chunk;
+  bool in_order;
+};
+
+// The persistent tile loop.  Instantiated with and without the split-K epilogue, so that lists that
+// split nothing (the common case) run code whose registers the split path does not disturb.
+template <bool GU, bool kSplit>
+__device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, int32_t* split_cnt,
+                                                float* split_part, int* slot) {
   int q = 0;
   MfmaTile<GU> tile;
-  // the claimed tile; the epilogue's fields are copied here so that it reads no Seg memory after
-  // the next tile's loads were issued (a vector load would wait for them)
-  struct Cur { int m0, rows, n0, h, K, N, row0; void* out; };
-  auto claim = [&](Cur& c) -> bool {
-    const int pos = pop_tile_xcd(meta + kMetaQueue, ntiles, chunk, &slot, q);
+  auto claim = [&](MfmaCur& c) -> bool {
+    const int pos = pop_tile_xcd(Q.queues, kSplit ? Q.nq : Q.ntiles, Q.chunk, slot, q);
     if (pos < 0) return false;
-    const int t = interleave_tile(pos, heavy, ntiles);
-    const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(seg_base, nseg, t));
-    const Seg& sg = segs[si];
+    int tp = pos;
+    c.piece = -1;
+    c.u = 0;
+    if (kSplit && pos >= Q.sbase) {
+      c.u = (pos - Q.sbase) / Q.S;
+      c.piece = pos - Q.sbase - c.u * Q.S;
+      tp = Q.sbase + c.u;
+    }
+    const int t = Q.in_order ? tp : interleave_tile(tp, Q.ntiles0, Q.ntiles);
+    const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(Q.seg_base, Q.nseg, t));
+    const Seg& sg = Q.segs[si];
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     c.m0 = mt * BM;
     c.rows = min(BM, sg.rows - c.m0);
     c.n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
-    c.K = sg.K;
+    const int nkt = sg.K / BK64;
+    c.nk = c.piece < 0 ? nkt : nkt / Q.S;
     c.N = sg.N;
     c.row0 = sg.row0;
     c.out = sg.out;
-    tile.setup(sg, c.m0, c.rows, c.n0);
+    tile.setup(sg, c.m0, c.rows, c.n0, c.piece < 0 ? 0 : c.piece * c.nk);
     c.h = __builtin_amdgcn_readfirstlane(tile.bm);
-    tile.prologue(sg.K);
+    tile.prologue(c.nk);
     return true;
   };
-  Cur cur;
+  auto part = [&](const MfmaCur& c) { return split_part + (size_t)c.u * Q.S * kSplitSlotFloats; };
+  MfmaCur cur;
   if (!claim(cur)) return;
   for (;;) {
-    // run, then start the next tile's loads before this tile's epilogue; each height has its own
-    // branch so the accumulators a shorter tile leaves unused are dead around the loop
+    // run, then this tile's epilogue, then the next claim; each height has its own branch so the
+    // accumulators a shorter tile leaves unused are dead around the loop
     if (cur.h == BM) {
-      tile.run_full(cur.K);
-      MfmaTileStore<GU>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      tile.run_full(cur.nk);
+      if (!kSplit || cur.piece < 0 ||
+          split_reduce<4, 4>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+        MfmaTileStore<GU>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     } else if (cur.h == 128) {
-      tile.template run_short<4>(cur.K);
-      MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      tile.template run_short<4>(cur.nk);
+      if (!kSplit || cur.piece < 0 ||
+          split_reduce<2, 4>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+        MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     } else {
-      tile.template run_short<2>(cur.K);
-      MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      tile.template run_short<2>(cur.nk);
+      if (!kSplit || cur.piece < 0 ||
+          split_reduce<2, 2>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+        MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
     }
     if (!claim(cur)) break;
   }
+}
+
+template <bool GU>
+__global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__ segs,
+                                                          int32_t* __restrict__ meta,
+                                                          int32_t* __restrict__ split_cnt,
+                                                          float* __restrict__ split_part) {
+  __shared__ int slot;
+  __shared__ int seg_base[kSegCap];
+  MfmaQueue Q;
+  Q.ntiles = meta[1];
+  if (Q.ntiles == 0) return;
+  Q.segs = segs;
+  Q.queues = meta + kMetaQueue;
+  Q.seg_base = seg_base;
+  Q.nseg = meta[0];
+  Q.ntiles0 = meta[kMetaClass0];
+  Q.in_order = meta[kMetaOrder] != 0;
+  Q.sbase = meta[kMetaSplitBase];
+  Q.S = meta[kMetaSplitS];
+  Q.nq = Q.sbase + (Q.ntiles - Q.sbase) * Q.S;
+  Q.chunk = max(1, (int)gridDim.x / kXcds);
+  for (int i = threadIdx.x; i < Q.nseg; i += blockDim.x) seg_base[i] = segs[i].tile_base;
+  __syncthreads();
+  if (Q.S > 1) mfma_persistent<GU, true>(Q, split_cnt, split_part, &slot);
+  else mfma_persistent<GU, false>(Q, split_cnt, split_part, &slot);
 }
 
 hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, bool stream, bool mfma,
@@ -761,12 +882,13 @@ hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, bool stream
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
+  int32_t* cnt = o.split_cnt ? o.split_cnt + g * kSplitMaxPieces : nullptr;
   if (g == kGemmGateUp) {
     if (stream) gemm_stream_bf16<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm);
+    if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   } else {
     if (stream) gemm_stream_bf16<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm);
+    if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   }
   return hipGetLastError();
 }

@@ -25,7 +25,7 @@ constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 // wavefront per 16 columns over the whole K, or a four-way split of a short K, streams slower.
 constexpr int kStreamSplitK = 4096;
 __host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 32; }
-constexpr int kSegCap = 1024;       // segment slots per (gemm, family); >= E + 1
+constexpr int kSegCap = 1040;       // segment slots per (gemm, family); >= 2 * (E + 1)
 // fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
 // the weights from L2; 32 keeps the kernels' registers low enough for 3 or more wavefronts per
 // SIMD), h columns per gate/up tile (one whole 128-column requantisation block), y columns per
@@ -51,10 +51,21 @@ struct Seg {
   int32_t tn;           // output columns per tile
 };
 
+// Last-round split of an MFMA GEMM: when its tiles leave a last round of CUs partly idle, the
+// tiles of that round are split two or four ways in K, every piece writes its fp32 partial sums
+// to a slot of split_part, and the last piece of a tile to finish adds the slots in piece order
+// (so results do not depend on which piece finishes last) and runs the epilogue.
+constexpr int kSplitMaxPieces = 256;  // partial-sum slots (one round of CUs)
+constexpr int kSplitSlotFloats = 256 * 256;  // one full tile's accumulators
+constexpr int kSplitMaxRounds = 3;    // longest-first order and split: fewer whole rounds than this
+
 // Where the selection kernel writes its results (all inside the caller's workspace).
 struct SelectOut {
-  Seg* segs;        // [2 gemms][kNumFam][E + 1]
-  int32_t* meta;    // [2 gemms][kNumFam] { nseg, ntiles, queue } -> 3 ints each, 16 entries padded
+  Seg* segs;           // [2 gemms][kNumFam][E + 1]
+  int32_t* meta;       // [2 gemms][kNumFam][kMetaStride] (layout below)
+  int32_t* split_cnt;  // [2 gemms][kSplitMaxPieces] pieces finished per split tile (bf16 only)
+  float* split_part;   // [kSplitMaxPieces][kSplitSlotFloats] partial sums (bf16 only; the two
+                       // GEMMs run one after the other and share it)
 };
 
 // Everything the selection kernel needs to describe the two GEMMs.
@@ -76,12 +87,17 @@ struct SelectArgs {
 };
 
 // ints per (gemm, family): nseg, ntiles, then kXcds queue counters (the stream family uses the
-// first), zeroed by the selection kernel before each GEMM, then the number of heavy tiles (those
-// of experts with two or more m-tiles, which come first in tile order).
+// first), zeroed by the selection kernel before each GEMM, then the number of class-0 tiles (which
+// come first in tile order; see select_dev.h), then (MFMA family) the first queue position whose
+// tile is split in K and the pieces per split tile (positions [0, base) are whole tiles, and each
+// tile of [base, ntiles) takes S consecutive positions), then the ordering mode.
 constexpr int kMetaStride = 16;
 constexpr int kMetaQueue = 2;
-constexpr int kMetaHeavy = kMetaQueue + kXcds;
-static_assert(kMetaHeavy < kMetaStride, "meta layout");
+constexpr int kMetaClass0 = kMetaQueue + kXcds;
+constexpr int kMetaSplitBase = kMetaClass0 + 1;
+constexpr int kMetaSplitS = kMetaClass0 + 2;
+constexpr int kMetaOrder = kMetaClass0 + 3;  // 1: longest first, 0: class-1 tiles interleaved
+static_assert(kMetaOrder < kMetaStride, "meta layout");
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t s);

@@ -18,10 +18,11 @@
 // An MFMA tile costs a whole K loop on one CU however few rows it holds: when a GEMM's MFMA tiles
 // would not fill two rounds of CUs, its experts of up to 64 rows take the streaming tiles, which
 // spread each expert's weights over many workgroups.  Block-scaled fp8 experts always take the
-// streaming family (up to 32 rows per pass).  Inside a (GEMM, family) list, experts with several
-// m-tiles come first ("heavy"); the MFMA kernels spread the light tiles evenly between the heavy
-// ones, so HBM-bound and MFMA-bound tiles run side by side.  Experts with no rows get no segment
-// and their weights are never read.
+// streaming family (up to 32 rows per pass).  Inside an MFMA list, segments of full-height tiles come
+// first and those of shorter tiles last (an expert's short last m-tile is a segment of its own), so
+// the persistent kernel hands out the longest tiles first and the short ones fill the last round;
+// when that round would leave CUs idle, its tiles are split in K (kernels.h).  Experts with no rows
+// get no segment and their weights are never read.
 #include "select_dev.h"
 
 namespace moe {
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, SelectOut o)
 }
 
 hipError_t launch_select(const SelectArgs& a, const SelectOut& o, hipStream_t s) {
-  select_kernel<<<1, kSelMax, 0, s>>>(a, o);
+  select_kernel<<<1, kSelThreads, 0, s>>>(a, o);
   return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 
 namespace moe {
 
-constexpr int kSelMax = kSegCap;
+constexpr int kSelThreads = 1024;  // one thread per expert (E + 1 <= kSelThreads)
+static_assert(kSegCap >= 2 * (kSelThreads / 2 + 1), "two segments per expert (E <= 512)");
 
 __device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
   if (c <= 0) return -1;
@@ -18,12 +19,21 @@ __device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
   return c <= (g == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown) ? kFamStream : kFamMfma;
 }
 
-// Per expert (one thread each, blockDim.x = 1024 >= E + 1) and per GEMM: family, tile counts, and
-// the segment's place in its (GEMM, family) list.  Order inside a list: experts with two or more
-// m-tiles first ("heavy"), then the rest ("light"), each by expert id; the ranks and tile bases
-// come from one block-wide scan of 16 per-expert counts.  Every thread of the block must call this
-// (it contains barriers).  Counts and offsets come from LDS when the caller has them there
-// (lds_counts, lds_offsets), else from a.counts / a.offsets.
+// Per expert (one thread each, blockDim.x = kSelThreads >= E + 1) and per GEMM: family, tile
+// counts, and the segments' places in their (GEMM, family) list.  Each list has two classes of
+// segments, class 0 first, each class by expert id:
+//  * default: class 0 = experts with two or more m-tiles ("heavy"), class 1 = the rest ("light");
+//    the MFMA kernel spreads the light tiles evenly between the heavy ones, so HBM-bound and
+//    MFMA-bound tiles run side by side, and an expert's last m-tile stays next to its siblings
+//    (which share its weight tile in L2);
+//  * MFMA list of one to kSplitMaxRounds rounds of tiles ("longest first"): round
+//    quantization dominates, so an expert whose last m-tile would hold at most 128 rows gets that
+//    tail as a segment of its own, class 0 = segments of full-height tiles, class 1 = shorter ones,
+//    and the kernel hands them out in order (longest first, short tiles fill the last round, whose
+//    tiles may be split in K).
+// The ranks and tile bases come from one block-wide scan of 16 per-expert counts.  Every thread of
+// the block must call this (it contains barriers).  Counts and offsets come from LDS when the
+// caller has them there (lds_counts, lds_offsets), else from a.counts / a.offsets.
 __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOut& o,
                                              const int* lds_counts = nullptr,
                                              const int* lds_offsets = nullptr) {
@@ -34,36 +44,51 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   if (e < nexp) c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
-  // One segment per expert and GEMM: segment j is GEMM j (gate/up, down), family fm[j] (-1: none).
-  constexpr int NS = 2;
-  int fm[NS], mt[NS], nt[NS], tn[NS], cls[NS];
+  int fm[2];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) fm[j] = e < nexp ? pick_family(c, j, a.config, a.fp8) : -1;
+  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8) : -1;
   // An MFMA tile costs a whole K loop on one CU however few rows it holds, so a GEMM whose MFMA
   // tiles would not fill two rounds of CUs (the last round is partly idle) keeps its small experts
   // (<= kStreamMaxRows rows) on the streaming tiles, which spread each expert's weights over many
-  // workgroups.
-  if (a.config < 0 && !a.fp8) {
+  // workgroups.  The same (block-wide) totals give the list's ordering mode: one to
+  // kSplitMaxRounds rounds -> longest first (below one round every tile starts at once and order
+  // does not matter).
+  bool lpt[2] = {false, false};
+  if (!a.fp8) {
     int w[2], wex[2], wtot[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      w[j] = fm[j] == kFamMfma
+    for (int g = 0; g < 2; ++g)
+      w[g] = fm[g] == kFamMfma
                  ? (c + kMfmaBM - 1) / kMfmaBM *
-                       (j == 0 ? ffe / kMfmaBNGateUp : (a.d + kMfmaBNDown - 1) / kMfmaBNDown)
+                       (g == 0 ? ffe / kMfmaBNGateUp : (a.d + kMfmaBNDown - 1) / kMfmaBNDown)
                  : 0;
     block_scan<2, 16>(w, wex, wtot, scan_lds);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (fm[j] == kFamMfma && wtot[j] < 2 * a.num_cus && c <= kStreamMaxRows) fm[j] = kFamStream;
+    for (int g = 0; g < 2; ++g) {
+      if (a.config < 0 && fm[g] == kFamMfma && wtot[g] < 2 * a.num_cus && c <= kStreamMaxRows)
+        fm[g] = kFamStream;
+      const int C = min(a.num_cus, kSplitMaxPieces);
+      lpt[g] = wtot[g] >= C && wtot[g] < kSplitMaxRounds * C;
+    }
   }
+  // Segment j = 2 * gemm + part (part 0: main, 1: MFMA tail), rows [r0[j], r0[j] + nr[j]) of the
+  // expert; fam[j] < 0: no such segment.
+  constexpr int NS = 4;
+  const int tail = c > kMfmaBM && c % kMfmaBM <= kMfmaBM / 2 ? c % kMfmaBM : 0;
+  int fam[NS], r0[NS], nr[NS], mt[NS], nt[NS], tn[NS], cls[NS];
   // v: flags [gemm][fam][cls] (8), then tiles [gemm][fam][cls] (8)
   int v[16], ex[16], tot[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const int g = j;
-    const bool st = fm[j] == kFamStream;
+    const int g = j >> 1, part = j & 1;
+    const bool mf = fm[g] == kFamMfma;
+    const bool split = mf && lpt[g] && tail > 0;
+    fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
+    r0[j] = part == 0 ? 0 : c - tail;
+    nr[j] = part == 0 ? (split ? c - tail : c) : tail;
+    const bool st = fam[j] == kFamStream;
     const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
     if (g == kGemmGateUp) {
       tn[j] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
@@ -72,26 +97,28 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
       nt[j] = (a.d + tn[j] - 1) / tn[j];  // a down tile of 256 columns may be half full at the edge
     }
-    mt[j] = (c + tm - 1) / tm;
-    cls[j] = mt[j] >= 2 ? 0 : 1;
+    mt[j] = (nr[j] + tm - 1) / tm;
+    cls[j] = st || !lpt[g] ? (mt[j] >= 2 ? 0 : 1) : (nr[j] <= kMfmaBM / 2 ? 1 : 0);
     // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (fm[j] >= 0 && i == (g * 2 + fm[j]) * 2 + cls[j]) {
+      if (fam[j] >= 0 && i == (g * 2 + fam[j]) * 2 + cls[j]) {
         v[i] += 1;
         v[8 + i] += mt[j] * nt[j];
       }
   }
   block_scan<16, 16>(v, ex, tot, scan_lds);
+  // (an expert's two segments of one GEMM have different classes, so each list index i takes at
+  // most one segment per expert)
   int rank[NS], tbase[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const int g = j;
+    const int g = j >> 1;
     rank[j] = tbase[j] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (fm[j] >= 0 && i == (g * 2 + fm[j]) * 2 + cls[j]) {
-        // light experts follow all heavy ones of their list
+      if (fam[j] >= 0 && i == (g * 2 + fam[j]) * 2 + cls[j]) {
+        // class-1 segments follow all class-0 ones of their list
         rank[j] = ((i & 1) ? tot[i - 1] : 0) + ex[i];
         tbase[j] = ((i & 1) ? tot[8 + i - 1] : 0) + ex[8 + i];
       }
@@ -102,11 +129,11 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   const int row0 = (e < nexp && !shared) ? (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e)) : 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    if (fm[j] < 0) continue;
-    const int g = j;
+    if (fam[j] < 0) continue;
+    const int g = j >> 1;
     Seg sg;
-    sg.row0 = row0;
-    sg.rows = c;
+    sg.row0 = row0 + r0[j];
+    sg.rows = nr[j];
     sg.mtiles = mt[j];
     sg.expert = e;
     sg.tile_base = tbase[j];
@@ -157,23 +184,47 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
         sg.out = a.y;
       }
     }
-    o.segs[((size_t)g * kNumFam + fm[j]) * kSelMax + rank[j]] = sg;
+    o.segs[((size_t)g * kNumFam + fam[j]) * kSegCap + rank[j]] = sg;
   }
-  // per (gemm, family): segment count, tile count, zeroed queues, heavy tile count
+  // per (gemm, family): segment count, tile count, zeroed queues, class-0 tile count
   if (e < 2 * kNumFam) {  // e = gemm * kNumFam + family; its flags and tiles sit at 2e, 2e + 1
-    int nseg = 0, ntl = 0, heavy = 0;
+    int nseg = 0, ntl = 0, ntl0 = 0;
 #pragma unroll
     for (int i = 0; i < 2 * kNumFam; ++i)
       if (i == e) {
         nseg = tot[2 * i] + tot[2 * i + 1];
         ntl = tot[8 + 2 * i] + tot[8 + 2 * i + 1];
-        heavy = tot[8 + 2 * i];
+        ntl0 = tot[8 + 2 * i];
       }
     int32_t* m = o.meta + e * kMetaStride;
     m[0] = nseg;
     m[1] = ntl;
     for (int q = kMetaQueue; q < kMetaQueue + kXcds; ++q) m[q] = 0;
-    m[kMetaHeavy] = heavy;
+    m[kMetaClass0] = ntl0;
+    // MFMA lists of bf16 GEMMs with fewer than kSplitMaxRounds whole rounds (longest first when
+    // there is at least one) split in K the tiles past the last whole round of CUs, S = 4 or 2
+    // ways, when their pieces still fit one round, every piece keeps an even number of 64-wide
+    // K-steps, and K is the same for every segment.
+    int base = ntl, S = 1;
+    const int g = e / kNumFam;
+    const int K = g == kGemmGateUp ? a.d : a.f;
+    const bool uniform_k = g == kGemmGateUp || !a.has_shared || a.f_sh == a.f;
+    const int C = min(a.num_cus, kSplitMaxPieces);
+    const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8;
+    m[kMetaOrder] = mfma_bf16 && lpt[g] ? 1 : 0;  // (lpt[] is the same for every thread)
+    if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_cnt && uniform_k) {
+      const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
+      if (rem > 0) {
+        if (rem * 4 <= C && nk % 8 == 0) S = 4;
+        else if (rem * 2 <= C && nk % 4 == 0) S = 2;
+      }
+      if (S > 1) {
+        base = ntl - rem;
+        for (int u = 0; u < rem; ++u) o.split_cnt[g * kSplitMaxPieces + u] = 0;
+      }
+    }
+    m[kMetaSplitBase] = base;
+    m[kMetaSplitS] = S;
   }
 }
 
