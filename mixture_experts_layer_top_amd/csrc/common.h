@@ -24,8 +24,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// Two fp32 -> packed bf16 (lo in the low half), round to nearest even: one v_cvt_pk_bf16_f32 on
+// gfx950 (the same rounding as f32_to_bf16 for finite inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // SiLU(g) * u in fp32, with the hardware exp2 and reciprocal (about 1 ulp each; the result is then
