@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -124,15 +125,25 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
   }
 }
 
-// max_rows bounds the rows of any one expert; when no expert can pass the streaming threshold the
-// MFMA kernel (whose queue would be empty) is not launched.
-hipError_t launch_gemms(const SelectOut& o, int gemm, int fp8, int config, int64_t max_rows,
-                        hipStream_t s) {
-  if (fp8) return moe::launch_gemms_fp8(o, gemm, device_cus(), s);
+// max_rows bounds the rows of any one expert and total_rows the rows of all of them.  The MFMA
+// kernel (whose queue would be empty) is not launched when no expert can pass the streaming
+// threshold, nor when the selection's two-round rule must move every expert to the streaming
+// tiles: no expert exceeds kStreamMaxRows rows and even one m-tile per expert that can hold rows
+// would not make two rounds of CUs.
+hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
+                        int64_t total_rows, hipStream_t s) {
+  const int cus = device_cus();
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
   const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
-  const bool stream = config != MOE_CONFIG_MFMA;
-  const bool mfma = config == MOE_CONFIG_MFMA || (config == MOE_CONFIG_AUTO && max_rows > thr);
-  return moe::launch_gemms_bf16(o, gemm, device_cus(), stream, mfma, s);
+  const bool stream = p->config != MOE_CONFIG_MFMA;
+  bool mfma = p->config == MOE_CONFIG_MFMA || (p->config == MOE_CONFIG_AUTO && max_rows > thr);
+  if (mfma && p->config == MOE_CONFIG_AUTO && max_rows <= kStreamMaxRows && !p->has_shared) {
+    const int64_t experts = std::min<int64_t>(p->num_experts, total_rows);
+    const int64_t nt = gemm == kGemmGateUp ? p->d_ff / kMfmaBNGateUp
+                                           : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
+    if (experts * nt < 2 * (int64_t)cus) mfma = false;
+  }
+  return moe::launch_gemms_bf16(o, gemm, cus, stream, mfma, s);
 }
 }  // namespace
 
@@ -255,8 +266,8 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   SelectOut o{f.segs, f.meta, f.split_cnt, f.split_part};
   hipError_t e = launch_select(a, o, stream);
   const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
-  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, p->config, n, stream);
-  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, p->config, n, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, n, n, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, n, n, stream);
   return hip_status(e);
 }
 
@@ -393,9 +404,9 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
     if (e == hipSuccess) e = mark(4);
   }
   // each token routes to k distinct experts, so no expert (nor the shared one) holds more than T rows
-  if (e == hipSuccess) e = launch_gemms(o, kGemmGateUp, fp8, p->config, T, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, T, (int64_t)T * p->top_k, stream);
   if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess) e = launch_gemms(o, kGemmDown, fp8, p->config, T, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, T, (int64_t)T * p->top_k, stream);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)
     e = launch_combine(L.y, slot_dst, wts, T, k, d, p->has_shared ? L.ffn.y_sh : nullptr, out,
