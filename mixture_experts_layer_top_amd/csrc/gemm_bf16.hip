@@ -214,9 +214,10 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // tile was measured: ~3% on many-expert prefill, -2% on 8-expert prefill and ~40% more gate/up L2
 // miss traffic).
 //
-// Scheduling: one persistent workgroup per CU.  Tiles are handed out in one of two orders chosen by
-// the selection kernel (select_dev.h): class-1 (light) tiles spread evenly between class-0 ones, or,
-// for GEMMs of few rounds, longest first.  Within a segment the m-tiles of one weight tile are next
+// Scheduling: one persistent workgroup per CU.  Tiles are handed out in one of three orders chosen
+// by the selection kernel (select_dev.h): light tiles spread between heavy ones; XCD chunks of
+// short tiles spread between chunks of full-height ones (long K); or, for GEMMs of few rounds,
+// longest first.  Within a segment the m-tiles of one weight tile are next
 // to each other; consecutive runs of (CUs per XCD) tiles go to
 // one XCD, so tiles that share weight and activation tiles run side by side on the same L2.  Each
 // XCD has its own queue; a workgroup whose queue is empty takes work from the other XCDs' queues.
@@ -679,9 +680,24 @@ __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chu
   return -1;
 }
 
-// Queue position -> tile index, with the L class-1 tiles spread evenly between the H class-0 ones
-// (class-0 tiles are [0, H) in tile order, class-1 ones [H, H + L)): among the first p positions,
-// floor(p * H / (H + L)) are class 0.  (32-bit products while they fit.)
+// Queue position -> tile index in the chunked order: class-0 tiles are [0, H) in tile order,
+// class-1 ones [H, N).  Positions come in units of B (one XCD chunk); each class's whole units are
+// spread evenly over the first U0 + U1 units (among the first u units, floor(u * U1 / U) are
+// class 1), and the two classes' partial units (fewer than B tiles each) come last.
+__device__ __forceinline__ int chunked_interleave(int p, int H, int N, int B) {
+  const int L = N - H, U0 = H / B, U1 = L / B, U = U0 + U1;
+  const int u = p / B, o = p - u * B;
+  if (u < U) {
+    const int c1 = (int)((long long)u * U1 / U), c1n = (int)((long long)(u + 1) * U1 / U);
+    return c1n > c1 ? H + c1 * B + o : (u - c1) * B + o;
+  }
+  const int q = p - U * B, r0 = H - U0 * B;
+  return q < r0 ? U0 * B + q : H + U1 * B + (q - r0);
+}
+
+// Queue position -> tile index in the mixed order: the L class-1 tiles spread evenly between the
+// H class-0 ones (class-0 tiles are [0, H) in tile order, class-1 ones [H, H + L)): among the first
+// p positions, floor(p * H / (H + L)) are class 0.  (32-bit products while they fit.)
 __device__ __forceinline__ int interleave_tile(int p, int heavy, int ntiles) {
   int h0, h1;
   if (ntiles < 65536) {
@@ -785,7 +801,7 @@ struct MfmaQueue {
   int32_t* queues;
   const int* seg_base;  // LDS: first tile of each segment
   int nseg, ntiles, ntiles0, sbase, S, nq, chunk;
-  bool in_order;
+  int order;  // TileOrder
 };
 
 // The persistent tile loop.  Instantiated with and without the split-K epilogue, so that lists that
@@ -806,7 +822,9 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, int32_t* spl
       c.piece = pos - Q.sbase - c.u * Q.S;
       tp = Q.sbase + c.u;
     }
-    const int t = Q.in_order ? tp : interleave_tile(tp, Q.ntiles0, Q.ntiles);
+    const int t = Q.order == kOrderLongestFirst ? tp
+                  : Q.order == kOrderChunks      ? chunked_interleave(tp, Q.ntiles0, Q.ntiles, Q.chunk)
+                                                 : interleave_tile(tp, Q.ntiles0, Q.ntiles);
     const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(Q.seg_base, Q.nseg, t));
     const Seg& sg = Q.segs[si];
     const int local = t - sg.tile_base;
@@ -865,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   Q.seg_base = seg_base;
   Q.nseg = meta[0];
   Q.ntiles0 = meta[kMetaClass0];
-  Q.in_order = meta[kMetaOrder] != 0;
+  Q.order = meta[kMetaOrder];
   Q.sbase = meta[kMetaSplitBase];
   Q.S = meta[kMetaSplitS];
   Q.nq = Q.sbase + (Q.ntiles - Q.sbase) * Q.S;

@@ -96,7 +96,9 @@ constexpr int kMetaQueue = 2;
 constexpr int kMetaClass0 = kMetaQueue + kXcds;
 constexpr int kMetaSplitBase = kMetaClass0 + 1;
 constexpr int kMetaSplitS = kMetaClass0 + 2;
-constexpr int kMetaOrder = kMetaClass0 + 3;  // 1: longest first, 0: class-1 tiles interleaved
+constexpr int kMetaOrder = kMetaClass0 + 3;  // tile order of an MFMA list (select_dev.h)
+enum TileOrder { kOrderMix = 0, kOrderChunks = 1, kOrderLongestFirst = 2 };
+constexpr int kLongK = 4096;  // K from which an MFMA list keeps XCD chunks of equal-length tiles
 static_assert(kMetaOrder < kMetaStride, "meta layout");
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,

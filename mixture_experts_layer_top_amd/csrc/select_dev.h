@@ -21,16 +21,22 @@ __device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
 
 // Per expert (one thread each, blockDim.x = kSelThreads >= E + 1) and per GEMM: family, tile
 // counts, and the segments' places in their (GEMM, family) list.  Each list has two classes of
-// segments, class 0 first, each class by expert id:
-//  * default: class 0 = experts with two or more m-tiles ("heavy"), class 1 = the rest ("light");
-//    the MFMA kernel spreads the light tiles evenly between the heavy ones, so HBM-bound and
-//    MFMA-bound tiles run side by side, and an expert's last m-tile stays next to its siblings
-//    (which share its weight tile in L2);
-//  * MFMA list of one to kSplitMaxRounds rounds of tiles ("longest first"): round
-//    quantization dominates, so an expert whose last m-tile would hold at most 128 rows gets that
-//    tail as a segment of its own, class 0 = segments of full-height tiles, class 1 = shorter ones,
-//    and the kernel hands them out in order (longest first, short tiles fill the last round, whose
-//    tiles may be split in K).
+// segments, class 0 first, each class by expert id, and the MFMA kernel hands its tiles out in one
+// of three orders (kMetaOrder):
+//  * kOrderMix (short K, several rounds): class 0 = experts with two or more m-tiles ("heavy"),
+//    class 1 = the rest; the light tiles are spread evenly between the heavy ones, and an expert's
+//    last m-tile stays next to its siblings, which share its weight tile in L2.  (Streaming lists
+//    use the same classes.)
+//  * kOrderChunks (K >= kLongK, several rounds): an expert whose last 256-row m-tile would hold at
+//    most 128 rows gets that tail as a segment of its own; class 0 = segments of full-height tiles,
+//    class 1 = shorter ones; whole XCD chunks of one class, the class-1 chunks spread evenly between
+//    the class-0 ones.  Short tiles still run beside MFMA-bound full ones across the chip, while the
+//    CUs of one XCD work on tiles of equal length and stay in step with the neighbours they share
+//    weight tiles with in L2 (with long K, a short tile inside a chunk drifts its neighbours apart:
+//    twice the gate/up L2 miss traffic was measured).
+//  * kOrderLongestFirst (one to kSplitMaxRounds rounds): classes as for kOrderChunks, tiles in
+//    order -- round quantization dominates, so the short ones fill the last round, whose tiles may
+//    be split in K.
 // The ranks and tile bases come from one block-wide scan of 16 per-expert counts.  Every thread of
 // the block must call this (it contains barriers).  Counts and offsets come from LDS when the
 // caller has them there (lds_counts, lds_offsets), else from a.counts / a.offsets.
@@ -84,7 +90,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   for (int j = 0; j < NS; ++j) {
     const int g = j >> 1, part = j & 1;
     const bool mf = fm[g] == kFamMfma;
-    const bool split = mf && lpt[g] && tail > 0;
+    const bool split = mf && tail > 0 && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
     fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
     r0[j] = part == 0 ? 0 : c - tail;
     nr[j] = part == 0 ? (split ? c - tail : c) : tail;
@@ -98,7 +104,8 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       nt[j] = (a.d + tn[j] - 1) / tn[j];  // a down tile of 256 columns may be half full at the edge
     }
     mt[j] = (nr[j] + tm - 1) / tm;
-    cls[j] = st || !lpt[g] ? (mt[j] >= 2 ? 0 : 1) : (nr[j] <= kMfmaBM / 2 ? 1 : 0);
+    const bool by_height = mf && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
+    cls[j] = by_height ? (nr[j] <= kMfmaBM / 2 ? 1 : 0) : (mt[j] >= 2 ? 0 : 1);
     // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -211,7 +218,9 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     const bool uniform_k = g == kGemmGateUp || !a.has_shared || a.f_sh == a.f;
     const int C = min(a.num_cus, kSplitMaxPieces);
     const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8;
-    m[kMetaOrder] = mfma_bf16 && lpt[g] ? 1 : 0;  // (lpt[] is the same for every thread)
+    // (lpt[] is the same for every thread)
+    m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : K >= kLongK ? kOrderChunks
+                                                                                      : kOrderMix;
     if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_cnt && uniform_k) {
       const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
       if (rem > 0) {
