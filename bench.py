@@ -98,7 +98,9 @@ def algorithmic(p, n_active: int):
 
 
 TRAFFIC_SOURCES = ("mixture_experts_layer_top_amd/csrc/gemm_bf16.hip",
-                   "mixture_experts_layer_top_amd/csrc/common.h")
+                   "mixture_experts_layer_top_amd/csrc/common.h",
+                   "mixture_experts_layer_top_amd/csrc/kernels.h",
+                   "mixture_experts_layer_top_amd/csrc/select_dev.h")
 
 
 def profiled_traffic(workload: str):

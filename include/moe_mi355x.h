@@ -64,7 +64,8 @@ enum moe_dtype {
 enum moe_config {
   MOE_CONFIG_AUTO = -1,
   MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
-  MOE_CONFIG_MFMA = 1    /* LDS-tiled MFMA tiles of 256 rows x 256 weight rows */
+  MOE_CONFIG_MFMA = 1    /* LDS-tiled MFMA tiles: 64, 128 or 256 rows (from the rows a tile
+                            holds) x 256 weight rows */
 };
 
 typedef struct moe_problem {
@@ -138,7 +139,8 @@ int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream
  * SwiGLU output is requantised to e4m3 per row and 128 channels before the down GEMM.  Tile
  * shapes are chosen on the device from counts (p->config may force one family).  The shared expert
  * fields of p and w are ignored here.
- *   ws: moe_grouped_ffn_workspace_bytes(p) bytes (rows = T*k of p). */
+ *   ws: moe_grouped_ffn_workspace_bytes(p) bytes (rows = T*k of p).  For bf16 weights it includes
+ *   64 MiB of partial-sum slots for the GEMMs' last-round split in K. */
 int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
                     const int32_t* counts, const int32_t* offsets, const moe_weights* w,
                     void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -154,7 +156,7 @@ int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w
  * grouped down (+ shared expert) -> combine.  The token gather is fused into the gate/up GEMM's
  * activation loads.
  *   logits [T][E] fp32, x [T][d] bf16, out [T][d] bf16.  keep: optional routing outputs.
- *   ws: moe_layer_workspace_bytes(p) bytes. */
+ *   ws: moe_layer_workspace_bytes(p) bytes (bf16 weights: including 64 MiB of split-K slots). */
 int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
               void* out, const moe_routing* keep, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_layer_workspace_bytes(const moe_problem* p);
