@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times (auto tile
 selection, one moe_layer call).  Routing ids, counts, offsets and both permutations are compared
-with the oracle in full, bit for bit; topk_w within 2e-6; the output is compared on sampled tokens,
-each computed by the oracle token by token (its per-token form needs only that token's experts),
-against max|ref| over the sampled rows.  Properties that hold at any size are checked on the whole
+with the oracle in full, bit for bit; topk_w within 2e-6; the output is compared on sampled tokens
+(random ones and the owners of the largest experts' last rows), each computed by the oracle token
+by token (its per-token form needs only that token's experts), against max|ref| over the sampled
+rows.  Properties that hold at any size are checked on the whole
 output: two calls give identical bits, counts sum to T*k, every row is finite."""
 import numpy as np
 import pytest
@@ -71,7 +72,12 @@ def _check_full(moe, inp, n_sample, tol, seed=0):
     assert np.array_equal(keep["slot_dst"].cpu().numpy(), slot_dst)
     got_all = bits_to_f64(out)
     assert np.isfinite(got_all).all()
-    tok = _sample_tokens(p.T, n_sample, seed)
+    # random tokens, plus the owners of the last row of the (up to) 8 largest experts: those rows
+    # sit in each expert's last m-tile, the one that becomes a short tail tile, a split piece or a
+    # last-round tile
+    big = np.argsort(-counts, kind="stable")[:8]
+    last_rows = [int(offsets[e + 1]) - 1 for e in big if counts[e] > 0]
+    tok = np.union1d(_sample_tokens(p.T, n_sample, seed), perm_src[last_rows] // p.k)
     cache = getattr(inp, "_host", None) or _HostCache(inp)
     inp._host = cache
     ref = O.moe_tokens(tok, inp.logits, inp.x, p.k, cache, inp.get_shared(),

@@ -225,6 +225,16 @@ def test_mfma_last_round_split(moe, f):
         _check_layer(moe, Inputs(p), config=config, runs=3)
 
 
+# Tile orders at a size the oracle still checks in full: the long-K gate/up GEMM (d = 4096, 848
+# tiles on 256 CUs) takes the chunked order, with two heavy experts whose short last m-tiles become
+# segments of their own, 46 light experts and full-height single tiles; the down GEMM (K = 2048)
+# takes the mixed order.  (Routing draw: Dirichlet(0.3) over 64 experts, seed 150.)
+def test_mfma_order_modes(moe):
+    p = I.Problem("order_modes", 150, T=1000, d=4096, f=2048, E=64, k=2, routing="dirichlet",
+                  alpha=0.3)
+    _check_layer(moe, Inputs(p), config=-1, runs=2)
+
+
 def test_generator_device_independent(moe):
     for p, which, e in ((I.TINY, "gate", 3), (I.DSV3, "down", 200), (I.FP8, "up", 7)):
         a = I.gen_expert_weight(p, which, e, "cpu")
