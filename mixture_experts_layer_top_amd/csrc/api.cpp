@@ -17,7 +17,6 @@ using namespace moe;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxExperts = 512;
-constexpr int kMaxTopK = 8;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -143,7 +142,9 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
                                            : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
     if (experts * nt < 2 * (int64_t)cus) mfma = false;
   }
-  return moe::launch_gemms_bf16(o, gemm, cus, stream, mfma, s);
+  const int max_k = gemm == kGemmGateUp ? p->d_model
+                                         : std::max(p->d_ff, p->has_shared ? p->d_ff_shared : 0);
+  return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k, stream, mfma, s);
 }
 }  // namespace
 
@@ -381,7 +382,33 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_cnt, L.ffn.split_part};
 
   hipError_t e = mark(0);
-  if (front_small_fits(T, k)) {
+  // a single bf16 token without a shared expert: routing runs inside the gate/up kernel, which
+  // also writes the routing outputs and the down GEMM's segments (phases 1 to 4 are empty)
+  const bool decode1 = T == 1 && !fp8 && !p->has_shared && p->config != MOE_CONFIG_MFMA &&
+                       d <= kStreamXlMaxK;
+  if (decode1) {
+    Decode1Args da;
+    da.logits = logits;
+    da.E = E;
+    da.k = k;
+    da.d = d;
+    da.f = p->d_ff;
+    da.x = x;
+    da.w_gate = w->w_gate;
+    da.w_up = w->w_up;
+    da.w_down = w->w_down;
+    da.h = L.ffn.h;
+    da.y = L.y;
+    da.ids = ids;
+    da.w = wts;
+    da.counts = counts;
+    da.offsets = offsets;
+    da.perm_src = perm_src;
+    da.slot_dst = slot_dst;
+    da.tok = L.tok;
+    for (int i = 1; i <= 4 && e == hipSuccess; ++i) e = mark(i);
+    if (e == hipSuccess) e = launch_decode1_bf16(da, o, device_cus(), stream);
+  } else if (front_small_fits(T, k)) {
     // decode-sized: route, permute and select in one launch (phases 1, 2 and 4 share it)
     if (e == hipSuccess)
       e = launch_front_small(logits, T, E, k, ids, wts, counts, offsets, perm_src, slot_dst,
@@ -404,7 +431,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
     if (e == hipSuccess) e = mark(4);
   }
   // each token routes to k distinct experts, so no expert (nor the shared one) holds more than T rows
-  if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, T, (int64_t)T * p->top_k, stream);
+  if (e == hipSuccess && !decode1)
+    e = launch_gemms(o, p, kGemmGateUp, T, (int64_t)T * p->top_k, stream);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, T, (int64_t)T * p->top_k, stream);
   if (e == hipSuccess) e = mark(6);

@@ -15,18 +15,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (c >= d) return;
+  // all k rows' indices and weights, then all k row loads, before any arithmetic (k <= 8)
+  int row[kMaxTopK];
+  float wj[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      row[j] = slot_dst[(size_t)t * k + j];
+      wj[j] = w[(size_t)t * k + j];
+    }
+  }
+  uint4 v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const uint4*>(y + (size_t)row[j] * d + c);
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int row = slot_dst[(size_t)t * k + j];
-    const float wj = w[(size_t)t * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)row * d + c);
-    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wj * bf16_to_f32(uint16_t(p[i] & 0xFFFF));
-      acc[2 * i + 1] += wj * bf16_to_f32(uint16_t(p[i] >> 16));
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      const uint32_t p[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wj[j] * bf16_to_f32(uint16_t(p[i] & 0xFFFF));
+        acc[2 * i + 1] += wj[j] * bf16_to_f32(uint16_t(p[i] >> 16));
+      }
     }
   }
   if (sh) {

@@ -18,14 +18,16 @@
 // kernel), heaviest experts first, m-tiles of one weight tile adjacent in the queue.
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
-__device__ __forceinline__ int find_seg(const Seg* __restrict__ segs, int nseg, int t) {
+// Index of the segment holding tile t: the last one whose first tile (base[], in LDS) is <= t.
+__device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (segs[mid].tile_base <= t) lo = mid;
+    if (base[mid] <= t) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -49,9 +51,12 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // enough workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its share
 // of the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
 // ------------------------------------------------------------------------------------------------
-template <int MQ, bool GU, int WK>
+// XL: the tile has one row; its activations (xrow, K bf16) are staged in LDS (xs) once the first
+// weight loads are in flight, and the MFMA loop reads the B operand from there.
+template <int MQ, bool GU, int WK, bool XL = false>
 __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0,
-                                                 float* red) {
+                                                 float* red, const char* xs = nullptr,
+                                                 const void* xrow = nullptr) {
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K, N = sg.N;
@@ -71,8 +76,8 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
     int r = q * 16 + r16;
     r = r < rows ? r : rows - 1;  // padded columns re-read a valid row; never stored
     const int gr = sg.row0 + m0 + r;
-    const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-    xoff[q] = (uint32_t)src * K * 2 + kbase;
+    const int src = XL ? 0 : sg.tok ? gload_i32(sg.tok, gr) : gr;
+    xoff[q] = (uint32_t)src * K * 2 + kbase;  // (XL: byte offset in the staged row)
   }
   f32x4 acc0[MQ], acc1[MQ];
 #pragma unroll
@@ -88,28 +93,43 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       const uint32_t ko = (uint32_t)(ks + u) * 64;
       bt.a0[u] = gload16(wg, woff + ko);
       if (GU) bt.a1[u] = gload16(wu, woff + ko);
+      if (!XL) {
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(xa, xoff[q] + ko);
+        for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(xa, xoff[q] + ko);
+      }
     }
   };
-  auto compute = [&](const Batch& bt) {
+  auto xfrag = [&](const Batch& bt, int u, int q, int ks) {
+    return XL ? *reinterpret_cast<const uint4*>(xs + xoff[q] + (uint32_t)(ks + u) * 64)
+              : bt.b[u][q];
+  };
+  auto compute = [&](const Batch& bt, int ks) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        acc0[q] = mfma16(as_bf16x8(bt.a0[u]), as_bf16x8(bt.b[u][q]), acc0[q]);
-        if (GU) acc1[q] = mfma16(as_bf16x8(bt.a1[u]), as_bf16x8(bt.b[u][q]), acc1[q]);
+        const uint4 b = xfrag(bt, u, q, ks);
+        acc0[q] = mfma16(as_bf16x8(bt.a0[u]), as_bf16x8(b), acc0[q]);
+        if (GU) acc1[q] = mfma16(as_bf16x8(bt.a1[u]), as_bf16x8(b), acc1[q]);
       }
   };
   const int nsteps = kq / 32;             // K-steps of this wavefront (>= 1)
   const int nfull = nsteps / U * U;        // pipelined part: whole batches only
   Batch b0, b1;
   if (nfull > 0) load(b0, 0);
+  if (XL) {
+    // stage the row's activations (the first weight loads are already in flight); the previous
+    // tile's readers of xs all passed the barrier before its split-K reduction
+    const uint4* xg = static_cast<const uint4*>(xrow);
+    uint4* xw = reinterpret_cast<uint4*>(const_cast<char*>(xs));
+    for (int i = threadIdx.x; i < K / 8; i += 256) xw[i] = xg[i];
+    __syncthreads();
+  }
   for (int ks = 0; ks < nfull; ks += 2 * U) {
     if (ks + U < nfull) load(b1, ks + U);
-    compute(b0);
+    compute(b0, ks);
     if (ks + 2 * U < nfull) load(b0, ks + 2 * U);
-    if (ks + U < nfull) compute(b1);
+    if (ks + U < nfull) compute(b1, ks + U);
   }
   for (int ks = nfull; ks < nsteps; ++ks) {  // remainder, one K-step at a time
     const uint32_t ko = (uint32_t)ks * 64;
@@ -117,7 +137,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
     const uint4 a1 = GU ? gload16(wu, woff + ko) : a0;
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
-      const uint4 b = gload16(xa, xoff[q] + ko);
+      const uint4 b = XL ? *reinterpret_cast<const uint4*>(xs + xoff[q] + ko) : gload16(xa, xoff[q] + ko);
       acc0[q] = mfma16(as_bf16x8(a0), as_bf16x8(b), acc0[q]);
       if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
@@ -167,32 +187,62 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
   }
 }
 
-template <bool GU>
+// Rows [m0, m0 + rows) of one tile, in passes of at most 16 * MQMAX rows.  The kernel's register
+// budget is that of its widest pass, so the host instantiates MQMAX from a bound on any expert's
+// rows (every expert holds at most T rows): at MQMAX = 1 four workgroups fit on each CU.
+// MQMAX = 0 (the host launches it when every expert holds at most one row, as at T = 1, and K <=
+// kStreamXlMaxK): rows one at a time, each staging its activations in LDS (xs) for the MFMA loop.
+template <bool GU, int WK, int MQMAX>
+__device__ __forceinline__ void stream_rows_bf16(const Seg& sg, int m0, int rows, int n0,
+                                                 float* red, const char* xs) {
+  if (MQMAX == 0) {
+    if (sg.K > kStreamXlMaxK) return;  // (excluded by the host)
+    for (int r = 0; r < rows; ++r) {
+      const int gr = sg.row0 + m0 + r;
+      const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
+      const void* xrow = static_cast<const char*>(sg.a) + (size_t)src * sg.K * 2;
+      stream_tile_bf16<1, GU, WK, true>(sg, m0 + r, 1, n0, red, xs, xrow);
+    }
+    return;
+  }
+  constexpr int MQ = MQMAX > 0 ? MQMAX : 1;
+  for (int sub = 0; sub < rows; sub += 16 * MQ) {
+    const int r = min(16 * MQ, rows - sub);
+    if (MQ == 1 || r <= 16) stream_tile_bf16<1, GU, WK>(sg, m0 + sub, r, n0, red);
+    else if (MQ == 2 || r <= 32) stream_tile_bf16<MQ >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red);
+    else stream_tile_bf16<MQ, GU, WK>(sg, m0 + sub, r, n0, red);
+  }
+}
+
+// Persistent: workgroup b takes tile b first, then pops tiles gridDim.x, gridDim.x + 1, ... from
+// the list's queue counter (zeroed by the selection kernel), so a launch whose tiles all fit in
+// one round makes no atomic at all.  The segments' first tiles are staged in LDS once.
+template <bool GU, int MQMAX>
 __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ segs,
                                                          int32_t* __restrict__ meta) {
+  constexpr int MQ = MQMAX > 0 ? MQMAX : 1;
   __shared__ int slot;
-  // split-K partials of wavefronts 1..3: up to 4 token groups x 4 x 2 floats per lane
-  __shared__ float red[3 * 4 * 4 * 2 * 64];
+  __shared__ int seg_base[kSegCap];
+  // split-K partials of wavefronts 1..3: up to MQ token groups x 4 x 2 floats per lane
+  __shared__ float red[3 * MQ * 4 * 2 * 64];
+  // MQMAX = 0: the activations of a one-row tile
+  __shared__ __attribute__((aligned(16))) char xs[MQMAX == 0 ? kStreamXlMaxK * 2 : 16];
   const int nseg = meta[0], ntiles = meta[1];
-  if (ntiles == 0) return;
+  if ((int)blockIdx.x >= ntiles) return;
+  for (int i = threadIdx.x; i < nseg; i += 256) seg_base[i] = segs[i].tile_base;
+  __syncthreads();
+  int t = blockIdx.x;
   for (;;) {
-    const int t = __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
-    if (t >= ntiles) break;
-    const Seg& sg = segs[__builtin_amdgcn_readfirstlane(find_seg(segs, nseg, t))];
+    const Seg& sg = segs[__builtin_amdgcn_readfirstlane(find_seg_lds(seg_base, nseg, t))];
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     const int m0 = mt * kStreamMaxRows;
     const int rows = min(kStreamMaxRows, sg.rows - m0);
     const int n0 = nt * sg.tn;
-    if (sg.tn == 16) {  // long K: split across the 4 wavefronts
-      if (rows <= 16) stream_tile_bf16<1, GU, 4>(sg, m0, rows, n0, red);
-      else if (rows <= 32) stream_tile_bf16<2, GU, 4>(sg, m0, rows, n0, red);
-      else stream_tile_bf16<4, GU, 4>(sg, m0, rows, n0, red);
-    } else {  // 32 columns: split across pairs of wavefronts
-      if (rows <= 16) stream_tile_bf16<1, GU, 2>(sg, m0, rows, n0, red);
-      else if (rows <= 32) stream_tile_bf16<2, GU, 2>(sg, m0, rows, n0, red);
-      else stream_tile_bf16<4, GU, 2>(sg, m0, rows, n0, red);
-    }
+    if (sg.tn == 16) stream_rows_bf16<GU, 4, MQMAX>(sg, m0, rows, n0, red, xs);  // long K: 4-way split
+    else stream_rows_bf16<GU, 2, MQMAX>(sg, m0, rows, n0, red, xs);  // 32 columns: wavefront pairs
+    t = gridDim.x + __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
+    if (t >= ntiles) break;
   }
 }
 
@@ -710,17 +760,6 @@ __device__ __forceinline__ int interleave_tile(int p, int heavy, int ntiles) {
   return h1 > h0 ? h0 : heavy + (p - h0);
 }
 
-// Segment holding tile t, by binary search over the segments' first tiles cached in LDS.
-__device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (base[mid] <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 // A piece of a split tile (accumulator blocks a < NA, b < NB): writes its partial sums to its slot
 // of the tile's S slots, then counts itself done; the piece that finds the other S - 1 done adds
 // the S slots in piece order into acc (its own from registers, bit-identical to its slot) and
@@ -894,18 +933,150 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   else mfma_persistent<GU, false>(Q, split_cnt, split_part, &slot);
 }
 
-hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, bool stream, bool mfma,
-                             hipStream_t s) {
+// ------------------------------------------------------------------------------------------------
+// single-token decode: routing fused into the gate/up kernel
+//
+// With one token, each expert's segment is one row and the rows follow the selected experts in
+// increasing id (the stable permutation of the token's k slots), so a workgroup that has routed
+// the token itself knows every tile's expert and row: tile t = (row t / P, columns (t % P) * tn),
+// P = f / tn.  Routing is a single wavefront's work (route_dev.h) and costs each workgroup less
+// than a separate front-end launch and its selection pass would cost the whole layer.
+// ------------------------------------------------------------------------------------------------
+template <int VPL, int WK>
+__global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, SelectOut o) {
+  constexpr int tn = WK == 4 ? 16 : 32;
+  __shared__ int s_ids[kMaxTopK];   // the routing, in slot order
+  __shared__ int s_exp[kMaxTopK];   // the selected experts in increasing id (row order)
+  __shared__ float red[3 * 4 * 2 * 64];
+  __shared__ __attribute__((aligned(16))) char xs[kStreamXlMaxK * 2];
+  const int tid = threadIdx.x, k = a.k;
+  const int per_exp = a.f / tn, ntiles = k * per_exp;
+  const bool lead = blockIdx.x == 0;
+  if ((int)blockIdx.x >= ntiles) return;
+  if (tid < 64) route_token<VPL>(a.logits, 0, a.E, k, lead ? a.ids : nullptr, lead ? a.w : nullptr,
+                                 s_ids);
+  __syncthreads();
+  if (tid < k) {  // the k ids are distinct: row = number of selected ids below this one
+    const int e = s_ids[tid];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += s_ids[j] < e ? 1 : 0;
+    s_exp[r] = e;
+    if (lead) {
+      a.perm_src[r] = tid;
+      a.slot_dst[tid] = r;
+      a.tok[r] = 0;
+    }
+  }
+  if (lead) {
+    for (int e = tid; e <= a.E; e += 256) {
+      int below = 0, hit = 0;
+      for (int j = 0; j < k; ++j) {
+        below += s_ids[j] < e ? 1 : 0;
+        hit |= s_ids[j] == e ? 1 : 0;
+      }
+      if (e < a.E) a.counts[e] = hit;
+      a.offsets[e] = below;
+    }
+  }
+  __syncthreads();
+  if (lead && tid < k) {
+    // the down GEMM's streaming list, as the selection writes it: one segment per row, by id
+    const int r = tid, e = s_exp[r];
+    const int dtn = stream_bn(a.f), dt = (a.d + dtn - 1) / dtn;
+    Seg sg;
+    sg.a = a.h;
+    sg.tok = nullptr;
+    sg.as = nullptr;
+    sg.w0 = static_cast<const uint8_t*>(a.w_down) + (size_t)e * a.d * a.f * 2;
+    sg.w1 = nullptr;
+    sg.s0 = nullptr;
+    sg.s1 = nullptr;
+    sg.out = a.y;
+    sg.outs = nullptr;
+    sg.row0 = r;
+    sg.rows = 1;
+    sg.N = a.d;
+    sg.K = a.f;
+    sg.tile_base = r * dt;
+    sg.mtiles = 1;
+    sg.ntiles = dt;
+    sg.expert = e;
+    sg.tn = dtn;
+    o.segs[(size_t)(kGemmDown * kNumFam + kFamStream) * kSegCap + r] = sg;
+    if (r == 0) {  // stream list: k segments, k * dt tiles, zeroed queue; MFMA list: empty
+      for (int fam = 0; fam < kNumFam; ++fam) {
+        int32_t* m = o.meta + (kGemmDown * kNumFam + fam) * kMetaStride;
+        const bool st = fam == kFamStream;
+        for (int q = 0; q < kMetaStride; ++q) m[q] = 0;
+        m[0] = st ? k : 0;
+        m[1] = st ? k * dt : 0;
+        m[kMetaSplitS] = 1;
+      }
+    }
+  }
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int r = t / per_exp, e = s_exp[r];
+    Seg sg;
+    sg.a = a.x;
+    sg.tok = nullptr;
+    sg.as = nullptr;
+    sg.w0 = static_cast<const uint8_t*>(a.w_gate) + (size_t)e * a.f * a.d * 2;
+    sg.w1 = static_cast<const uint8_t*>(a.w_up) + (size_t)e * a.f * a.d * 2;
+    sg.s0 = nullptr;
+    sg.s1 = nullptr;
+    sg.out = a.h;
+    sg.outs = nullptr;
+    sg.row0 = r;
+    sg.rows = 1;
+    sg.N = a.f;
+    sg.K = a.d;
+    sg.tile_base = r * per_exp;
+    sg.mtiles = 1;
+    sg.ntiles = per_exp;
+    sg.expert = e;
+    sg.tn = tn;
+    stream_tile_bf16<1, true, WK, true>(sg, 0, 1, (t - r * per_exp) * tn, red, xs, a.x);
+  }
+}
+
+template <int VPL>
+static void launch_decode1_vpl(const Decode1Args& a, const SelectOut& o, int g, hipStream_t s) {
+  if (stream_bn(a.d) == 16) decode1_gate_up_bf16<VPL, 4><<<g, 256, 0, s>>>(a, o);
+  else decode1_gate_up_bf16<VPL, 2><<<g, 256, 0, s>>>(a, o);
+}
+
+hipError_t launch_decode1_bf16(const Decode1Args& a, const SelectOut& o, int num_cus,
+                               hipStream_t s) {
+  const int g = num_cus * 4;
+  if (a.E <= 64) launch_decode1_vpl<1>(a, o, g, s);
+  else if (a.E <= 128) launch_decode1_vpl<2>(a, o, g, s);
+  else if (a.E <= 256) launch_decode1_vpl<4>(a, o, g, s);
+  else launch_decode1_vpl<8>(a, o, g, s);
+  return hipGetLastError();
+}
+
+template <bool GU>
+static void launch_stream_bf16(const Seg* ss, int32_t* ms, int num_cus, int64_t max_rows,
+                               int max_k, hipStream_t s) {
+  if (GU && max_rows <= 1 && max_k <= kStreamXlMaxK)  // (down tiles are too short to gain)
+    gemm_stream_bf16<GU, 0><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+  else if (max_rows <= 16) gemm_stream_bf16<GU, 1><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+  else if (max_rows <= 32) gemm_stream_bf16<GU, 2><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+  else gemm_stream_bf16<GU, 4><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+}
+
+hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, int64_t max_rows, int max_k,
+                             bool stream, bool mfma, hipStream_t s) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
   int32_t* cnt = o.split_cnt ? o.split_cnt + g * kSplitMaxPieces : nullptr;
   if (g == kGemmGateUp) {
-    if (stream) gemm_stream_bf16<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    if (stream) launch_stream_bf16<true>(ss, ms, num_cus, max_rows, max_k, s);
     if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   } else {
-    if (stream) gemm_stream_bf16<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    if (stream) launch_stream_bf16<false>(ss, ms, num_cus, max_rows, max_k, s);
     if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   }
   return hipGetLastError();

@@ -10,6 +10,8 @@ namespace moe {
 enum Family { kFamStream = 0, kFamMfma = 1, kNumFam = 2 };
 enum Gemm { kGemmGateUp = 0, kGemmDown = 1 };
 
+constexpr int kMaxTopK = 8;  // experts per token (the boundary rejects more)
+
 constexpr int kStreamMaxRows = 64;  // rows per weight-streaming pass
 // Automatic selection: an expert takes the weight-streaming family for a GEMM while its row
 // count is at most this, the LDS-tiled MFMA family above it (whose short tiles stream the
@@ -25,6 +27,8 @@ constexpr int kXcds = 8;            // MI355X: 8 XCDs, each with its own L2
 // wavefront per 16 columns over the whole K, or a four-way split of a short K, streams slower.
 constexpr int kStreamSplitK = 4096;
 __host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ? 16 : 32; }
+// Longest K whose one-row activations a streaming tile stages in LDS (16 KB).
+constexpr int kStreamXlMaxK = 8192;
 constexpr int kSegCap = 1040;       // segment slots per (gemm, family); >= 2 * (E + 1)
 // fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
 // the weights from L2; 32 keeps the kernels' registers low enough for 3 or more wavefronts per
@@ -116,11 +120,32 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
                               int32_t* slot_dst, int32_t* tok, const SelectArgs& sa,
                               const SelectOut& so, hipStream_t s);
-// Launches both tile families of one GEMM (kGemmGateUp or kGemmDown).
-// Launches the persistent kernel of each family that may hold tiles (the other's queue is empty).
-hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, bool stream, bool mfma,
-                             hipStream_t s);
+// Launches the persistent kernel of each tile family of one GEMM (kGemmGateUp or kGemmDown) that
+// may hold tiles (the other's queue is empty).  max_rows bounds the rows of any one expert, max_k
+// the GEMM's K over all its segments.
+hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
+                             int max_k, bool stream, bool mfma, hipStream_t s);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
+
+// Single-token decode (T = 1, bf16 weights, no shared expert, d <= kStreamXlMaxK): one kernel routes
+// the token in every workgroup (the k selected experts are then known without a dispatch step),
+// runs the gate/up GEMM on streaming tiles, and from workgroup 0 writes the routing, the
+// histogram, the permutation and the down GEMM's streaming segments, which the down kernel then
+// takes as the selection kernel would have written them.
+struct Decode1Args {
+  const float* logits;  // [E]
+  int E, k, d, f;
+  const void* x;        // [d] bf16
+  const void* w_gate; const void* w_up; const void* w_down;
+  void* h;              // [k][f] bf16
+  void* y;              // [k][d] bf16
+  int32_t* ids; float* w;                 // [k]
+  int32_t* counts; int32_t* offsets;      // [E], [E + 1]
+  int32_t* perm_src; int32_t* slot_dst;   // [k]
+  int32_t* tok;                           // [k]
+};
+hipError_t launch_decode1_bf16(const Decode1Args& a, const SelectOut& o, int num_cus,
+                               hipStream_t s);
 hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
                           int d, const void* shared_y, void* out, hipStream_t s);
 hipError_t launch_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t s);

@@ -172,8 +172,8 @@ __global__ __launch_bounds__(1024) void front_small_kernel(const float* __restri
   }
   __syncthreads();
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int myrank[2], myexp[2];
-  for (int r = 0; r < 2; ++r) {
+  int myrank[2] = {0, 0}, myexp[2] = {0, 0};
+  for (int r = 0; r * 1024 < n; ++r) {  // (n <= 2048; the bound is the same for every thread)
     const int s = r * 1024 + tid;
     const bool valid = s < n;
     const int e = valid ? s_ids[s] : 0;

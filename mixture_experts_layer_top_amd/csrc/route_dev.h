@@ -1,59 +1,73 @@
 // Top-k routing of one token by one wavefront (shared by the routing kernel and the fused decode
-// front end).  Lane l holds logits l, l+64, ...; each of the k rounds takes every lane's best
-// untaken candidate and reduces over the wavefront with a butterfly on the total order
-// (value desc, id asc); IEEE comparisons make -0.0 and +0.0 a tie.  Weights: expf of the gap to
-// the largest selected logit, divided by their sum (softmax renormalised over the selected k).
+// front end).  Lane l holds logits l, l+64, ...; each of the k rounds selects the best untaken
+// candidate in the total order (value desc, id asc; -0.0 and +0.0 tie).  Weights: expf of the gap
+// to the largest selected logit, divided by their sum (softmax renormalised over the selected k).
 #pragma once
 
 #include "common.h"
 
 namespace moe {
 
-__device__ __forceinline__ bool route_better(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
+// Candidate keys: the logit's bits mapped so that unsigned order is IEEE order (+0.0 and -0.0 are
+// first made the same value, so they tie).  Every finite logit maps above 0, and key 0 marks "no
+// candidate" (past E, or already selected).
+__device__ __forceinline__ uint32_t route_ordered(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0.0 + 0.0 = +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float route_unordered(uint32_t h) {
+  return __uint_as_float((h & 0x80000000u) ? (h & 0x7fffffffu) : ~h);
 }
 
-// Routes token t; lane 0 writes ids/w (and the ids to lds_ids[t*k + j] if lds_ids is not null).
+// Largest key of the wavefront: DPP max inside rows of 16 lanes (swap neighbours, swap pairs,
+// mirror halves, mirror rows: every lane then holds its row's largest), then across the four rows
+// through scalar registers.
+__device__ __forceinline__ uint32_t route_wave_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xf, 0xf, false));  // row_mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Routes token t; lane 0 writes ids/w when they are not null, and the ids to lds_ids[t*k + j] when
+// lds_ids is not null.  Each of the k rounds takes the largest remaining key of the wavefront, and
+// among the candidates holding it (equal logits) the lowest expert id: lane l holds experts l,
+// l + 64, ..., so that is the lowest set lane of the first of its VPL ballots that has one.
 template <int VPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
                                             int* lds_ids) {
   const int lane = threadIdx.x & 63;
   const float* row = logits + (size_t)t * E;
-  float v[VPL];
+  uint32_t kh[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
+    kh[i] = e < E ? route_ordered(row[e]) : 0u;
   }
-  uint32_t taken = 0;
   float sel_v[8];
   int sel_i[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < k) {
-      float best = 0.0f;
-      int bi = 0x7fffffff;
+      uint32_t m = kh[0];
+#pragma unroll
+      for (int i = 1; i < VPL; ++i) m = max(m, kh[i]);
+      const uint32_t best = route_wave_max(m);
+      int bi = -1;
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
-        const int e = lane + 64 * i;
-        const bool cand = e < E && !((taken >> i) & 1u);
-        if (cand && (bi == 0x7fffffff || route_better(v[i], e, best, bi))) {
-          best = v[i];
-          bi = e;
-        }
+        const uint64_t hit = __ballot(kh[i] == best);
+        if (bi < 0 && hit != 0) bi = 64 * i + (__ffsll((unsigned long long)hit) - 1);
       }
+      // the selected candidate drops out of later rounds
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || route_better(ob, oi, best, bi))) {
-          best = ob;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      sel_v[j] = best;
+      for (int i = 0; i < VPL; ++i)
+        if (lane + 64 * i == bi) kh[i] = 0u;
+      sel_v[j] = route_unordered(best);
       sel_i[j] = bi;
     }
   }
@@ -70,8 +84,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k) {
-        ids[(size_t)t * k + j] = sel_i[j];
-        w[(size_t)t * k + j] = ex[j] / sum;
+        if (ids) ids[(size_t)t * k + j] = sel_i[j];
+        if (w) w[(size_t)t * k + j] = ex[j] / sum;
         if (lds_ids) lds_ids[t * k + j] = sel_i[j];
       }
     }

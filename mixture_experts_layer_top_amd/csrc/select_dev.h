@@ -87,32 +87,38 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = 0;
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int g = j >> 1, part = j & 1;
-    const bool mf = fm[g] == kFamMfma;
-    const bool split = mf && tail > 0 && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
-    fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
-    r0[j] = part == 0 ? 0 : c - tail;
-    nr[j] = part == 0 ? (split ? c - tail : c) : tail;
-    const bool st = fam[j] == kFamStream;
-    const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
-    if (g == kGemmGateUp) {
-      tn[j] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
-      nt[j] = ffe / tn[j];  // f is a multiple of 128
-    } else {
-      tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
-      nt[j] = (a.d + tn[j] - 1) / tn[j];  // a down tile of 256 columns may be half full at the edge
-    }
-    mt[j] = (nr[j] + tm - 1) / tm;
-    const bool by_height = mf && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
-    cls[j] = by_height ? (nr[j] <= kMfmaBM / 2 ? 1 : 0) : (mt[j] >= 2 ? 0 : 1);
-    // (all indexing below is static after unrolling, so nothing lands in scratch memory)
+  for (int j = 0; j < NS; ++j) fam[j] = -1;
+  // (threads past the experts skip the per-segment work; whole wavefronts of them branch over it)
+  if (e < nexp) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (fam[j] >= 0 && i == (g * 2 + fam[j]) * 2 + cls[j]) {
-        v[i] += 1;
-        v[8 + i] += mt[j] * nt[j];
+    for (int j = 0; j < NS; ++j) {
+      const int g = j >> 1, part = j & 1;
+      const bool mf = fm[g] == kFamMfma;
+      const bool split = mf && tail > 0 && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
+      fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
+      r0[j] = part == 0 ? 0 : c - tail;
+      nr[j] = part == 0 ? (split ? c - tail : c) : tail;
+      const bool st = fam[j] == kFamStream;
+      const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
+      if (g == kGemmGateUp) {
+        tn[j] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
+        nt[j] = ffe / tn[j];  // f is a multiple of 128
+      } else {
+        tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
+        // (a down tile of 256 columns may be half full at the edge)
+        nt[j] = (a.d + tn[j] - 1) / tn[j];
       }
+      mt[j] = (nr[j] + tm - 1) / tm;
+      const bool by_height = mf && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
+      cls[j] = by_height ? (nr[j] <= kMfmaBM / 2 ? 1 : 0) : (mt[j] >= 2 ? 0 : 1);
+      // (all indexing below is static after unrolling, so nothing lands in scratch memory)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (fam[j] >= 0 && i == (g * 2 + fam[j]) * 2 + cls[j]) {
+          v[i] += 1;
+          v[8 + i] += mt[j] * nt[j];
+        }
+    }
   }
   block_scan<16, 16>(v, ex, tot, scan_lds);
   // (an expert's two segments of one GEMM have different classes, so each list index i takes at
@@ -136,7 +142,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   const int row0 = (e < nexp && !shared) ? (lds_offsets ? lds_offsets[e] : gload_i32(a.offsets, e)) : 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    if (fam[j] < 0) continue;
+    if (fam[j] < 0) continue;  // (also every thread past the experts)
     const int g = j >> 1;
     Seg sg;
     sg.row0 = row0 + r0[j];

@@ -190,6 +190,43 @@ def test_layer_matches_oracle(moe, p, config):
     _check_layer(moe, Inputs(p), config=config, runs=2)
 
 
+# One token (bf16, no shared expert, d <= 8192): every workgroup of the gate/up kernel routes the
+# token itself and takes its tiles' experts from that; its first workgroup also writes the routing
+# outputs and the down GEMM's segments.  Cases: each width of the routing's per-lane candidates
+# (E <= 64, 128, 256, 512), both streaming tile widths (d below 4096: 32 columns, else 16), more
+# tiles than workgroups (f = 4096, k = 8: 2048 tiles of 16 columns), and d above the staging limit
+# (the general path).  The down GEMM runs on the segments the gate/up kernel wrote.
+DECODE1 = [
+    _small("decode1_E64_k1", T=1, d=256, f=256, E=64, k=1, cfg_index=160),
+    _small("decode1_E128", T=1, d=1024, f=512, E=128, k=6, routing="dirichlet", alpha=0.3,
+           cfg_index=161),
+    _small("decode1_E256", T=1, d=4096, f=384, E=256, k=8, routing="dirichlet", alpha=1.0,
+           cfg_index=162),
+    _small("decode1_E512", T=1, d=512, f=384, E=512, k=8, cfg_index=163),
+    _small("decode1_many_tiles", T=1, d=4096, f=4096, E=8, k=8, cfg_index=164),
+    _small("decode1_wide_d", T=1, d=8320, f=256, E=8, k=2, cfg_index=165),
+]
+
+
+@pytest.mark.parametrize("config", [-1, 0])
+@pytest.mark.parametrize("p", DECODE1, ids=lambda p: p.name)
+def test_decode1_matches_oracle(moe, p, config):
+    _check_layer(moe, Inputs(p), config=config, runs=2)
+
+
+# Ties inside the single-token routing: equal logits (and +0.0 / -0.0) go to the lower expert id.
+@pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (512, 3)])
+def test_decode1_ties(moe, E, k):
+    inp = Inputs(_small(f"decode1_ties_E{E}", T=1, d=256, f=256, E=E, k=k, cfg_index=166))
+    rng = np.random.default_rng(E + k)
+    L = rng.integers(-1, 2, size=(1, E)).astype(np.float32)
+    L[0, ::5] = -0.0
+    L[0, 1::5] = 0.0
+    inp.logits = L
+    inp.d_logits = torch.from_numpy(L).cuda()
+    _check_layer(moe, inp, config=-1)
+
+
 # MFMA tiles take a height of 64, 128 or 256 token rows from the rows they hold; one expert whose
 # row count sits at each boundary, with K of 2 K-steps (the three-stage ring of the short tiles
 # then reloads its last step) and of 6.
