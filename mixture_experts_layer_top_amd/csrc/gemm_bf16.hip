@@ -51,9 +51,10 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // enough workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its share
 // of the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
 // ------------------------------------------------------------------------------------------------
-// XL: the tile has one row; its activations (xrow, K bf16) are staged in LDS (xs) once the first
-// weight loads are in flight, and the MFMA loop reads the B operand from there.
-template <int MQ, bool GU, int WK, bool XL = false>
+// XL > 0: the tile has one row, whose activations (K bf16) the MFMA loop reads from LDS (xs): with
+// XL = 1 the tile stages them from xrow once its first weight loads are in flight, with XL = 2 the
+// caller has staged them.
+template <int MQ, bool GU, int WK, int XL = 0>
 __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0,
                                                  float* red, const char* xs = nullptr,
                                                  const void* xrow = nullptr) {
@@ -117,7 +118,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
   const int nfull = nsteps / U * U;        // pipelined part: whole batches only
   Batch b0, b1;
   if (nfull > 0) load(b0, 0);
-  if (XL) {
+  if (XL == 1) {
     // stage the row's activations (the first weight loads are already in flight); the previous
     // tile's readers of xs all passed the barrier before its split-K reduction
     const uint4* xg = static_cast<const uint4*>(xrow);
@@ -201,7 +202,7 @@ __device__ __forceinline__ void stream_rows_bf16(const Seg& sg, int m0, int rows
       const int gr = sg.row0 + m0 + r;
       const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
       const void* xrow = static_cast<const char*>(sg.a) + (size_t)src * sg.K * 2;
-      stream_tile_bf16<1, GU, WK, true>(sg, m0 + r, 1, n0, red, xs, xrow);
+      stream_tile_bf16<1, GU, WK, 1>(sg, m0 + r, 1, n0, red, xs, xrow);
     }
     return;
   }
@@ -953,8 +954,13 @@ __global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, Selec
   const int per_exp = a.f / tn, ntiles = k * per_exp;
   const bool lead = blockIdx.x == 0;
   if ((int)blockIdx.x >= ntiles) return;
-  if (tid < 64) route_token<VPL>(a.logits, 0, a.E, k, lead ? a.ids : nullptr, lead ? a.w : nullptr,
-                                 s_ids);
+  if (tid < 64) {
+    route_token<VPL>(a.logits, 0, a.E, k, lead ? a.ids : nullptr, lead ? a.w : nullptr, s_ids);
+  } else {  // meanwhile the other wavefronts stage the token's activations for every tile
+    const uint4* xg = static_cast<const uint4*>(a.x);
+    uint4* xw = reinterpret_cast<uint4*>(xs);
+    for (int i = tid - 64; i < a.d / 8; i += 192) xw[i] = xg[i];
+  }
   __syncthreads();
   if (tid < k) {  // the k ids are distinct: row = number of selected ids below this one
     const int e = s_ids[tid];
@@ -1035,7 +1041,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, Selec
     sg.ntiles = per_exp;
     sg.expert = e;
     sg.tn = tn;
-    stream_tile_bf16<1, true, WK, true>(sg, 0, 1, (t - r * per_exp) * tn, red, xs, a.x);
+    stream_tile_bf16<1, true, WK, 2>(sg, 0, 1, (t - r * per_exp) * tn, red, xs);
   }
 }
 
