@@ -22,17 +22,6 @@
 
 namespace moe {
 
-// Index of the segment holding tile t: the last one whose first tile (base[], in LDS) is <= t.
-__device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (base[mid] <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Pops the next tile index for the whole workgroup.
 __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
   if (threadIdx.x == 0) *slot = atomicAdd(queue, 1);

@@ -32,15 +32,6 @@ __device__ __forceinline__ i32x8 as_i32x8(const uint4& lo, const uint4& hi) {
   return r;
 }
 
-__device__ __forceinline__ int find_seg8(const Seg* __restrict__ segs, int nseg, int t) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (segs[mid].tile_base <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
 
 // Runs compute over the nkb K blocks.  Pipelined: the loads of block kb + 1 are issued before block
 // kb is computed (two register buffers, unrolled by two so no buffer is copied); otherwise each
@@ -228,20 +219,21 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
   }
 }
 
+// Persistent, as the bf16 streaming kernel: workgroup b takes tile b first, then pops tiles
+// gridDim.x, gridDim.x + 1, ... from the list's queue counter; segment bases are staged in LDS.
 template <bool GU>
 __global__ __launch_bounds__(256) void gemm_stream_fp8(const Seg* __restrict__ segs,
                                                         int32_t* __restrict__ meta) {
   __shared__ int slot;
+  __shared__ int seg_base[kSegCap];
   __shared__ float red[4][kFp8Rows];
   const int nseg = meta[0], ntiles = meta[1];
-  if (ntiles == 0) return;
+  if ((int)blockIdx.x >= ntiles) return;
+  for (int i = threadIdx.x; i < nseg; i += 256) seg_base[i] = segs[i].tile_base;
+  __syncthreads();
+  int t = blockIdx.x;
   for (;;) {
-    if (threadIdx.x == 0) slot = atomicAdd(&meta[kMetaQueue], 1);
-    __syncthreads();
-    const int t = __builtin_amdgcn_readfirstlane(slot);
-    __syncthreads();
-    if (t >= ntiles) break;
-    const Seg& sg = segs[__builtin_amdgcn_readfirstlane(find_seg8(segs, nseg, t))];
+    const Seg& sg = segs[__builtin_amdgcn_readfirstlane(find_seg_lds(seg_base, nseg, t))];
     const int local = t - sg.tile_base;
     const int mt = local % sg.mtiles, nt = local / sg.mtiles;
     const int m0 = mt * kFp8Rows;
@@ -256,6 +248,11 @@ __global__ __launch_bounds__(256) void gemm_stream_fp8(const Seg* __restrict__ s
       if (rows <= 16) fp8_down_tile<1>(sg, m0, rows, n0);
       else fp8_down_tile<2>(sg, m0, rows, n0);
     }
+    if (threadIdx.x == 0) slot = atomicAdd(&meta[kMetaQueue], 1);
+    __syncthreads();
+    t = gridDim.x + __builtin_amdgcn_readfirstlane(slot);
+    __syncthreads();
+    if (t >= ntiles) break;
   }
 }
 

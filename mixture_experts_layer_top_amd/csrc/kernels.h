@@ -55,6 +55,17 @@ struct Seg {
   int32_t tn;           // output columns per tile
 };
 
+// Index of the segment holding tile t: the last one whose first tile (base[], in LDS) is <= t.
+__device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Last-round split of an MFMA GEMM: when its tiles leave a last round of CUs partly idle, the
 // tiles of that round are split two or four ways in K, every piece writes its fp32 partial sums
 // to a slot of split_part, and the last piece of a tile to finish adds the slots in piece order
