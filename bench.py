@@ -343,7 +343,10 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     traffic = profiled_traffic(p.name)
-    roof.update({"kernel": "gate/up grouped GEMM + SwiGLU (both tile families)",
+    single = p.T == 1 and p.wdtype != "fp8" and not p.shared and p.d <= 8192 and args.tile_config != 1
+    roof.update({"kernel": "gate/up grouped GEMM + SwiGLU" + (
+                     " with the token's routing fused in (single-token decode kernel)" if single
+                     else " (both tile families)"),
                  "avg_launch_ms": round(gu_ms, 4),
                  "traffic": traffic, "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + "
                  "WRITE_SIZE, calibrated on a 1 GiB copy)" if traffic else None,
