@@ -23,11 +23,13 @@ __device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
 // counts, and the segments' places in their (GEMM, family) list.  Each list has two classes of
 // segments, class 0 first, each class by expert id, and the MFMA kernel hands its tiles out in one
 // of three orders (kMetaOrder):
-//  * kOrderMix (short K, several rounds): class 0 = experts with two or more m-tiles ("heavy"),
-//    class 1 = the rest; the light tiles are spread evenly between the heavy ones, and an expert's
-//    last m-tile stays next to its siblings, which share its weight tile in L2.  (Streaming lists
-//    use the same classes.)
-//  * kOrderChunks (K >= kLongK, several rounds): an expert whose last 256-row m-tile would hold at
+//  * kOrderMix (several rounds, short K or no expert of two m-tiles): class 0 = experts with two
+//    or more m-tiles ("heavy"), class 1 = the rest; the light tiles are spread evenly between the
+//    heavy ones, and an expert's last m-tile stays next to its siblings, which share its weight
+//    tile in L2.  (Streaming lists use the same classes.)
+//  * kOrderChunks (K >= kLongK, several rounds, some expert of more than one m-tile -- without one
+//    no weight tile is shared by several m-tiles and the mixed order is faster, 3.5% on a
+//    DeepSeek-V3-shaped layer at T = 256): an expert whose last 256-row m-tile would hold at
 //    most 128 rows gets that tail as a segment of its own; class 0 = segments of full-height tiles,
 //    class 1 = shorter ones; whole XCD chunks of one class, the class-1 chunks spread evenly between
 //    the class-0 ones.  Short tiles still run beside MFMA-bound full ones across the chip, while the
@@ -58,23 +60,27 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   // (<= kStreamMaxRows rows) on the streaming tiles, which spread each expert's weights over many
   // workgroups.  The same (block-wide) totals give the list's ordering mode: one to
   // kSplitMaxRounds rounds -> longest first (below one round every tile starts at once and order
-  // does not matter).
-  bool lpt[2] = {false, false};
+  // does not matter); else XCD chunks when K >= kLongK and some expert spans several m-tiles.
+  bool lpt[2] = {false, false}, chunks[2] = {false, false};
   if (!a.fp8) {
-    int w[2], wex[2], wtot[2];
+    // w[0..1]: MFMA tiles per GEMM; w[2..3]: MFMA experts of more than one m-tile per GEMM
+    int w[4], wex[4], wtot[4];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 2; ++g) {
       w[g] = fm[g] == kFamMfma
                  ? (c + kMfmaBM - 1) / kMfmaBM *
                        (g == 0 ? ffe / kMfmaBNGateUp : (a.d + kMfmaBNDown - 1) / kMfmaBNDown)
                  : 0;
-    block_scan<2, 16>(w, wex, wtot, scan_lds);
+      w[2 + g] = fm[g] == kFamMfma && c > kMfmaBM ? 1 : 0;
+    }
+    block_scan<4, 16>(w, wex, wtot, scan_lds);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       if (a.config < 0 && fm[g] == kFamMfma && wtot[g] < 2 * a.num_cus && c <= kStreamMaxRows)
         fm[g] = kFamStream;
       const int C = min(a.num_cus, kSplitMaxPieces);
       lpt[g] = wtot[g] >= C && wtot[g] < kSplitMaxRounds * C;
+      chunks[g] = !lpt[g] && (g == kGemmGateUp ? a.d : ffe) >= kLongK && wtot[2 + g] > 0;
     }
   }
   // Segment j = 2 * gemm + part (part 0: main, 1: MFMA tail), rows [r0[j], r0[j] + nr[j]) of the
@@ -94,7 +100,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     for (int j = 0; j < NS; ++j) {
       const int g = j >> 1, part = j & 1;
       const bool mf = fm[g] == kFamMfma;
-      const bool split = mf && tail > 0 && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
+      const bool split = mf && tail > 0 && (lpt[g] || chunks[g]);
       fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
       r0[j] = part == 0 ? 0 : c - tail;
       nr[j] = part == 0 ? (split ? c - tail : c) : tail;
@@ -109,7 +115,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
         nt[j] = (a.d + tn[j] - 1) / tn[j];
       }
       mt[j] = (nr[j] + tm - 1) / tm;
-      const bool by_height = mf && (lpt[g] || (g == kGemmGateUp ? a.d : ffe) >= kLongK);
+      const bool by_height = mf && (lpt[g] || chunks[g]);
       cls[j] = by_height ? (nr[j] <= kMfmaBM / 2 ? 1 : 0) : (mt[j] >= 2 ? 0 : 1);
       // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
@@ -225,7 +231,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     const int C = min(a.num_cus, kSplitMaxPieces);
     const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8;
     // (lpt[] is the same for every thread)
-    m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : K >= kLongK ? kOrderChunks
+    m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : chunks[g] ? kOrderChunks
                                                                                       : kOrderMix;
     if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_cnt && uniform_k) {
       const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
