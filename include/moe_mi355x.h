@@ -154,7 +154,9 @@ int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w
 
 /* The whole layer: route -> permute -> (fp8: quantise activations) -> grouped gate/up + SwiGLU ->
  * grouped down (+ shared expert) -> combine.  The token gather is fused into the gate/up GEMM's
- * activation loads.
+ * activation loads.  For a single bf16 token without a shared expert (T = 1, d <= 8192, config
+ * not forcing MFMA tiles) routing, permutation and selection run inside the gate/up kernel: same
+ * results and routing outputs, one launch fewer.
  *   logits [T][E] fp32, x [T][d] bf16, out [T][d] bf16.  keep: optional routing outputs.
  *   ws: moe_layer_workspace_bytes(p) bytes (bf16 weights: including 64 MiB of split-K slots). */
 int moe_layer(const moe_problem* p, const float* logits, const void* x, const moe_weights* w,
@@ -163,7 +165,8 @@ size_t moe_layer_workspace_bytes(const moe_problem* p);
 
 /* moe_layer with phase timing: records events[0] before the first launch and events[i] after
  * phase i, for the phases route (1), permute (2), activation quantisation (3, empty for bf16),
- * tile selection (4), gate/up GEMM + SwiGLU (5), down GEMM (6) and combine (7).  The caller creates
+ * tile selection (4), gate/up GEMM + SwiGLU (5), down GEMM (6) and combine (7).  (In the
+ * single-token case of moe_layer phases 1-4 are empty and phase 5 includes them.)  The caller creates
  * the MOE_TRACE_EVENTS events (hipEventCreate) and reads them after the stream has passed them.
  * NULL entries are skipped (each recorded timing event adds a few microseconds of GPU time, so
  * a caller may record only the boundaries it needs).  Same results as moe_layer; num_events must
