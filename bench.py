@@ -220,6 +220,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM byte-counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time replays of one layer call captured in a HIP graph")
     ap.add_argument("--select-control", action="store_true",
                     help="also time the layer with every expert forced onto one tile family (the "
                          "control arms of the device-side selection), same protocol, fewer steps")
@@ -315,6 +317,45 @@ def main() -> int:
     for e in evs:
         hip.destroy(e)
 
+    # HIP-graph replay (optional): one layer call captured on a side stream's capture, replayed K
+    # times with the same flush protocol; the library launches no allocation, memset or host sync,
+    # so the whole call is capturable.
+    graph = None
+    if args.graph:
+        static_logits, static_x = d_logits.clone(), d_x.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer(static_logits, static_x)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer(static_logits, static_x)
+        torch.cuda.synchronize()
+        for _ in range(Wm):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        rep_ms = []
+        t0 = time.perf_counter()
+        for i in range(K):
+            flush(i)
+            e0.record()
+            g.replay()
+            e1.record()
+            if args.flush:
+                e1.synchronize()
+                rep_ms.append(e0.elapsed_time(e1))
+        torch.cuda.synchronize()
+        g_wall = time.perf_counter() - t0
+        g_ms = statistics.median(rep_ms) if args.flush else g_wall * 1e3 / K
+        graph = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(p.T / (g_ms * 1e-3), 1),
+                 "timing": "median of events around each replay" if args.flush
+                 else "wall clock over the replays"}
+        del g
+
     n_active = int((counts.cpu() > 0).sum())
     alg = algorithmic(p, n_active)
     if args.flush:
@@ -380,6 +421,8 @@ def main() -> int:
     }
     if step_spread:
         out["layer"]["step_ms"] = step_spread
+    if graph:
+        out["graph_replay"] = graph
     if args.select_control and p.wdtype != "fp8":
         out["select_control"] = select_control(args, p, ew, d_logits, d_x, flush, ms_per_step)
     if args.copy_calibration:
