@@ -194,8 +194,9 @@ def test_layer_matches_oracle(moe, p, config):
 # token itself and takes its tiles' experts from that; its first workgroup also writes the routing
 # outputs and the down GEMM's segments.  Cases: each width of the routing's per-lane candidates
 # (E <= 64, 128, 256, 512), both streaming tile widths (d below 4096: 32 columns, else 16), more
-# tiles than workgroups (f = 4096, k = 8: 2048 tiles of 16 columns), and d above the staging limit
-# (the general path).  The down GEMM runs on the segments the gate/up kernel wrote.
+# tiles than workgroups (f = 4096, k = 8: 2048 gate/up tiles of 16 columns), f above 8192, and d
+# above the staging limit (the general path).  The down GEMM runs on the segments the gate/up
+# kernel wrote.
 DECODE1 = [
     _small("decode1_E64_k1", T=1, d=256, f=256, E=64, k=1, cfg_index=160),
     _small("decode1_E128", T=1, d=1024, f=512, E=128, k=6, routing="dirichlet", alpha=0.3,
@@ -205,6 +206,7 @@ DECODE1 = [
     _small("decode1_E512", T=1, d=512, f=384, E=512, k=8, cfg_index=163),
     _small("decode1_many_tiles", T=1, d=4096, f=4096, E=8, k=8, cfg_index=164),
     _small("decode1_wide_d", T=1, d=8320, f=256, E=8, k=2, cfg_index=165),
+    _small("decode1_wide_f", T=1, d=256, f=8320, E=4, k=2, cfg_index=167),
 ]
 
 
