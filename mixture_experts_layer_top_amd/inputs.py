@@ -134,6 +134,49 @@ def gen_dirichlet_p(p: Problem) -> np.ndarray:
     return np.maximum(prob, 1e-38)
 
 
+# ---------------------------------------------------------------------------------------------
+# routing skew as "effective experts"
+#
+# "Decoding the Skew ..." (Abstract) characterises routing by its Effective Experts and models it
+# with Dirichlet draws.  For p ~ Dirichlet(alpha * 1_E) the expected entropy has a closed form,
+#     E[-sum_e p_e ln p_e] = psi(E alpha + 1) - psi(alpha + 1)        (psi: digamma),
+# and exp of it is the effective expert count of a typical draw; it rises monotonically from 1
+# (alpha -> 0) to E (alpha -> infinity), so a target count fixes alpha (bisection in log alpha).
+# ---------------------------------------------------------------------------------------------
+
+def expected_entropy(E: int, alpha: float) -> float:
+    """Expected entropy (nats) of p ~ Dirichlet(alpha * 1_E)."""
+    from scipy.special import digamma
+    return float(digamma(E * alpha + 1.0) - digamma(alpha + 1.0))
+
+
+def expected_eeff(E: int, alpha: float) -> float:
+    """exp of the expected entropy: the effective expert count of a typical Dirichlet draw."""
+    return math.exp(expected_entropy(E, alpha))
+
+
+def alpha_for_eeff(E: int, target: float, lo: float = 1e-6, hi: float = 1e6) -> float:
+    """The Dirichlet concentration whose draws have `target` effective experts (1 < target < E)."""
+    if not 1.0 < target < E:
+        raise ValueError(f"effective experts must lie in (1, {E}), got {target}")
+    h = math.log(target)
+    a, b = math.log(lo), math.log(hi)
+    for _ in range(200):
+        m = 0.5 * (a + b)
+        if expected_entropy(E, math.exp(m)) < h:
+            a = m
+        else:
+            b = m
+    return math.exp(0.5 * (a + b))
+
+
+def effective_experts(counts: np.ndarray) -> float:
+    """Effective experts of a routing histogram: exp(-sum q ln q), q = counts / sum(counts)."""
+    c = np.asarray(counts, dtype=np.float64)
+    q = c[c > 0] / c.sum()
+    return float(math.exp(-(q * np.log(q)).sum()))
+
+
 def gen_x(p: Problem) -> np.ndarray:
     """Activations [T, d] as bf16 bit patterns (uint16)."""
     rng = np.random.Generator(np.random.PCG64(_seedseq(p, TAG_X, p.T)))

@@ -1,4 +1,5 @@
 """The seeded input generator: determinism, distributions, device independence (CPU side)."""
+import math
 import numpy as np
 import torch
 
@@ -87,3 +88,35 @@ def test_shapes():
     assert W["gate"].shape == (8, 512, 256) and W["down"].shape == (8, 256, 512)
     assert W["gate"].dtype == torch.int16
     assert I.gen_logits(I.TINY).shape == (64, 8) and I.gen_x(I.TINY).shape == (64, 256)
+
+
+# Dirichlet effective-experts model: the closed-form expected entropy against Monte Carlo draws of
+# the same distribution, its limits, monotonicity, and the inverse (alpha from a target count).
+def test_expected_entropy_closed_form_vs_monte_carlo():
+    rng = np.random.default_rng(7)
+    for E, alpha in ((256, 0.1), (256, 1.0), (384, 0.3), (8, 10.0)):
+        draws = rng.dirichlet(np.full(E, alpha), size=400)
+        d = np.maximum(draws, 1e-300)
+        h = -(d * np.log(d)).sum(axis=1)
+        assert abs(h.mean() - I.expected_entropy(E, alpha)) <= 0.02 * I.expected_entropy(E, alpha) + 3 * h.std() / 20
+
+
+def test_expected_eeff_limits_and_monotone():
+    E = 256
+    vals = [I.expected_eeff(E, a) for a in (1e-4, 1e-2, 0.1, 1.0, 10.0, 1e4)]
+    assert all(x < y for x, y in zip(vals, vals[1:]))
+    assert vals[0] < 1.05 and abs(vals[-1] - E) / E < 0.01
+    # a uniform p (alpha -> infinity) has entropy ln E exactly
+    assert abs(I.expected_entropy(E, 1e9) - math.log(E)) < 1e-6
+
+
+def test_alpha_for_eeff_round_trip():
+    for E in (8, 256, 384):
+        for alpha in (0.05, 0.3, 1.0, 7.0):
+            target = I.expected_eeff(E, alpha)
+            assert abs(I.alpha_for_eeff(E, target) / alpha - 1.0) < 1e-6
+
+
+def test_effective_experts_of_counts():
+    assert abs(I.effective_experts(np.array([5, 5, 5, 5, 0])) - 4.0) < 1e-12
+    assert abs(I.effective_experts(np.array([7, 0, 0])) - 1.0) < 1e-12
