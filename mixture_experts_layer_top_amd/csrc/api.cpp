@@ -126,9 +126,9 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
 
 // max_rows bounds the rows of any one expert and total_rows the rows of all of them.  The MFMA
 // kernel (whose queue would be empty) is not launched when no expert can pass the streaming
-// threshold, nor when the selection's two-round rule must move every expert to the streaming
-// tiles: no expert exceeds kStreamMaxRows rows and even one m-tile per expert that can hold rows
-// would not make two rounds of CUs.
+// threshold, nor when the selection's few-tile rule must move every expert to the streaming tiles:
+// no expert exceeds kFewTileRows rows and even one m-tile per expert that can hold rows would not
+// make 1.6 rounds of CUs.
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, hipStream_t s) {
   const int cus = device_cus();
@@ -136,11 +136,11 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
   const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
   const bool stream = p->config != MOE_CONFIG_MFMA;
   bool mfma = p->config == MOE_CONFIG_MFMA || (p->config == MOE_CONFIG_AUTO && max_rows > thr);
-  if (mfma && p->config == MOE_CONFIG_AUTO && max_rows <= kStreamMaxRows && !p->has_shared) {
+  if (mfma && p->config == MOE_CONFIG_AUTO && max_rows <= kFewTileRows && !p->has_shared) {
     const int64_t experts = std::min<int64_t>(p->num_experts, total_rows);
     const int64_t nt = gemm == kGemmGateUp ? p->d_ff / kMfmaBNGateUp
                                            : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
-    if (experts * nt < 2 * (int64_t)cus) mfma = false;
+    if (5 * experts * nt < kFewTileRounds5 * (int64_t)cus) mfma = false;
   }
   const int max_k = gemm == kGemmGateUp ? p->d_model
                                          : std::max(p->d_ff, p->has_shared ? p->d_ff_shared : 0);

@@ -18,6 +18,11 @@ constexpr int kStreamMaxRows = 64;  // rows per weight-streaming pass
 // weights of even a one-row gate/up expert faster, given enough tiles; see select.hip).
 constexpr int kStreamRowsGateUp = 0;
 constexpr int kStreamRowsDown = 8;
+// Few-tile rule: a GEMM whose MFMA tiles would fill fewer than kFewTileRounds5 / 5 rounds of CUs
+// runs wholly on the streaming tiles when none of its MFMA experts holds more than kFewTileRows
+// rows (one 16-row MFMA pass per weight load); a larger expert keeps the whole GEMM on MFMA.
+constexpr int kFewTileRows = 16;
+constexpr int kFewTileRounds5 = 8;
 constexpr int kMfmaBM = 256;        // rows per full LDS-tiled MFMA tile
 constexpr int kMfmaBNGateUp = 128;  // h columns per gate/up MFMA tile (128 gate + 128 up rows)
 constexpr int kMfmaBNDown = 256;    // y columns per down MFMA tile

@@ -8,7 +8,9 @@
 // Here the choice is made per expert and per GEMM, from the expert's row count c_e, inside one
 // workgroup that runs between the permutation and the GEMMs:
 //   down GEMM with c_e <= 8 -> weight-streaming tiles: the expert's rows ride along while its
-//                 weights stream from HBM once (a handful of rows: c_e FLOP per weight byte);
+//                 weights stream from HBM once (a handful of rows: c_e FLOP per weight byte) --
+//                 unless the down GEMM's heavier experts fill a round of MFMA tiles by
+//                 themselves: then the light ones join them on MFMA tiles;
 //   otherwise -> LDS-tiled MFMA tiles of 256 weight rows by 64, 128 or 256 token rows (the tile
 //                 height follows the rows the tile holds), so a light expert streams its weights
 //                 through LDS once and pays MFMA time for at most 63 padding rows.
@@ -16,8 +18,10 @@
 // faster on the MFMA family than on the streaming tiles as long as there are enough tiles, while
 // the down GEMM (short K = d_ff) still prefers streaming for up to about 8 rows.
 // An MFMA tile costs a whole K loop on one CU however few rows it holds: when a GEMM's MFMA tiles
-// would not fill two rounds of CUs, its experts of up to 64 rows take the streaming tiles, which
-// spread each expert's weights over many workgroups.  Block-scaled fp8 experts always take the
+// would fill fewer than 1.6 rounds of CUs and none of its experts holds more than 16 rows, the
+// whole GEMM takes the streaming tiles, which spread each expert's weights over many workgroups
+// (with one heavier expert it stays on MFMA: no GEMM is split between a streaming launch and an
+// under-filled MFMA launch by this rule).  Block-scaled fp8 experts always take the
 // streaming family (up to 32 rows per pass).  Inside an MFMA list, segments of full-height tiles come
 // first and those of shorter tiles last (an expert's short last m-tile is a segment of its own), so
 // the persistent kernel hands out the longest tiles first and the short ones fill the last round;

@@ -55,28 +55,47 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   int fm[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8) : -1;
-  // An MFMA tile costs a whole K loop on one CU however few rows it holds, so a GEMM whose MFMA
-  // tiles would not fill two rounds of CUs (the last round is partly idle) keeps its small experts
-  // (<= kStreamMaxRows rows) on the streaming tiles, which spread each expert's weights over many
-  // workgroups.  The same (block-wide) totals give the list's ordering mode: one to
-  // kSplitMaxRounds rounds -> longest first (below one round every tile starts at once and order
-  // does not matter); else XCD chunks when K >= kLongK and some expert spans several m-tiles.
+  // The down GEMM's light experts (<= kStreamRowsDown rows) take the streaming tiles only while its
+  // heavier experts' MFMA tiles fill less than one round of CUs; with a round or more they join the
+  // MFMA list, where their short tiles fill the rounds' gaps instead of running as a second launch
+  // after the MFMA one (2-10% faster on DeepSeek-V3-shaped layers at T = 64 and 256 with 8 to 32
+  // effective experts).
+  // An MFMA tile costs a whole K loop on one CU, and one CU alone draws a fraction of the chip's
+  // bandwidth, so a GEMM whose MFMA tiles would fill fewer than 1.6 rounds of CUs moves all its
+  // experts to the streaming tiles, which spread each expert's weights over many workgroups -- but
+  // only when every one of them is light (<= kFewTileRows rows).  With a heavier expert the GEMM
+  // stays on MFMA: the streaming tiles lose to MFMA once an expert spans several 16-row passes, and
+  // a split GEMM runs its two launches back to back with the MFMA one under-filled (1.3-1.5x the
+  // all-MFMA time on a DeepSeek-V3-shaped layer at T = 64 and 256 with 8 effective experts).  The
+  // same (block-wide) totals give the list's ordering mode: one to kSplitMaxRounds rounds ->
+  // longest first (below one round every tile starts at once and order does not matter); else XCD
+  // chunks when K >= kLongK and some expert spans several m-tiles.
   bool lpt[2] = {false, false}, chunks[2] = {false, false};
   if (!a.fp8) {
-    // w[0..1]: MFMA tiles per GEMM; w[2..3]: MFMA experts of more than one m-tile per GEMM
-    int w[4], wex[4], wtot[4];
+    // w[0..1]: MFMA tiles per GEMM; w[2..3]: MFMA experts of more than one m-tile per GEMM;
+    // w[4..5]: MFMA experts of more than kFewTileRows rows per GEMM; w[6]: down tiles of the light
+    // experts the threshold put on the streaming tiles (w[7] unused)
+    const int nt_dn = (a.d + kMfmaBNDown - 1) / kMfmaBNDown;
+    int w[8], wex[8], wtot[8];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       w[g] = fm[g] == kFamMfma
-                 ? (c + kMfmaBM - 1) / kMfmaBM *
-                       (g == 0 ? ffe / kMfmaBNGateUp : (a.d + kMfmaBNDown - 1) / kMfmaBNDown)
+                 ? (c + kMfmaBM - 1) / kMfmaBM * (g == 0 ? ffe / kMfmaBNGateUp : nt_dn)
                  : 0;
       w[2 + g] = fm[g] == kFamMfma && c > kMfmaBM ? 1 : 0;
+      w[4 + g] = fm[g] == kFamMfma && c > kFewTileRows ? 1 : 0;
     }
-    block_scan<4, 16>(w, wex, wtot, scan_lds);
+    w[6] = a.config < 0 && fm[kGemmDown] == kFamStream ? nt_dn : 0;  // c <= kStreamRowsDown < kMfmaBM
+    w[7] = 0;
+    block_scan<8, 16>(w, wex, wtot, scan_lds);
+    if (a.config < 0 && wtot[kGemmDown] >= a.num_cus) {
+      if (w[6]) fm[kGemmDown] = kFamMfma;
+      wtot[kGemmDown] += wtot[6];
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      if (a.config < 0 && fm[g] == kFamMfma && wtot[g] < 2 * a.num_cus && c <= kStreamMaxRows)
+      if (a.config < 0 && fm[g] == kFamMfma && 5 * wtot[g] < kFewTileRounds5 * a.num_cus &&
+          wtot[4 + g] == 0)
         fm[g] = kFamStream;
       const int C = min(a.num_cus, kSplitMaxPieces);
       lpt[g] = wtot[g] >= C && wtot[g] < kSplitMaxRounds * C;
