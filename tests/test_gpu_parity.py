@@ -161,6 +161,14 @@ LAYER = [
     _small("layer_down_tail64", T=320, d=128, f=4096, E=1, k=1, cfg_index=113),
     _small("layer_down_tail65", T=321, d=128, f=4096, E=1, k=1, cfg_index=114),
     _small("layer_down_tail2e", T=560, d=128, f=4096, E=2, k=1, cfg_index=115),
+    # down GEMM of 8 column tiles per expert with light (<= 8 rows) and heavier experts: 43 light
+    # experts beside heavier ones worth 392 down tiles, so on 256 CUs the light ones join the MFMA
+    # list; with 240 heavy tiles (below one round) they stay on the streaming tiles and the GEMM
+    # runs both launches
+    _small("layer_down_promote", T=300, d=2048, f=256, E=96, k=4, routing="dirichlet", alpha=1.0,
+           cfg_index=116),
+    _small("layer_down_split", T=160, d=2048, f=256, E=64, k=4, routing="dirichlet", alpha=1.0,
+           cfg_index=116),
 ]
 
 
