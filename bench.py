@@ -200,6 +200,53 @@ def select_control(args, p, ew, d_logits, d_x, flush, auto_ms):
     return res
 
 
+def vendor_dense(args, p, gu_ms, dn_ms, alg):
+    """The vendor library's dense bf16 GEMMs (hipBLASLt through torch.matmul) with the same FLOPs
+    as the layer's two grouped GEMMs, for context: all T*k routed rows against one weight matrix,
+    without grouping, gather, SwiGLU or the combine.  Same timing protocol as the layer (events
+    around each call after a cache flush with --flush, else wall clock over the calls).  A dense GEMM
+    reads one weight matrix where the grouped one streams every active expert's, so each entry also
+    gives the time those algorithmic bytes take at peak HBM bandwidth: the comparison means most
+    where that floor is well below the dense GEMM's time (prefill with few experts)."""
+    import torch
+    M = p.T * p.k
+    res = {"note": "torch.matmul bf16 (vendor library), dense, same FLOPs as each grouped GEMM"}
+    n = max(5, args.steps)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+    for name, (K, N), ours, nbytes in (("gate_up", (p.d, 2 * p.f), gu_ms, alg["bytes_gu"]),
+                                       ("down", (p.f, p.d), dn_ms, alg["bytes_dn"])):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        if flush_buf is not None:
+            ts = []
+            for _ in range(n):
+                flush_buf.view(torch.int64).sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                c = a @ b
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = statistics.median(ts)
+        else:
+            t0 = time.perf_counter()
+            for _ in range(n):
+                c = a @ b
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / n
+        del a, b, c
+        res[name] = {"shape_MxNxK": f"{M}x{N}x{K}", "ms": round(ms, 4),
+                     "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                     "this_layer_kernel_ms": round(ours, 4), "layer_kernel_over_vendor": round(ours / ms, 3),
+                     "grouped_bytes_hbm_floor_ms": round(nbytes / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+    res["kernel_ms_source"] = ("gate_up: HIP events around every second step's gate/up launches; "
+                               "down: the phase-traced steps (each phase event adds ~5 us)")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +269,9 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (for HBM byte-counter calibration)")
     ap.add_argument("--graph", action="store_true",
                     help="also time replays of one layer call captured in a HIP graph")
+    ap.add_argument("--vendor-dense", action="store_true",
+                    help="also time the vendor library's dense bf16 GEMMs of the same FLOPs as the "
+                         "layer's two grouped GEMMs (context for the MFMA kernels)")
     ap.add_argument("--select-control", action="store_true",
                     help="also time the layer with every expert forced onto one tile family (the "
                          "control arms of the device-side selection), same protocol, fewer steps")
@@ -423,6 +473,8 @@ def main() -> int:
         out["layer"]["step_ms"] = step_spread
     if graph:
         out["graph_replay"] = graph
+    if args.vendor_dense and p.wdtype != "fp8":
+        out["vendor_dense"] = vendor_dense(args, p, gu_ms, statistics.mean(phases["down"]), alg)
     if args.select_control and p.wdtype != "fp8":
         out["select_control"] = select_control(args, p, ew, d_logits, d_x, flush, ms_per_step)
     if args.copy_calibration:
