@@ -47,6 +47,7 @@ TAG_SCALE = 16  # added to the weight tag
 
 WDT_BF16 = "bf16"
 WDT_FP8 = "fp8"
+WDT_MXFP4 = "mxfp4"
 
 
 @dataclass(frozen=True)
@@ -82,7 +83,11 @@ FP8_TS = (32, 128)
 FP8 = Problem("fp8_dsv3_decode", 4, T=32, d=7168, f=2048, E=256, k=8, routing="dirichlet",
               alpha=1.0, wdtype=WDT_FP8, shared=True, shared_f=2048)
 
-CONFIGS = {p.name: p for p in (TINY, MIXTRAL, DSV3, KIMI, FP8)}
+# DeepSeek-V3-shaped decode with MXFP4 routed experts (bf16 activations); no shared expert
+MXFP4 = Problem("mxfp4_dsv3_decode", 5, T=64, d=7168, f=2048, E=256, k=8, routing="dirichlet",
+                alpha=1.0, wdtype=WDT_MXFP4)
+
+CONFIGS = {p.name: p for p in (TINY, MIXTRAL, DSV3, KIMI, FP8, MXFP4)}
 
 
 def dsv3_point(T: int, alpha: float) -> Problem:
@@ -290,6 +295,38 @@ def hashed_e4m3_codes(key: tuple[int, int], n: int, device, start: int = 0):
     return code.to(torch.uint8)
 
 
+# E2M1 magnitude codes 0..7 stand for 0, 0.5, 1, 1.5, 2, 3, 4, 6; a half-normal of std 2 (in those
+# units) split at the midpoints between them gives each code's probability.
+_E2M1_SIGMA = 2.0
+_E2M1_EDGES = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _e2m1_thresholds() -> list[int]:
+    """Cumulative 15-bit thresholds between the E2M1 magnitude codes of a half-normal(std 2)."""
+    return [min(int(round(math.erf(v / (_E2M1_SIGMA * math.sqrt(2.0))) * (1 << 15))), (1 << 15) - 1)
+            for v in _E2M1_EDGES]
+
+
+def hashed_e2m1_bytes(key: tuple[int, int], nbytes: int, device, start: int = 0):
+    """nbytes bytes of packed E2M1 codes (two per byte, low nibble first), each code drawn field by
+    field from 16 hash bits: a uniform sign and a magnitude code from a 15-bit uniform."""
+    import torch
+
+    h = hash_stream(key, start, nbytes, device)
+    th = torch.tensor(_e2m1_thresholds(), dtype=torch.int64, device=device)
+    nib = []
+    for half in (h & 0xFFFF, h >> 16):
+        mag = torch.bucketize(half & 0x7FFF, th, right=True)
+        nib.append(((half >> 15) << 3) | mag)
+    return (nib[0] | (nib[1] << 4)).to(torch.uint8)
+
+
+def hashed_e8m0_scales(key: tuple[int, int], n: int, device):
+    """n E8M0 scale codes, uniform over 120..124 (2^-7 ... 2^-3)."""
+    h = hash_stream(key, 0, n, device)
+    return (120 + (h >> 8) % 5).to(__import__("torch").uint8)
+
+
 def hashed_block_scales(key: tuple[int, int], n: int, device):
     """n fp32 block scales, uniform in [2^-13, 2^-12) with a random 23-bit mantissa (exact)."""
     import torch
@@ -306,6 +343,8 @@ def hashed_block_scales(key: tuple[int, int], n: int, device):
 #   gate, up : [E, f, d]  (math shape d x f, stored transposed)
 #   down     : [E, d, f]  (math shape f x d, stored transposed)
 #   fp8 block scales: gate/up [E, f/128, d/128], down [E, d/128, f/128]
+#   mxfp4: packed E2M1 gate/up [E, f, d/2], down [E, d, f/2] (low nibble = even column) and E8M0
+#          scales gate/up [E, f, d/32], down [E, d, f/32], one per 32 along the contraction dim
 WEIGHT_TAGS = {"gate": TAG_W_GATE, "up": TAG_W_UP, "down": TAG_W_DOWN,
                "sh_gate": TAG_SH_GATE, "sh_up": TAG_SH_UP, "sh_down": TAG_SH_DOWN}
 
@@ -323,18 +362,24 @@ def weight_shape(p: Problem, which: str) -> tuple[int, int]:
 
 
 def gen_expert_weight(p: Problem, which: str, e: int, device="cpu"):
-    """One expert's stored weight matrix: int16 bf16 bits, or uint8 e4m3 codes for fp8."""
+    """One expert's stored weight matrix: int16 bf16 bits, uint8 e4m3 codes for fp8, or packed
+    uint8 E2M1 pairs [rows, cols/2] for mxfp4."""
     rows, cols = weight_shape(p, which)
     key = stream_key(p.cfg_index, WEIGHT_TAGS[which], e)
     if p.wdtype == WDT_BF16:
         return hashed_normal_bf16(key, rows * cols, p.w_sigma, device).view(rows, cols)
+    if p.wdtype == WDT_MXFP4:
+        return hashed_e2m1_bytes(key, rows * cols // 2, device).view(rows, cols // 2)
     return hashed_e4m3_codes(key, rows * cols, device).view(rows, cols)
 
 
 def gen_expert_scales(p: Problem, which: str, e: int, device="cpu"):
-    """One expert's fp32 128x128 block scales (fp8 weights only)."""
+    """One expert's scales: fp32 per 128x128 block (fp8), or uint8 E8M0 per 32 along a row
+    [rows, cols/32] (mxfp4)."""
     rows, cols = weight_shape(p, which)
     key = stream_key(p.cfg_index, WEIGHT_TAGS[which] + TAG_SCALE, e)
+    if p.wdtype == WDT_MXFP4:
+        return hashed_e8m0_scales(key, rows * (cols // 32), device).view(rows, cols // 32)
     return hashed_block_scales(key, (rows // 128) * (cols // 128), device).view(rows // 128, cols // 128)
 
 
@@ -344,14 +389,22 @@ def gen_weights(p: Problem, device="cpu") -> dict:
 
     out = {}
     wdt = torch.int16 if p.wdtype == WDT_BF16 else torch.uint8
+    if p.wdtype == WDT_MXFP4 and p.shared:
+        raise ValueError("mxfp4 weights: no shared expert")
     for which in ("gate", "up", "down"):
         rows, cols = weight_shape(p, which)
-        t = torch.empty((p.E, rows, cols), dtype=wdt, device=device)
+        wcols = cols // 2 if p.wdtype == WDT_MXFP4 else cols
+        t = torch.empty((p.E, rows, wcols), dtype=wdt, device=device)
         for e in range(p.E):
             t[e] = gen_expert_weight(p, which, e, device)
         out[which] = t
         if p.wdtype == WDT_FP8:
             s = torch.empty((p.E, rows // 128, cols // 128), dtype=torch.float32, device=device)
+            for e in range(p.E):
+                s[e] = gen_expert_scales(p, which, e, device)
+            out["s_" + which] = s
+        elif p.wdtype == WDT_MXFP4:
+            s = torch.empty((p.E, rows, cols // 32), dtype=torch.uint8, device=device)
             for e in range(p.E):
                 s[e] = gen_expert_scales(p, which, e, device)
             out["s_" + which] = s

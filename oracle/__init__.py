@@ -8,5 +8,6 @@ which holds no arithmetic of the layer.
 
 Modules:
   fp8_e4m3   OCP E4M3FN codec written from the format definition.
+  mxfp4      OCP MXFP4 (E2M1 elements, E8M0 scales per 32) written from the format definitions.
   moe_oracle the layer, step by step, in float64.
 """

@@ -38,7 +38,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import fp8_e4m3
+from . import fp8_e4m3, mxfp4
 
 ACT_BLOCK = 128  # activation quantisation group (channels)
 W_BLOCK = 128  # weight scale block edge
@@ -81,12 +81,16 @@ def dequant_e4m3_blocks(codes, scales) -> np.ndarray:
 
 
 def decode_weight(raw, scales=None) -> np.ndarray:
-    """Stored expert weight -> float64: bf16 bits, or E4M3 codes with their block scales."""
+    """Stored expert weight -> float64: bf16 bits; E4M3 codes with fp32 128x128 block scales; or
+    packed MXFP4 (E2M1 pairs) with uint8 E8M0 scales per 32 along a row."""
     a = np.asarray(raw)
     if a.dtype == np.uint8:
         if scales is None:
-            raise ValueError("fp8 weights need block scales")
-        return dequant_e4m3_blocks(a, scales)
+            raise ValueError("fp8 and mxfp4 weights need scales")
+        sc = np.asarray(scales)
+        if sc.dtype == np.uint8:
+            return mxfp4.dequant(a, sc)
+        return dequant_e4m3_blocks(a, sc)
     return bf16_bits_to_f64(a)
 
 
