@@ -44,6 +44,10 @@ def workload(args):
         return I.dsv3_point(args.T or 256, args.alpha if args.alpha is not None else 1.0)
     if name == "fp8_dsv3_decode":
         return I.fp8_point(args.T or 128)
+    if name == "mxfp4_dsv3_decode":
+        base = I.MXFP4
+        T = args.T or base.T
+        return replace(base, T=T, name=f"{base.name}_T{T}")
     raise SystemExit(f"unknown --config {name}")
 
 
@@ -80,12 +84,15 @@ class HipEvents:
 def algorithmic(p, n_active: int):
     """FLOPs and bytes the layer must move (only experts with rows count; intermediates such as
     the permuted rows, h and y are implementation overhead and are not credited)."""
-    wb = 1 if p.wdtype == "fp8" else 2
+    wb = {"fp8": 1, "mxfp4": 0.5}.get(p.wdtype, 2)
     sh_f = p.shared_f if p.shared else 0
     flop_gu = 4.0 * p.d * (p.f * p.T * p.k + sh_f * p.T)
     flop_dn = 2.0 * p.d * (p.f * p.T * p.k + sh_f * p.T)
     w_gu = n_active * 2.0 * p.f * p.d * wb + (2.0 * sh_f * p.d * wb if p.shared else 0.0)
     w_dn = n_active * 1.0 * p.f * p.d * wb + (1.0 * sh_f * p.d * wb if p.shared else 0.0)
+    if p.wdtype == "mxfp4":  # one E8M0 byte per 32 weights
+        w_gu += n_active * 2 * p.f * p.d / 32
+        w_dn += n_active * p.f * p.d / 32
     if p.wdtype == "fp8":
         w_gu += (n_active * 2 * p.f * p.d + (2 * sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
         w_dn += (n_active * p.f * p.d + (sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
@@ -146,7 +153,7 @@ def cpu_baseline(p, logits, x, W, sample_tokens: int):
     host = {}
     for e in needed:
         host[e] = {n: W[n][e].cpu().numpy() for n in ("gate", "up", "down")}
-        if p.wdtype == "fp8":
+        if p.wdtype in ("fp8", "mxfp4"):
             host[e].update({"s_" + n: W["s_" + n][e].cpu().numpy() for n in ("gate", "up", "down")})
     sh = None
     if p.shared:
@@ -253,7 +260,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill",
-                    choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode"])
+                    choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode",
+                             "mxfp4_dsv3_decode"])
     ap.add_argument("--T", type=int, default=None, help="tokens (overrides the workload's batch)")
     ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
     ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
@@ -305,6 +313,8 @@ def main() -> int:
     kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
     if p.wdtype == "fp8":
         kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
+    if p.wdtype == "mxfp4":
+        kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
     if p.shared:
         kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
         if p.wdtype == "fp8":
@@ -434,7 +444,7 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     traffic = profiled_traffic(p.name)
-    single = p.T == 1 and p.wdtype != "fp8" and not p.shared and p.d <= 8192 and args.tile_config != 1
+    single = p.T == 1 and p.wdtype == "bf16" and not p.shared and p.d <= 8192 and args.tile_config != 1
     roof.update({"kernel": "gate/up grouped GEMM + SwiGLU" + (
                      " with the token's routing fused in (single-token decode kernel)" if single
                      else " (both tile families)"),
@@ -455,7 +465,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if p.wdtype == "fp8" else "bf16",
+        "dtype": {"fp8": "fp8", "mxfp4": "mxfp4 weights, bf16 activations"}.get(p.wdtype, "bf16"),
         "data": "synthetic",
         "config": {"workload": p.name, "T": p.T, "d_model": p.d, "d_ff": p.f, "experts": p.E,
                    "top_k": p.k, "routing": p.routing + (f"(alpha={p.alpha:g})" if p.routing == "dirichlet" else ""),
@@ -473,9 +483,9 @@ def main() -> int:
         out["layer"]["step_ms"] = step_spread
     if graph:
         out["graph_replay"] = graph
-    if args.vendor_dense and p.wdtype != "fp8":
+    if args.vendor_dense and p.wdtype == "bf16":
         out["vendor_dense"] = vendor_dense(args, p, gu_ms, statistics.mean(phases["down"]), alg)
-    if args.select_control and p.wdtype != "fp8":
+    if args.select_control and p.wdtype == "bf16":
         out["select_control"] = select_control(args, p, ew, d_logits, d_x, flush, ms_per_step)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

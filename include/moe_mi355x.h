@@ -27,6 +27,12 @@
  *       w_down       [E][d_model][d_ff]   (math shape d_ff x d_model)
  *     fp8 weights carry one fp32 scale per 128x128 block: s_gate, s_up [E][d_ff/128][d_model/128],
  *     s_down [E][d_model/128][d_ff/128]; the weight's value is code * scale.
+ *     mxfp4 weights (OCP MX MXFP4; GC-MoE, summary: FP4 grouped GEMM decoded in registers) pack
+ *     two E2M1 codes per byte, element 2j in the low nibble of byte j: w_gate, w_up
+ *     [E][d_ff][d_model/2], w_down [E][d_model][d_ff/2] bytes, with one E8M0 scale byte X per 32
+ *     elements along the contraction dimension: e_gate, e_up [E][d_ff][d_model/32], e_down
+ *     [E][d_model][d_ff/32]; the weight's value is e2m1(code) * 2^(X - 127).  Scales must lie in
+ *     [2, 252] (not checked), which keeps every scaled weight an exact bf16 value.
  *   - Return value: MOE_OK or an error code; moe_status_string() names it.  Arguments are checked
  *     on the host only (null pointers, sizes, 16-byte alignment, workspace size).  Device data is
  *     not validated: non-finite logits or out-of-range expert ids are undefined behaviour.
@@ -55,7 +61,9 @@ enum moe_status {
 
 enum moe_dtype {
   MOE_DTYPE_BF16 = 0,
-  MOE_DTYPE_FP8_E4M3 = 1
+  MOE_DTYPE_FP8_E4M3 = 1,
+  MOE_DTYPE_MXFP4 = 2  /* expert weights only: bf16 activations, no shared expert, streaming tiles
+                          only (config MOE_CONFIG_MFMA and has_shared give MOE_ERR_UNSUPPORTED) */
 };
 
 /* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert and per
@@ -93,6 +101,9 @@ typedef struct moe_weights {
   const float* s_sh_gate; /* fp8 only */
   const float* s_sh_up;
   const float* s_sh_down;
+  const uint8_t* e_gate; /* mxfp4 only: E8M0 scales [E][f][d/32]; NULL otherwise */
+  const uint8_t* e_up;
+  const uint8_t* e_down; /* [E][d][f/32] */
 } moe_weights;
 
 /* Optional routing outputs of moe_layer (any member may be NULL to skip it). */
@@ -135,7 +146,7 @@ int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream
 /* Grouped expert FFN on expert-contiguous rows: for every expert e with counts[e] > 0, rows
  * [offsets[e], offsets[e]+counts[e]) of x_perm go through (SiLU(X Wg^T) * (X Wu^T)) Wd^T; the result
  * lands in the same rows of y_perm ([rows][d] bf16, rows = offsets[E]).  bf16 weights: x_perm is
- * bf16 and x_perm_scale NULL.  fp8 weights: x_perm is e4m3 with x_perm_scale [rows][d/128]; the
+ * bf16 and x_perm_scale NULL (also for mxfp4 weights).  fp8 weights: x_perm is e4m3 with x_perm_scale [rows][d/128]; the
  * SwiGLU output is requantised to e4m3 per row and 128 channels before the down GEMM.  Tile
  * shapes are chosen on the device from counts (p->config may force one family).  The shared expert
  * fields of p and w are ignored here.

@@ -61,7 +61,11 @@ int check_problem(const moe_problem* p) {
   if (st) return st;
   if (p->d_model <= 0 || p->d_ff <= 0) return MOE_ERR_INVALID_ARG;
   if (p->d_model % 128 || p->d_ff % 128) return MOE_ERR_UNSUPPORTED;
-  if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3 &&
+      p->wdtype != MOE_DTYPE_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  if (p->wdtype == MOE_DTYPE_MXFP4 && (p->has_shared || p->config == MOE_CONFIG_MFMA))
+    return MOE_ERR_UNSUPPORTED;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
   if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) return MOE_ERR_INVALID_ARG;
@@ -75,6 +79,9 @@ int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) 
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) {
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_INVALID_ARG;
+  }
+  if (p->wdtype == MOE_DTYPE_MXFP4) {
+    if (!w->e_gate || !w->e_up || !w->e_down) return MOE_ERR_INVALID_ARG;
   }
   if (with_shared && p->has_shared) {
     const void* sh[] = {w->sh_gate, w->sh_up, w->sh_down};
@@ -133,6 +140,9 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
                         int64_t total_rows, hipStream_t s) {
   const int cus = device_cus();
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
+  const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
+  if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
+    return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, s, true);
   const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
   const bool stream = p->config != MOE_CONFIG_MFMA;
   bool mfma = p->config == MOE_CONFIG_MFMA || (p->config == MOE_CONFIG_AUTO && max_rows > thr);
@@ -144,7 +154,7 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
   }
   const int max_k = gemm == kGemmGateUp ? p->d_model
                                          : std::max(p->d_ff, p->has_shared ? p->d_ff_shared : 0);
-  return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k, stream, mfma, s);
+  return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k, stream, mfma, s, false);
 }
 }  // namespace
 
@@ -257,6 +267,8 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.config = p->config;
   a.num_cus = device_cus();
   a.fp8 = fp8;
+  a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
+  a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
   a.x = x_perm;
   a.xs = fp8 ? x_perm_scale : nullptr;
   a.tok = nullptr;
@@ -369,6 +381,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.config = p->config;
   a.num_cus = device_cus();
   a.fp8 = fp8;
+  a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
+  a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
   a.x = fp8 ? static_cast<const void*>(L.xq) : x;
   a.xs = L.xs;
   a.tok = L.tok;
@@ -384,7 +398,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   hipError_t e = mark(0);
   // a single bf16 token without a shared expert: routing runs inside the gate/up kernel, which
   // also writes the routing outputs and the down GEMM's segments (phases 1 to 4 are empty)
-  const bool decode1 = T == 1 && !fp8 && !p->has_shared && p->config != MOE_CONFIG_MFMA &&
+  const bool decode1 = T == 1 && p->wdtype == MOE_DTYPE_BF16 && !p->has_shared &&
+                       p->config != MOE_CONFIG_MFMA &&
                        d <= kStreamXlMaxK;
   if (decode1) {
     Decode1Args da;

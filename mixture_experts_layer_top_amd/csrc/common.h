@@ -70,6 +70,12 @@ __device__ __forceinline__ uint2 gload8(const void* base, uint32_t off) {
   const u32x2 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x2*>((gchar*)base + off);
   return __builtin_bit_cast(uint2, v);
 }
+__device__ __forceinline__ uint32_t gload4(const void* base, uint32_t off) {
+  return *reinterpret_cast<__attribute__((address_space(1))) const uint32_t*>((gchar*)base + off);
+}
+__device__ __forceinline__ uint32_t gload_u8(const uint8_t* p, uint32_t i) {
+  return reinterpret_cast<__attribute__((address_space(1))) const uint8_t*>((gchar*)p)[i];
+}
 __device__ __forceinline__ int32_t gload_i32(const int32_t* p, int i) {
   return reinterpret_cast<__attribute__((address_space(1))) const int32_t*>((gchar*)p)[i];
 }

@@ -40,6 +40,60 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // enough workgroups (T = 1, 8 experts: 1024 gate/up tiles), and each wavefront reads only its share
 // of the activations.  Loads are double-buffered in registers across unrolled batches of K-steps.
 // ------------------------------------------------------------------------------------------------
+// Split-K reduction and epilogue of a streaming tile: in each group of 16 weight rows, wavefronts
+// kw = 1..WK-1 park their partials in LDS and wavefront kw = 0 adds them in order (slots
+// grp * (WK - 1) + kw - 1, at most 3), then applies SwiGLU (gate/up) and stores bf16.  n0 is the
+// first column of the calling wavefront's group of 16.
+template <int MQ, bool GU, int WK>
+__device__ __forceinline__ void stream_tile_finish(const Seg& sg, int m0, int rows, int n0,
+                                                   float* red, f32x4 (&acc0)[MQ], f32x4 (&acc1)[MQ]) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int grp = wv / WK, kw = wv % WK;
+  const int N = sg.N;
+  constexpr int NV = MQ * 4 * (GU ? 2 : 1);  // floats per lane
+  if (WK > 1) __syncthreads();  // red[] may still be read by the previous tile
+  if (WK > 1 && kw > 0) {
+    float* dst = red + ((grp * (WK - 1) + kw - 1) * NV) * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < MQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[(q * 4 + i) * 64] = acc0[q][i];
+        if (GU) dst[(MQ * 4 + q * 4 + i) * 64] = acc1[q][i];
+      }
+  }
+  if (WK > 1) {
+    __syncthreads();
+    if (kw != 0) return;
+  }
+#pragma unroll
+  for (int w = 0; w < WK - 1; ++w) {
+    const float* src = red + ((grp * (WK - 1) + w) * NV) * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < MQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0[q][i] += src[(q * 4 + i) * 64];
+        if (GU) acc1[q][i] += src[(MQ * 4 + q * 4 + i) * 64];
+      }
+  }
+  // C[i][j]: i = weight row 4*kg + r, j = token r16 of group q
+#pragma unroll
+  for (int q = 0; q < MQ; ++q) {
+    const int r = q * 16 + r16;
+    if (r < rows) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = GU ? swiglu(acc0[q][i], acc1[q][i]) : acc0[q][i];
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      gstore8(sg.out, ((size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) * 2, pk);
+    }
+  }
+}
+
 // XL > 0: the tile has one row, whose activations (K bf16) the MFMA loop reads from LDS (xs): with
 // XL = 1 the tile stages them from xrow once its first weight loads are in flight, with XL = 2 the
 // caller has staged them.
@@ -49,7 +103,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
                                                  const void* xrow = nullptr) {
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
-  const int K = sg.K, N = sg.N;
+  const int K = sg.K;
   // WK wavefronts split K over each group of 16 weight rows; the 4 / WK groups are consecutive
   const int grp = wv / WK, kw = wv % WK;
   n0 += 16 * grp;
@@ -132,49 +186,111 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
   }
-  // split-K reduction: in each group, wavefronts kw = 1..WK-1 park their partials and wavefront
-  // kw = 0 adds them in order (slots grp * (WK - 1) + kw - 1, at most 3)
-  constexpr int NV = MQ * 4 * (GU ? 2 : 1);  // floats per lane
-  if (WK > 1) __syncthreads();  // red[] may still be read by the previous tile
-  if (WK > 1 && kw > 0) {
-    float* dst = red + ((grp * (WK - 1) + kw - 1) * NV) * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < MQ; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[(q * 4 + i) * 64] = acc0[q][i];
-        if (GU) dst[(MQ * 4 + q * 4 + i) * 64] = acc1[q][i];
-      }
-  }
-  if (WK > 1) {
-    __syncthreads();
-    if (kw != 0) return;
-  }
-#pragma unroll
-  for (int w = 0; w < WK - 1; ++w) {
-    const float* src = red + ((grp * (WK - 1) + w) * NV) * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < MQ; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc0[q][i] += src[(q * 4 + i) * 64];
-        if (GU) acc1[q][i] += src[(MQ * 4 + q * 4 + i) * 64];
-      }
-  }
-  // C[i][j]: i = weight row 4*kg + r, j = token r16 of group q
+  stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0, red, acc0, acc1);
+}
+
+// MXFP4 weights (W4A16): each weight row holds K/2 bytes of E2M1 pairs and K/32 E8M0 scales.  The
+// MFMA operands are the bf16 values e2m1 * 2^(X - 127), converted in registers (the scaled fp4 ->
+// bf16 conversion, two per instruction; exact, since every such product is a bf16 value), so the
+// tile is the bf16 streaming tile with a quarter of the weight bytes.  Inside a batch of U K-steps
+// each lane takes 8*U consecutive K values (8 per step), so its weights are one contiguous 4*U-byte
+// load and its scales whole blocks of 32; U = 8 for one token group keeps as many bytes in flight
+// per CU as the bf16 tile's four steps.  A step's K values per lane only have to agree between the
+// two operands, so the order differs from the bf16 tile's.  Leftover steps run one at a time.
+__device__ __forceinline__ uint4 decode_e2m1x8(uint32_t packed, uint32_t scale_code) {
+  const float sc = __builtin_bit_cast(float, scale_code << 23);  // 2^(X - 127), X >= 1
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 3));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+template <int MQ, bool GU, int WK>
+__device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, int n0, float* red) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int K = sg.K;
+  const int grp = wv / WK, kw = wv % WK;
+  n0 += 16 * grp;
+  const int nrow = n0 + r16;  // this lane's weight row (A operand)
+  const int k0 = kw * (K / WK);  // this wavefront's K range [k0, k0 + K/WK); K % 128 == 0
+  const uint32_t wrow = (uint32_t)nrow * (uint32_t)(K / 2);
+  const uint32_t srow = (uint32_t)nrow * (uint32_t)(K / 32);
+  uint32_t xrow[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
-    const int r = q * 16 + r16;
-    if (r < rows) {
-      float v[4];
+    int r = q * 16 + r16;
+    r = r < rows ? r : rows - 1;  // padded columns re-read a valid row; never stored
+    const int gr = sg.row0 + m0 + r;
+    const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
+    xrow[q] = (uint32_t)src * K * 2;
+  }
+  f32x4 acc0[MQ], acc1[MQ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = GU ? swiglu(acc0[q][i], acc1[q][i]) : acc0[q][i];
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      gstore8(sg.out, ((size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) * 2, pk);
+  for (int q = 0; q < MQ; ++q) {
+    acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  constexpr int U = (MQ == 1) ? 8 : 4;  // K-steps (of 32) per batch
+  constexpr int NW = U / 4;              // 16-byte weight loads (32 values, one scale) per batch
+  struct Batch { uint4 w0[NW], w1[NW]; uint32_t s0[NW], s1[NW]; uint4 b[U][MQ]; };
+  auto load = [&](Batch& bt, int ks) {
+    const uint32_t kl = (uint32_t)(k0 + 32 * ks + 8 * U * kg);  // this lane's first K
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      bt.w0[i] = gload16(sg.w0, wrow + kl / 2 + 16 * i);
+      bt.s0[i] = gload_u8(sg.e0, srow + kl / 32 + i);
+      if (GU) {
+        bt.w1[i] = gload16(sg.w1, wrow + kl / 2 + 16 * i);
+        bt.s1[i] = gload_u8(sg.e1, srow + kl / 32 + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(sg.a, xrow[q] + (kl + 8 * u) * 2);
+  };
+  auto compute = [&](const Batch& bt) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint4 a0 = decode_e2m1x8(dword_of(bt.w0[u >> 2], u & 3), bt.s0[u >> 2]);
+      const uint4 a1 = GU ? decode_e2m1x8(dword_of(bt.w1[u >> 2], u & 3), bt.s1[u >> 2]) : a0;
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) {
+        acc0[q] = mfma16(as_bf16x8(a0), as_bf16x8(bt.b[u][q]), acc0[q]);
+        if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(bt.b[u][q]), acc1[q]);
+      }
+    }
+  };
+  const int nsteps = K / WK / 32;     // K-steps of this wavefront (>= 1)
+  const int nfull = nsteps / U * U;   // pipelined part: whole batches only
+  Batch b0, b1;
+  if (nfull > 0) load(b0, 0);
+  for (int ks = 0; ks < nfull; ks += 2 * U) {
+    if (ks + U < nfull) load(b1, ks + U);
+    compute(b0);
+    if (ks + 2 * U < nfull) load(b0, ks + 2 * U);
+    if (ks + U < nfull) compute(b1);
+  }
+  for (int ks = nfull; ks < nsteps; ++ks) {  // remainder: lane kg takes K [32 ks + 8 kg, +8)
+    const uint32_t kl = (uint32_t)(k0 + 32 * ks + 8 * kg);
+    const uint32_t sb = srow + (uint32_t)(k0 + 32 * ks) / 32;
+    const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wrow + kl / 2), gload_u8(sg.e0, sb));
+    const uint4 a1 = GU ? decode_e2m1x8(gload4(sg.w1, wrow + kl / 2), gload_u8(sg.e1, sb)) : a0;
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) {
+      const uint4 b = gload16(sg.a, xrow[q] + kl * 2);
+      acc0[q] = mfma16(as_bf16x8(a0), as_bf16x8(b), acc0[q]);
+      if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
   }
+  stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0, red, acc0, acc1);
 }
 
 // Rows [m0, m0 + rows) of one tile, in passes of at most 16 * MQMAX rows.  The kernel's register
@@ -182,9 +298,20 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
 // rows (every expert holds at most T rows): at MQMAX = 1 four workgroups fit on each CU.
 // MQMAX = 0 (the host launches it when every expert holds at most one row, as at T = 1, and K <=
 // kStreamXlMaxK): rows one at a time, each staging its activations in LDS (xs) for the MFMA loop.
-template <bool GU, int WK, int MQMAX>
+template <bool GU, int WK, int MQMAX, bool W4>
 __device__ __forceinline__ void stream_rows_bf16(const Seg& sg, int m0, int rows, int n0,
                                                  float* red, const char* xs) {
+  static_assert(!(W4 && MQMAX == 0), "mxfp4 tiles do not stage a row in LDS");
+  if (W4) {
+    constexpr int MQ = MQMAX > 0 ? MQMAX : 1;
+    for (int sub = 0; sub < rows; sub += 16 * MQ) {
+      const int r = min(16 * MQ, rows - sub);
+      if (MQ == 1 || r <= 16) stream_tile_w4<1, GU, WK>(sg, m0 + sub, r, n0, red);
+      else if (MQ == 2 || r <= 32) stream_tile_w4<MQ >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red);
+      else stream_tile_w4<MQ, GU, WK>(sg, m0 + sub, r, n0, red);
+    }
+    return;
+  }
   if (MQMAX == 0) {
     if (sg.K > kStreamXlMaxK) return;  // (excluded by the host)
     for (int r = 0; r < rows; ++r) {
@@ -207,7 +334,7 @@ __device__ __forceinline__ void stream_rows_bf16(const Seg& sg, int m0, int rows
 // Persistent: workgroup b takes tile b first, then pops tiles gridDim.x, gridDim.x + 1, ... from
 // the list's queue counter (zeroed by the selection kernel), so a launch whose tiles all fit in
 // one round makes no atomic at all.  The segments' first tiles are staged in LDS once.
-template <bool GU, int MQMAX>
+template <bool GU, int MQMAX, bool W4 = false>
 __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ segs,
                                                          int32_t* __restrict__ meta) {
   constexpr int MQ = MQMAX > 0 ? MQMAX : 1;
@@ -229,8 +356,8 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
     const int m0 = mt * kStreamMaxRows;
     const int rows = min(kStreamMaxRows, sg.rows - m0);
     const int n0 = nt * sg.tn;
-    if (sg.tn == 16) stream_rows_bf16<GU, 4, MQMAX>(sg, m0, rows, n0, red, xs);  // long K: 4-way split
-    else stream_rows_bf16<GU, 2, MQMAX>(sg, m0, rows, n0, red, xs);  // 32 columns: wavefront pairs
+    if (sg.tn == 16) stream_rows_bf16<GU, 4, MQMAX, W4>(sg, m0, rows, n0, red, xs);  // long K: 4-way
+    else stream_rows_bf16<GU, 2, MQMAX, W4>(sg, m0, rows, n0, red, xs);  // 32 columns: pairs
     t = gridDim.x + __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
     if (t >= ntiles) break;
   }
@@ -986,6 +1113,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, Selec
     sg.w1 = nullptr;
     sg.s0 = nullptr;
     sg.s1 = nullptr;
+    sg.e0 = sg.e1 = nullptr;
     sg.out = a.y;
     sg.outs = nullptr;
     sg.row0 = r;
@@ -1019,6 +1147,7 @@ __global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, Selec
     sg.w1 = static_cast<const uint8_t*>(a.w_up) + (size_t)e * a.f * a.d * 2;
     sg.s0 = nullptr;
     sg.s1 = nullptr;
+    sg.e0 = sg.e1 = nullptr;
     sg.out = a.h;
     sg.outs = nullptr;
     sg.row0 = r;
@@ -1052,7 +1181,13 @@ hipError_t launch_decode1_bf16(const Decode1Args& a, const SelectOut& o, int num
 
 template <bool GU>
 static void launch_stream_bf16(const Seg* ss, int32_t* ms, int num_cus, int64_t max_rows,
-                               int max_k, hipStream_t s) {
+                               int max_k, hipStream_t s, bool w4) {
+  if (w4) {
+    if (max_rows <= 16) gemm_stream_bf16<GU, 1, true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    else if (max_rows <= 32) gemm_stream_bf16<GU, 2, true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    else gemm_stream_bf16<GU, 4, true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    return;
+  }
   if (GU && max_rows <= 1 && max_k <= kStreamXlMaxK)  // (down tiles are too short to gain)
     gemm_stream_bf16<GU, 0><<<num_cus * 4, 256, 0, s>>>(ss, ms);
   else if (max_rows <= 16) gemm_stream_bf16<GU, 1><<<num_cus * 4, 256, 0, s>>>(ss, ms);
@@ -1061,17 +1196,17 @@ static void launch_stream_bf16(const Seg* ss, int32_t* ms, int num_cus, int64_t 
 }
 
 hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, int64_t max_rows, int max_k,
-                             bool stream, bool mfma, hipStream_t s) {
+                             bool stream, bool mfma, hipStream_t s, bool w4) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
   int32_t* cnt = o.split_cnt ? o.split_cnt + g * kSplitMaxPieces : nullptr;
   if (g == kGemmGateUp) {
-    if (stream) launch_stream_bf16<true>(ss, ms, num_cus, max_rows, max_k, s);
+    if (stream) launch_stream_bf16<true>(ss, ms, num_cus, max_rows, max_k, s, w4);
     if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   } else {
-    if (stream) launch_stream_bf16<false>(ss, ms, num_cus, max_rows, max_k, s);
+    if (stream) launch_stream_bf16<false>(ss, ms, num_cus, max_rows, max_k, s, w4);
     if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
   }
   return hipGetLastError();

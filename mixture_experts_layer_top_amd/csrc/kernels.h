@@ -53,6 +53,8 @@ struct Seg {
   const void* w1;       // up weights (gate/up GEMM), [N][K]
   const float* s0;      // fp8 block scales of w0, [N/128][K/128]
   const float* s1;      // fp8 block scales of w1
+  const uint8_t* e0;    // mxfp4: E8M0 scales of w0, [N][K/32] (w0 then holds [N][K/2] bytes)
+  const uint8_t* e1;    // mxfp4: E8M0 scales of w1
   void* out;            // output base [.][N] (bf16, or e4m3 for the fp8 gate/up GEMM)
   float* outs;          // fp8 gate/up: output scales [.][N/128]
   int32_t row0, rows, N, K;
@@ -93,6 +95,8 @@ struct SelectArgs {
   const int32_t* counts;   // [E]
   const int32_t* offsets;  // [E + 1]
   int E, T, k, d, f, f_sh, has_shared, config, fp8;
+  int w4;                  // mxfp4 expert weights (streaming tiles, bf16 activations)
+  const uint8_t* e_gate; const uint8_t* e_up; const uint8_t* e_down;  // their E8M0 scales
   int num_cus;              // compute units of the device (one MFMA-tile round)
   const void* x;           // gate/up activations (bf16 x, or e4m3 xq)
   const float* xs;         // fp8 activation scales
@@ -139,8 +143,9 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
 // Launches the persistent kernel of each tile family of one GEMM (kGemmGateUp or kGemmDown) that
 // may hold tiles (the other's queue is empty).  max_rows bounds the rows of any one expert, max_k
 // the GEMM's K over all its segments.
+// w4: mxfp4 weights (streaming tiles only; mfma must be false)
 hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
-                             int max_k, bool stream, bool mfma, hipStream_t s);
+                             int max_k, bool stream, bool mfma, hipStream_t s, bool w4);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
 
 // Single-token decode (T = 1, bf16 weights, no shared expert, d <= kStreamXlMaxK): one kernel routes

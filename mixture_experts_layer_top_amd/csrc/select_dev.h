@@ -54,7 +54,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   const int ffe = shared ? a.f_sh : a.f;
   int fm[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8) : -1;
+  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8 || a.w4) : -1;
   // The down GEMM's light experts (<= kStreamRowsDown rows) take the streaming tiles only while its
   // heavier experts' MFMA tiles fill less than one round of CUs; with a round or more they join the
   // MFMA list, where their short tiles fill the rounds' gaps instead of running as a second launch
@@ -71,7 +71,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   // longest first (below one round every tile starts at once and order does not matter); else XCD
   // chunks when K >= kLongK and some expert spans several m-tiles.
   bool lpt[2] = {false, false}, chunks[2] = {false, false};
-  if (!a.fp8) {
+  if (!a.fp8 && !a.w4) {
     // w[0..1]: MFMA tiles per GEMM; w[2..3]: MFMA experts of more than one m-tile per GEMM;
     // w[4..5]: MFMA experts of more than kFewTileRows rows per GEMM; w[6]: down tiles of the light
     // experts the threshold put on the streaming tiles (w[7] unused)
@@ -186,12 +186,16 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       if (shared) {
         sg.w0 = a.sh_gate;
         sg.w1 = a.sh_up;
+        sg.e0 = sg.e1 = nullptr;
         sg.s0 = a.s_sh_gate;
         sg.s1 = a.s_sh_up;
         sg.out = a.h_sh;
         sg.outs = a.hs_sh;
       } else {
-        const size_t wo = (size_t)e * ffe * a.d * wb;
+        const size_t wo = a.w4 ? (size_t)e * ffe * (a.d / 2) : (size_t)e * ffe * a.d * wb;
+        const size_t eo = (size_t)e * ffe * (a.d / 32);
+        sg.e0 = a.e_gate ? a.e_gate + eo : nullptr;
+        sg.e1 = a.e_up ? a.e_up + eo : nullptr;
         const size_t so = (size_t)e * kb_f * kb_d;
         sg.w0 = static_cast<const uint8_t*>(a.w_gate) + wo;
         sg.w1 = static_cast<const uint8_t*>(a.w_up) + wo;
@@ -207,17 +211,21 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       sg.tok = nullptr;
       sg.w1 = nullptr;
       sg.s1 = nullptr;
+      sg.e1 = nullptr;
       sg.outs = nullptr;
       if (shared) {
         sg.a = a.h_sh;
         sg.as = a.hs_sh;
         sg.w0 = a.sh_down;
+        sg.e0 = nullptr;
         sg.s0 = a.s_sh_down;
         sg.out = a.y_sh;
       } else {
         sg.a = a.h;
         sg.as = a.hs;
-        sg.w0 = static_cast<const uint8_t*>(a.w_down) + (size_t)e * a.d * ffe * wb;
+        sg.w0 = static_cast<const uint8_t*>(a.w_down) +
+                (a.w4 ? (size_t)e * a.d * (ffe / 2) : (size_t)e * a.d * ffe * wb);
+        sg.e0 = a.e_down ? a.e_down + (size_t)e * a.d * (ffe / 32) : nullptr;
         sg.s0 = a.s_down ? a.s_down + (size_t)e * kb_d * kb_f : nullptr;
         sg.out = a.y;
       }

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-DTYPE_BF16, DTYPE_FP8 = 0, 1
+DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4 = 0, 1, 2
 CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -33,7 +33,8 @@ class Problem(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-        "sh_gate", "sh_up", "sh_down", "s_sh_gate", "s_sh_up", "s_sh_down")]
+        "sh_gate", "sh_up", "sh_down", "s_sh_gate", "s_sh_up", "s_sh_down",
+        "e_gate", "e_up", "e_down")]
 
 
 class Routing(ctypes.Structure):
@@ -121,6 +122,9 @@ class ExpertWeights:
     s_sh_gate: torch.Tensor | None = None
     s_sh_up: torch.Tensor | None = None
     s_sh_down: torch.Tensor | None = None
+    e_gate: torch.Tensor | None = None  # mxfp4: uint8 E8M0 scales [E, f, d/32] / [E, d, f/32]
+    e_up: torch.Tensor | None = None
+    e_down: torch.Tensor | None = None
 
     def struct(self) -> Weights:
         w = Weights()
@@ -130,17 +134,29 @@ class ExpertWeights:
         return w
 
     @property
+    def wdtype(self) -> int:
+        if self.e_gate is not None:
+            return DTYPE_MXFP4
+        return DTYPE_FP8 if self.gate.dtype == torch.uint8 else DTYPE_BF16
+
+    @property
     def fp8(self) -> bool:
-        return self.gate.dtype == torch.uint8
+        return self.wdtype == DTYPE_FP8
+
+    @property
+    def d_model(self) -> int:
+        """d from the gate weights' last dim (two mxfp4 elements per byte)."""
+        return self.gate.shape[2] * (2 if self.wdtype == DTYPE_MXFP4 else 1)
 
     @property
     def has_shared(self) -> bool:
         return self.sh_gate is not None
 
 
-def problem(T, d, f, E, k, fp8=False, shared_f=0, config=CONFIG_AUTO) -> Problem:
-    return Problem(T, d, f, E, k, DTYPE_FP8 if fp8 else DTYPE_BF16, 1 if shared_f else 0,
-                   shared_f, config)
+def problem(T, d, f, E, k, fp8=False, shared_f=0, config=CONFIG_AUTO, wdtype=None) -> Problem:
+    if wdtype is None:
+        wdtype = DTYPE_FP8 if fp8 else DTYPE_BF16
+    return Problem(T, d, f, E, k, wdtype, 1 if shared_f else 0, shared_f, config)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -197,7 +213,7 @@ def grouped_ffn(x_perm, x_perm_scale, counts, offsets, weights: ExpertWeights, T
     n, d = x_perm.shape
     E = counts.shape[0]
     f = weights.gate.shape[1]
-    p = problem(T, d, f, E, k, fp8=weights.fp8, config=config)
+    p = problem(T, d, f, E, k, config=config, wdtype=weights.wdtype)
     dev = _dev(x_perm)
     y = torch.empty((n, d), dtype=torch.int16, device=dev)
     ws = torch.empty(max(1, lib().moe_grouped_ffn_workspace_bytes(ctypes.byref(p))),
@@ -223,11 +239,11 @@ class Layer:
 
     def __init__(self, weights: ExpertWeights, T: int, E: int, k: int, config: int = CONFIG_AUTO,
                  device=None):
-        d = weights.gate.shape[2]
+        d = weights.d_model
         f = weights.gate.shape[1]
         shf = weights.sh_gate.shape[0] if weights.has_shared else 0
         self.weights = weights
-        self.p = problem(T, d, f, E, k, fp8=weights.fp8, shared_f=shf, config=config)
+        self.p = problem(T, d, f, E, k, shared_f=shf, config=config, wdtype=weights.wdtype)
         self.w = weights.struct()
         dev = device if device is not None else weights.gate.device
         self.ws = torch.empty(max(1, lib().moe_layer_workspace_bytes(ctypes.byref(self.p))),

@@ -34,6 +34,8 @@ class Inputs:
         kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
         if self.p.wdtype == I.WDT_FP8:
             kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
+        if self.p.wdtype == I.WDT_MXFP4:
+            kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
         if self.p.shared:
             kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
             if self.p.wdtype == I.WDT_FP8:
@@ -46,7 +48,7 @@ class Inputs:
     def get(self, e):
         if e not in self._cache:
             r = {n: self.W[n][e].cpu().numpy() for n in ("gate", "up", "down")}
-            if self.p.wdtype == I.WDT_FP8:
+            if self.p.wdtype in (I.WDT_FP8, I.WDT_MXFP4):
                 r.update({"s_" + n: self.W["s_" + n][e].cpu().numpy() for n in ("gate", "up", "down")})
             if len(self._cache) > 24:
                 self._cache.clear()

@@ -113,3 +113,8 @@ def test_kimi_prefill_full(moe):
 @pytest.mark.parametrize("T", I.FP8_TS)
 def test_fp8_decode_full(moe, T):
     _check_full(moe, Inputs(I.fp8_point(T)), n_sample=2, tol=FP8_TOL, seed=T)
+
+
+def test_mxfp4_decode_full(moe):
+    """DeepSeek-V3-shaped layer with MXFP4 experts at T = 64 (bf16 activations)."""
+    _check_full(moe, Inputs(I.MXFP4), n_sample=2, tol=BF16_TOL, seed=64)

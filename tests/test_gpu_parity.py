@@ -371,3 +371,49 @@ def test_fp8_grouped_ffn_matches_oracle(moe):
                         inp.expert_weights(), p.T, p.k)
     ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, None, act_fp8=True)["y_perm"]
     assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# MXFP4 experts (E2M1 pairs with E8M0 scales per 32; bf16 activations; streaming tiles only).  The
+# tile converts the weights to bf16 exactly, so the bar is the bf16 one.  K-loop cases: K / WK / 32
+# steps per wavefront against batches of 8 (one token group) or 4 steps: remainder only (d = 256,
+# 384), whole batches plus a remainder (d = 384 at 4-step batches), an even (d = 4096) and an odd
+# (d = 1536) number of pipelined batches; one token (the general path: the single-token kernel is
+# bf16 only); three token-group widths (T = 64 and 300 reach passes of 33-64 rows).
+# ------------------------------------------------------------------------------------------------
+
+MXFP4_SMALL = [
+    I.Problem("mx_tiny", 120, T=64, d=256, f=512, E=8, k=2, wdtype=I.WDT_MXFP4),
+    I.Problem("mx_ragged", 121, T=300, d=384, f=640, E=6, k=2, wdtype=I.WDT_MXFP4),
+    I.Problem("mx_long_k", 122, T=40, d=4096, f=1024, E=16, k=4, routing="dirichlet", alpha=1.0,
+              wdtype=I.WDT_MXFP4),
+    I.Problem("mx_odd_batches", 123, T=24, d=1536, f=256, E=8, k=2, wdtype=I.WDT_MXFP4),
+    I.Problem("mx_T1", 124, T=1, d=1024, f=512, E=32, k=4, routing="dirichlet", alpha=1.0,
+              wdtype=I.WDT_MXFP4),
+]
+
+
+@pytest.mark.parametrize("config", [-1, 0])
+@pytest.mark.parametrize("p", MXFP4_SMALL, ids=lambda p: p.name)
+def test_mxfp4_layer_matches_oracle(moe, p, config):
+    _check_layer(moe, Inputs(p), config=config, tol=BF16_TOL, runs=2)
+
+
+def test_mxfp4_grouped_ffn_matches_oracle(moe):
+    p = MXFP4_SMALL[2]
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    x_perm = torch.from_numpy(np.ascontiguousarray(inp.x[perm_src // p.k]).view(np.int16)).cuda()
+    y = moe.grouped_ffn(x_perm, None, torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get)["y_perm"]
+    assert rel_err(bits_to_f64(y), ref) <= BF16_TOL
+
+
+def test_mxfp4_rejects_mfma_config(moe):
+    inp = Inputs(MXFP4_SMALL[0])
+    with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
+        moe.Layer(inp.expert_weights(), inp.p.T, inp.p.E, inp.p.k, config=1)(inp.d_logits, inp.d_x)
