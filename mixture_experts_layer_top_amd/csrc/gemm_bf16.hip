@@ -197,6 +197,9 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
 // load and its scales whole blocks of 32; U = 8 for one token group keeps as many bytes in flight
 // per CU as the bf16 tile's four steps.  A step's K values per lane only have to agree between the
 // two operands, so the order differs from the bf16 tile's.  Leftover steps run one at a time.
+// Each wavefront group covers NR = 2 sets of 16 weight rows against the same activation fragments
+// (the tile is twice the bf16 tile's width): activations are bf16, four times the bytes of the
+// weights per K, and they are re-read from L2 once per 16 weight rows.
 __device__ __forceinline__ uint4 decode_e2m1x8(uint32_t packed, uint32_t scale_code) {
   const float sc = __builtin_bit_cast(float, scale_code << 23);  // 2^(X - 127), X >= 1
   uint4 r;
@@ -213,15 +216,20 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int j) {
 
 template <int MQ, bool GU, int WK>
 __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, int n0, float* red) {
+  constexpr int NR = 2;  // sets of 16 weight rows per wavefront group
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K;
   const int grp = wv / WK, kw = wv % WK;
-  n0 += 16 * grp;
-  const int nrow = n0 + r16;  // this lane's weight row (A operand)
+  n0 += 16 * NR * grp;
   const int k0 = kw * (K / WK);  // this wavefront's K range [k0, k0 + K/WK); K % 128 == 0
-  const uint32_t wrow = (uint32_t)nrow * (uint32_t)(K / 2);
-  const uint32_t srow = (uint32_t)nrow * (uint32_t)(K / 32);
+  uint32_t wrow[NR], srow[NR];
+#pragma unroll
+  for (int h = 0; h < NR; ++h) {
+    const int nrow = n0 + 16 * h + r16;  // this lane's weight rows (A operands)
+    wrow[h] = (uint32_t)nrow * (uint32_t)(K / 2);
+    srow[h] = (uint32_t)nrow * (uint32_t)(K / 32);
+  }
   uint32_t xrow[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
@@ -231,26 +239,30 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
     const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
     xrow[q] = (uint32_t)src * K * 2;
   }
-  f32x4 acc0[MQ], acc1[MQ];
+  f32x4 acc0[NR][MQ], acc1[NR][MQ];
 #pragma unroll
-  for (int q = 0; q < MQ; ++q) {
-    acc0[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int h = 0; h < NR; ++h)
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) {
+      acc0[h][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[h][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   constexpr int U = (MQ == 1) ? 8 : 4;  // K-steps (of 32) per batch
   constexpr int NW = U / 4;              // 16-byte weight loads (32 values, one scale) per batch
-  struct Batch { uint4 w0[NW], w1[NW]; uint32_t s0[NW], s1[NW]; uint4 b[U][MQ]; };
+  struct Batch { uint4 w0[NR][NW], w1[NR][NW]; uint32_t s0[NR][NW], s1[NR][NW]; uint4 b[U][MQ]; };
   auto load = [&](Batch& bt, int ks) {
     const uint32_t kl = (uint32_t)(k0 + 32 * ks + 8 * U * kg);  // this lane's first K
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      bt.w0[i] = gload16(sg.w0, wrow + kl / 2 + 16 * i);
-      bt.s0[i] = gload_u8(sg.e0, srow + kl / 32 + i);
-      if (GU) {
-        bt.w1[i] = gload16(sg.w1, wrow + kl / 2 + 16 * i);
-        bt.s1[i] = gload_u8(sg.e1, srow + kl / 32 + i);
+    for (int h = 0; h < NR; ++h)
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        bt.w0[h][i] = gload16(sg.w0, wrow[h] + kl / 2 + 16 * i);
+        bt.s0[h][i] = gload_u8(sg.e0, srow[h] + kl / 32 + i);
+        if (GU) {
+          bt.w1[h][i] = gload16(sg.w1, wrow[h] + kl / 2 + 16 * i);
+          bt.s1[h][i] = gload_u8(sg.e1, srow[h] + kl / 32 + i);
+        }
       }
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -258,15 +270,18 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
   };
   auto compute = [&](const Batch& bt) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint4 a0 = decode_e2m1x8(dword_of(bt.w0[u >> 2], u & 3), bt.s0[u >> 2]);
-      const uint4 a1 = GU ? decode_e2m1x8(dword_of(bt.w1[u >> 2], u & 3), bt.s1[u >> 2]) : a0;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) {
-        acc0[q] = mfma16(as_bf16x8(a0), as_bf16x8(bt.b[u][q]), acc0[q]);
-        if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(bt.b[u][q]), acc1[q]);
+      for (int h = 0; h < NR; ++h) {
+        const uint4 a0 = decode_e2m1x8(dword_of(bt.w0[h][u >> 2], u & 3), bt.s0[h][u >> 2]);
+        const uint4 a1 =
+            GU ? decode_e2m1x8(dword_of(bt.w1[h][u >> 2], u & 3), bt.s1[h][u >> 2]) : a0;
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) {
+          acc0[h][q] = mfma16(as_bf16x8(a0), as_bf16x8(bt.b[u][q]), acc0[h][q]);
+          if (GU) acc1[h][q] = mfma16(as_bf16x8(a1), as_bf16x8(bt.b[u][q]), acc1[h][q]);
+        }
       }
-    }
   };
   const int nsteps = K / WK / 32;     // K-steps of this wavefront (>= 1)
   const int nfull = nsteps / U * U;   // pipelined part: whole batches only
@@ -280,17 +295,26 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
   }
   for (int ks = nfull; ks < nsteps; ++ks) {  // remainder: lane kg takes K [32 ks + 8 kg, +8)
     const uint32_t kl = (uint32_t)(k0 + 32 * ks + 8 * kg);
-    const uint32_t sb = srow + (uint32_t)(k0 + 32 * ks) / 32;
-    const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wrow + kl / 2), gload_u8(sg.e0, sb));
-    const uint4 a1 = GU ? decode_e2m1x8(gload4(sg.w1, wrow + kl / 2), gload_u8(sg.e1, sb)) : a0;
+    uint4 b[MQ];
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) {
-      const uint4 b = gload16(sg.a, xrow[q] + kl * 2);
-      acc0[q] = mfma16(as_bf16x8(a0), as_bf16x8(b), acc0[q]);
-      if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
+    for (int q = 0; q < MQ; ++q) b[q] = gload16(sg.a, xrow[q] + kl * 2);
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+      const uint32_t sb = srow[h] + (uint32_t)(k0 + 32 * ks) / 32;
+      const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wrow[h] + kl / 2), gload_u8(sg.e0, sb));
+      const uint4 a1 =
+          GU ? decode_e2m1x8(gload4(sg.w1, wrow[h] + kl / 2), gload_u8(sg.e1, sb)) : a0;
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) {
+        acc0[h][q] = mfma16(as_bf16x8(a0), as_bf16x8(b[q]), acc0[h][q]);
+        if (GU) acc1[h][q] = mfma16(as_bf16x8(a1), as_bf16x8(b[q]), acc1[h][q]);
+      }
     }
   }
-  stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0, red, acc0, acc1);
+  // one reduction and epilogue per set of 16 rows (each ends with every wavefront past its barriers)
+#pragma unroll
+  for (int h = 0; h < NR; ++h)
+    stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0 + 16 * h, red, acc0[h], acc1[h]);
 }
 
 // Rows [m0, m0 + rows) of one tile, in passes of at most 16 * MQMAX rows.  The kernel's register
@@ -356,8 +380,10 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
     const int m0 = mt * kStreamMaxRows;
     const int rows = min(kStreamMaxRows, sg.rows - m0);
     const int n0 = nt * sg.tn;
-    if (sg.tn == 16) stream_rows_bf16<GU, 4, MQMAX, W4>(sg, m0, rows, n0, red, xs);  // long K: 4-way
-    else stream_rows_bf16<GU, 2, MQMAX, W4>(sg, m0, rows, n0, red, xs);  // 32 columns: pairs
+    // long K: 16 columns per wavefront group, 4-way split in K; else 32 columns, wavefront pairs
+    // (mxfp4 tiles are twice as wide)
+    if ((W4 ? sg.tn / 2 : sg.tn) == 16) stream_rows_bf16<GU, 4, MQMAX, W4>(sg, m0, rows, n0, red, xs);
+    else stream_rows_bf16<GU, 2, MQMAX, W4>(sg, m0, rows, n0, red, xs);
     t = gridDim.x + __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
     if (t >= ntiles) break;
   }

@@ -126,10 +126,11 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       const bool st = fam[j] == kFamStream;
       const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
       if (g == kGemmGateUp) {
-        tn[j] = a.fp8 ? kStream8BNGateUp : st ? stream_bn(a.d) : kMfmaBNGateUp;
+        tn[j] = a.fp8 ? kStream8BNGateUp
+                      : st ? (a.w4 ? 2 : 1) * stream_bn(a.d) : kMfmaBNGateUp;
         nt[j] = ffe / tn[j];  // f is a multiple of 128
       } else {
-        tn[j] = a.fp8 ? kStream8BNDown : st ? stream_bn(ffe) : kMfmaBNDown;
+        tn[j] = a.fp8 ? kStream8BNDown : st ? (a.w4 ? 2 : 1) * stream_bn(ffe) : kMfmaBNDown;
         // (a down tile of 256 columns may be half full at the edge)
         nt[j] = (a.d + tn[j] - 1) / tn[j];
       }
