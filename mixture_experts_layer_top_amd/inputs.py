@@ -323,8 +323,10 @@ def hashed_e2m1_bytes(key: tuple[int, int], nbytes: int, device, start: int = 0)
 
 def hashed_e8m0_scales(key: tuple[int, int], n: int, device):
     """n E8M0 scale codes, uniform over 120..124 (2^-7 ... 2^-3)."""
+    import torch
+
     h = hash_stream(key, 0, n, device)
-    return (120 + (h >> 8) % 5).to(__import__("torch").uint8)
+    return (120 + (h >> 8) % 5).to(torch.uint8)
 
 
 def hashed_block_scales(key: tuple[int, int], n: int, device):

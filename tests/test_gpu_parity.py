@@ -283,13 +283,15 @@ def test_mfma_order_modes(moe):
 
 
 def test_generator_device_independent(moe):
-    for p, which, e in ((I.TINY, "gate", 3), (I.DSV3, "down", 200), (I.FP8, "up", 7)):
+    for p, which, e in ((I.TINY, "gate", 3), (I.DSV3, "down", 200), (I.FP8, "up", 7),
+                        (I.MXFP4, "gate", 11)):
         a = I.gen_expert_weight(p, which, e, "cpu")
         b = I.gen_expert_weight(p, which, e, "cuda").cpu()
         assert torch.equal(a, b)
-    a = I.gen_expert_scales(I.FP8, "down", 5, "cpu")
-    b = I.gen_expert_scales(I.FP8, "down", 5, "cuda").cpu()
-    assert torch.equal(a, b)
+    for p, which, e in ((I.FP8, "down", 5), (I.MXFP4, "down", 9)):
+        a = I.gen_expert_scales(p, which, e, "cpu")
+        b = I.gen_expert_scales(p, which, e, "cuda").cpu()
+        assert torch.equal(a, b)
 
 
 def test_t0_is_noop(moe):
