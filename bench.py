@@ -313,7 +313,8 @@ def main() -> int:
     kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
     if p.wdtype == "fp8":
         kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
-    if p.wdtype == "mxfp4":
+    if p.wdtype == "mxfp4":  # the library's tiled weight layout (made once, untimed)
+        kw.update({n: moe.mxfp4_tile(W[n]) for n in ("gate", "up", "down")})
         kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
     if p.shared:
         kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])

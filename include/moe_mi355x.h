@@ -32,7 +32,9 @@
  *     [E][d_ff][d_model/2], w_down [E][d_model][d_ff/2] bytes, with one E8M0 scale byte X per 32
  *     elements along the contraction dimension: e_gate, e_up [E][d_ff][d_model/32], e_down
  *     [E][d_model][d_ff/32]; the weight's value is e2m1(code) * 2^(X - 127).  Scales must lie in
- *     [2, 252] (not checked), which keeps every scaled weight an exact bf16 value.
+ *     [2, 252] (not checked), which keeps every scaled weight an exact bf16 value.  The weight
+ *     bytes are passed in the library's tiled layout, made once by moe_mxfp4_tile from the
+ *     row-major one; the scales stay row-major.
  *   - Return value: MOE_OK or an error code; moe_status_string() names it.  Arguments are checked
  *     on the host only (null pointers, sizes, 16-byte alignment, workspace size).  Device data is
  *     not validated: non-finite logits or out-of-range expert ids are undefined behaviour.
@@ -156,6 +158,16 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
                     const int32_t* counts, const int32_t* offsets, const moe_weights* w,
                     void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t moe_grouped_ffn_workspace_bytes(const moe_problem* p);
+
+/* MXFP4 weight layout for the library (load time): src holds a row-major matrix of rows x cols
+ * E2M1 elements ([rows][cols/2] bytes, element 2j in the low nibble of byte j; stacked experts
+ * [E][N][K] are rows = E*N); dst (same size, not overlapping src) receives the tiled layout the
+ * expert GEMMs read: per 16-row block and 128-element chunk of a row, 1 KB ordered
+ * [g 0..3][row 0..15][16 bytes = elements 32 g .. 32 g + 31 of the chunk], blocks in row-block
+ * then chunk order.  rows % 16 == 0 and cols % 128 == 0, else MOE_ERR_UNSUPPORTED; NULL or
+ * misaligned (16 bytes) pointers give MOE_ERR_INVALID_ARG.  (GC-MoE, summary: FP4 grouped GEMM;
+ * the layout is this library's, so that each wavefront load reads 1 KB contiguously.) */
+int moe_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 
 /* Combine: out[t] = bf16( sum_{j<k} topk_w[t][j] * y_perm[slot_dst[t*k+j]] (+ shared_y[t]) ),
  * the sum in fp32 in increasing j, the shared row (if not NULL) added last.

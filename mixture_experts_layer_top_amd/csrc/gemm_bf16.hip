@@ -189,12 +189,16 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
   stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0, red, acc0, acc1);
 }
 
-// MXFP4 weights (W4A16): each weight row holds K/2 bytes of E2M1 pairs and K/32 E8M0 scales.  The
+// MXFP4 weights (W4A16), in the library's tiled layout (moe_mxfp4_tile): per 16-row block and
+// 128-value chunk of K, 1 KB ordered [lane group kg][row r][16 bytes = values 32 kg .. 32 kg + 31
+// of the chunk], so lane kg * 16 + r of a wavefront reads bytes [16 lane, +16) of the chunk and one
+// load instruction reads 1 KB contiguously; E8M0 scales stay row-major [N][K/32].  The
 // MFMA operands are the bf16 values e2m1 * 2^(X - 127), converted in registers (the scaled fp4 ->
 // bf16 conversion, two per instruction; exact, since every such product is a bf16 value), so the
 // tile is the bf16 streaming tile with a quarter of the weight bytes.  Inside a batch of U K-steps
-// each lane takes 8*U consecutive K values (8 per step), so its weights are one contiguous 4*U-byte
-// load and its scales whole blocks of 32; U = 8 for one token group keeps as many bytes in flight
+// each lane takes U/4 pieces of 32 consecutive K values (piece i: chunk 2 c + i for U = 8, 8 values
+// per step), so its weights are U/4 16-byte loads from the tiled layout and its scales whole blocks
+// of 32; U = 8 for one token group keeps as many bytes in flight
 // per CU as the bf16 tile's four steps.  A step's K values per lane only have to agree between the
 // two operands, so the order differs from the bf16 tile's.  Leftover steps run one at a time.
 // Each wavefront group covers NR = 2 sets of 16 weight rows against the same activation fragments
@@ -225,12 +229,11 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
   const int K = sg.K;
   const int grp = wv / WK, kw = wv % WK;
   n0 += 16 * NR * grp;
-  uint32_t wrow[NR], srow[NR];
+  uint32_t wblk[NR], srow[NR];  // byte offsets of each 16-row block; this lane's scale rows
 #pragma unroll
   for (int h = 0; h < NR; ++h) {
-    const int nrow = n0 + 16 * h + r16;  // this lane's weight rows (A operands)
-    wrow[h] = (uint32_t)nrow * (uint32_t)(K / 2);
-    srow[h] = (uint32_t)nrow * (uint32_t)(K / 32);
+    wblk[h] = (uint32_t)(n0 + 16 * h) * (uint32_t)(K / 2);
+    srow[h] = (uint32_t)(n0 + 16 * h + r16) * (uint32_t)(K / 32);
   }
   uint32_t xrow[MQ];
 #pragma unroll
@@ -258,22 +261,27 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
   const int rsteps = (K - kr0) / 32 / WK;
   const int kr = kr0 + kw * rsteps * 32;
   auto load = [&](Batch& bt, int j) {
-    const uint32_t kl = (uint32_t)((j * WK + kw) * CK + 8 * U * kg);  // this lane's first K
+    const uint32_t c0 = (uint32_t)(j * WK + kw) * NW;  // first 128-value chunk of this batch
 #pragma unroll
     for (int h = 0; h < NR; ++h)
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        bt.w0[h][i] = gload16(sg.w0, wrow[h] + kl / 2 + 16 * i);
-        bt.s0[h][i] = gload_u8(sg.e0, srow[h] + kl / 32 + i);
+        const uint32_t wo = wblk[h] + (c0 + i) * 1024 + lane * 16;
+        const uint32_t so = srow[h] + (c0 + i) * 4 + kg;
+        bt.w0[h][i] = gload16(sg.w0, wo);
+        bt.s0[h][i] = gload_u8(sg.e0, so);
         if (GU) {
-          bt.w1[h][i] = gload16(sg.w1, wrow[h] + kl / 2 + 16 * i);
-          bt.s1[h][i] = gload_u8(sg.e1, srow[h] + kl / 32 + i);
+          bt.w1[h][i] = gload16(sg.w1, wo);
+          bt.s1[h][i] = gload_u8(sg.e1, so);
         }
       }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      // step u: piece u / 4, values 32 kg + 8 (u % 4) .. + 8 of its chunk
+      const uint32_t kx = (c0 + (u >> 2)) * 128 + 32 * kg + 8 * (u & 3);
 #pragma unroll
-      for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(sg.a, xrow[q] + (kl + 8 * u) * 2);
+      for (int q = 0; q < MQ; ++q) bt.b[u][q] = gload16(sg.a, xrow[q] + kx * 2);
+    }
   };
   auto compute = [&](const Batch& bt) {
 #pragma unroll
@@ -298,17 +306,19 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
     if (j + 2 < nchunk) load(b0, j + 2);
     if (j + 1 < nchunk) compute(b1);
   }
-  for (int ks = 0; ks < rsteps; ++ks) {  // remainder: lane kg takes K [kr + 32 ks + 8 kg, +8)
-    const uint32_t kl = (uint32_t)(kr + 32 * ks + 8 * kg);
+  for (int ks = 0; ks < rsteps; ++ks) {  // remainder: lane kg takes K [32 st + 8 kg, +8)
+    const uint32_t st = (uint32_t)(kr / 32 + ks);  // global 32-step: chunk st / 4, slot st % 4
+    const uint32_t kl = 32 * st + 8 * kg;
+    const uint32_t wo = (st >> 2) * 1024 + ((st & 3) * 16 + r16) * 16 + 4 * kg;
     uint4 b[MQ];
 #pragma unroll
     for (int q = 0; q < MQ; ++q) b[q] = gload16(sg.a, xrow[q] + kl * 2);
 #pragma unroll
     for (int h = 0; h < NR; ++h) {
-      const uint32_t sb = srow[h] + (uint32_t)(kr + 32 * ks) / 32;
-      const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wrow[h] + kl / 2), gload_u8(sg.e0, sb));
+      const uint32_t sb = srow[h] + st;
+      const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wblk[h] + wo), gload_u8(sg.e0, sb));
       const uint4 a1 =
-          GU ? decode_e2m1x8(gload4(sg.w1, wrow[h] + kl / 2), gload_u8(sg.e1, sb)) : a0;
+          GU ? decode_e2m1x8(gload4(sg.w1, wblk[h] + wo), gload_u8(sg.e1, sb)) : a0;
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
         acc0[h][q] = mfma16(as_bf16x8(a0), as_bf16x8(b[q]), acc0[h][q]);
@@ -1198,6 +1208,34 @@ template <int VPL>
 static void launch_decode1_vpl(const Decode1Args& a, const SelectOut& o, int g, hipStream_t s) {
   if (stream_bn(a.d) == 16) decode1_gate_up_bf16<VPL, 4><<<g, 256, 0, s>>>(a, o);
   else decode1_gate_up_bf16<VPL, 2><<<g, 256, 0, s>>>(a, o);
+}
+
+// Row-major MXFP4 bytes [rows][cols/2] -> the tiled layout the MXFP4 tiles read (one 16-byte
+// unit per thread: unit u of block (rows / 16, cols / 128) holds row 16 nb + (u % 16), values
+// 128 c + 32 (u / 16 % 4) .. + 31).
+__global__ __launch_bounds__(256) void mxfp4_tile_kernel(const uint8_t* __restrict__ src,
+                                                         uint8_t* __restrict__ dst, int64_t rows,
+                                                         int64_t cols) {
+  const int64_t nchunk = cols / 128;
+  const int64_t units = rows / 16 * nchunk * 64;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < units;
+       t += (int64_t)gridDim.x * 256) {
+    const int64_t blk = t / 64, l = t % 64;     // blk = nb * nchunk + c
+    const int64_t nb = blk / nchunk, c = blk % nchunk;
+    const int64_t row = nb * 16 + (l & 15), kg = l >> 4;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + row * (cols / 2) + c * 64 + kg * 16);
+    *reinterpret_cast<uint4*>(dst + t * 16) = v;
+  }
+}
+
+hipError_t launch_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols,
+                             hipStream_t s) {
+  const int64_t units = rows / 16 * (cols / 128) * 64;
+  const int64_t grid = std::min<int64_t>((units + 255) / 256, 65536);
+  if (grid > 0)
+    mxfp4_tile_kernel<<<(unsigned)grid, 256, 0, s>>>(static_cast<const uint8_t*>(src),
+                                                     static_cast<uint8_t*>(dst), rows, cols);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode1_bf16(const Decode1Args& a, const SelectOut& o, int num_cus,

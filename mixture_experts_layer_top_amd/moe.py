@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_traced": (_i, [ctypes.POINTER(Problem), _vp, _vp, ctypes.POINTER(Weights), _vp,
                                       ctypes.POINTER(Routing), _vp, _sz, ctypes.POINTER(_vp), _i, _vp]),
             "moe_status_string": (ctypes.c_char_p, [_i]),
+            "moe_mxfp4_tile": (_i, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -82,7 +83,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
             "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
-            "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string")
+            "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string", "moe_mxfp4_tile")
 
 TRACE_EVENTS = 8
 TRACE_PHASES = ("route", "permute", "quant", "select", "gate_up", "down", "combine")
@@ -197,6 +198,17 @@ def permute(ids: torch.Tensor, E: int, x: torch.Tensor | None = None,
                              _ptr(offsets), _ptr(perm_src), _ptr(slot_dst), _ptr(xp), _ptr(xps),
                              _ptr(ws), ws.numel(), _stream()), "moe_permute")
     return counts, offsets, perm_src, slot_dst, xp, xps
+
+
+def mxfp4_tile(w: torch.Tensor) -> torch.Tensor:
+    """Row-major MXFP4 bytes [..., rows, cols/2] (uint8) -> the library's tiled layout (same shape;
+    every leading dimension folds into the rows)."""
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    rows = w.numel() // w.shape[-1]
+    _check(lib().moe_mxfp4_tile(_ptr(w), _ptr(out), rows, 2 * w.shape[-1], _stream()),
+           "moe_mxfp4_tile")
+    return out
 
 
 def quant_act(x: torch.Tensor):

@@ -35,6 +35,11 @@ class Inputs:
         if self.p.wdtype == I.WDT_FP8:
             kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
         if self.p.wdtype == I.WDT_MXFP4:
+            # the library reads its tiled layout; the oracle keeps the generator's row-major bytes
+            from mixture_experts_layer_top_amd.moe import mxfp4_tile
+            if getattr(self, "_tiled", None) is None:
+                self._tiled = {n: mxfp4_tile(W[n]) for n in ("gate", "up", "down")}
+            kw.update(self._tiled)
             kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
         if self.p.shared:
             kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])

@@ -80,3 +80,18 @@ def test_workspace_sizes_scale():
     assert L.moe_layer_workspace_bytes(ctypes.byref(b)) > L.moe_layer_workspace_bytes(ctypes.byref(a))
     assert L.moe_permute_workspace_bytes(64, 8, 2) > 0
     assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(a)) > 0
+
+
+def test_mxfp4_tile_argument_errors():
+    """moe_mxfp4_tile rejects bad arguments on the host, before any launch."""
+    L = moe.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    a = (ctypes.addressof(buf) + 15) // 16 * 16
+    b = a + 8192
+    assert L.moe_mxfp4_tile(None, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_tile(a, None, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_tile(a + 8, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert L.moe_mxfp4_tile(a, a + 16, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # overlap
+    assert L.moe_mxfp4_tile(a, b, 15, 128, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mxfp4_tile(a, b, 16, 96, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mxfp4_tile(a, b, -16, 128, None) == moe.MOE_ERR_INVALID_ARG

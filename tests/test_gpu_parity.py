@@ -415,6 +415,23 @@ def test_mxfp4_grouped_ffn_matches_oracle(moe):
     assert rel_err(bits_to_f64(y), ref) <= BF16_TOL
 
 
+def test_mxfp4_tile_layout(moe):
+    """The tiled layout, restated from its definition: 16-row blocks, 128-element chunks, 1 KB per
+    (block, chunk) ordered [g][row][elements 32 g .. 32 g + 31]."""
+    rows, cols = 48, 384
+    src = np.random.default_rng(5).integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    got = moe.mxfp4_tile(torch.from_numpy(src).cuda()).cpu().numpy().reshape(-1)
+    want = np.empty(rows * cols // 2, np.uint8)
+    o = 0
+    for nb in range(rows // 16):
+        for c in range(cols // 128):
+            for g in range(4):
+                for r in range(16):
+                    want[o:o + 16] = src[16 * nb + r, 64 * c + 16 * g:64 * c + 16 * g + 16]
+                    o += 16
+    assert np.array_equal(got, want)
+
+
 def test_mxfp4_rejects_mfma_config(moe):
     inp = Inputs(MXFP4_SMALL[0])
     with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
