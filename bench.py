@@ -311,7 +311,8 @@ def main() -> int:
     d_logits = torch.from_numpy(logits).cuda()
     d_x = torch.from_numpy(x.view(np.int16)).cuda()
     kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
-    if p.wdtype == "fp8":
+    if p.wdtype == "fp8":  # the library's tiled weight layout (made once, untimed)
+        kw.update({n: moe.fp8_tile(W[n]) for n in ("gate", "up", "down")})
         kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
     if p.wdtype == "mxfp4":  # the library's tiled weight layout (made once, untimed)
         kw.update({n: moe.mxfp4_tile(W[n]) for n in ("gate", "up", "down")})
@@ -319,6 +320,7 @@ def main() -> int:
     if p.shared:
         kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
         if p.wdtype == "fp8":
+            kw.update({n: moe.fp8_tile(W[n]) for n in ("sh_gate", "sh_up", "sh_down")})
             kw.update(s_sh_gate=W["s_sh_gate"], s_sh_up=W["s_sh_up"], s_sh_down=W["s_sh_down"])
     ew = moe.ExpertWeights(**kw)
     layer = moe.Layer(ew, p.T, p.E, p.k, config=args.tile_config)

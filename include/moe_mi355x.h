@@ -26,7 +26,9 @@
  *       w_gate, w_up [E][d_ff][d_model]   (math shape d_model x d_ff)
  *       w_down       [E][d_model][d_ff]   (math shape d_ff x d_model)
  *     fp8 weights carry one fp32 scale per 128x128 block: s_gate, s_up [E][d_ff/128][d_model/128],
- *     s_down [E][d_model/128][d_ff/128]; the weight's value is code * scale.
+ *     s_down [E][d_model/128][d_ff/128]; the weight's value is code * scale.  fp8 weight bytes
+ *     (routed and shared) are passed in the library's tiled layout, made once by moe_fp8_tile
+ *     from the row-major one; the block scales stay row-major.
  *     mxfp4 weights (OCP MX MXFP4; GC-MoE, summary: FP4 grouped GEMM decoded in registers) pack
  *     two E2M1 codes per byte, element 2j in the low nibble of byte j: w_gate, w_up
  *     [E][d_ff][d_model/2], w_down [E][d_model][d_ff/2] bytes, with one E8M0 scale byte X per 32
@@ -168,6 +170,11 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_problem* p);
  * misaligned (16 bytes) pointers give MOE_ERR_INVALID_ARG.  (GC-MoE, summary: FP4 grouped GEMM;
  * the layout is this library's, so that each wavefront load reads 1 KB contiguously.) */
 int moe_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
+
+/* fp8 (E4M3) weight layout for the library (load time), as moe_mxfp4_tile with one byte per
+ * element: per 16-row block and 128-element chunk, 2 KB ordered [h 0..1][g 0..3][row 0..15]
+ * [16 bytes = elements 32 g + 16 h .. + 15 of the chunk].  Same argument rules. */
+int moe_fp8_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream);
 
 /* Combine: out[t] = bf16( sum_{j<k} topk_w[t][j] * y_perm[slot_dst[t*k+j]] (+ shared_y[t]) ),
  * the sum in fp32 in increasing j, the shared row (if not NULL) added last.

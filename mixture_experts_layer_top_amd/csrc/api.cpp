@@ -160,15 +160,27 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
 
 extern "C" {
 
-int moe_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream) {
+namespace {
+int weight_tile(const void* src, void* dst, int64_t rows, int64_t cols, int bytes_per_128,
+                hipStream_t stream) {
   if (!src || !dst || !aligned16(src) || !aligned16(dst) || rows < 0 || cols < 0)
     return MOE_ERR_INVALID_ARG;
   if (rows % 16 || cols % 128) return MOE_ERR_UNSUPPORTED;
   const char* a = static_cast<const char*>(src);
   const char* b = static_cast<const char*>(dst);
-  const int64_t bytes = rows * (cols / 2);
+  const int64_t row_bytes = cols / 128 * bytes_per_128;
+  const int64_t bytes = rows * row_bytes;
   if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
-  return hip_status(moe::launch_mxfp4_tile(src, dst, rows, cols, stream));
+  return hip_status(moe::launch_weight_tile(src, dst, rows, row_bytes, bytes_per_128, stream));
+}
+}  // namespace
+
+int moe_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream) {
+  return weight_tile(src, dst, rows, cols, 64, stream);
+}
+
+int moe_fp8_tile(const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t stream) {
+  return weight_tile(src, dst, rows, cols, 128, stream);
 }
 
 const char* moe_status_string(int status) {

@@ -1210,31 +1210,34 @@ static void launch_decode1_vpl(const Decode1Args& a, const SelectOut& o, int g, 
   else decode1_gate_up_bf16<VPL, 2><<<g, 256, 0, s>>>(a, o);
 }
 
-// Row-major MXFP4 bytes [rows][cols/2] -> the tiled layout the MXFP4 tiles read (one 16-byte
-// unit per thread: unit u of block (rows / 16, cols / 128) holds row 16 nb + (u % 16), values
-// 128 c + 32 (u / 16 % 4) .. + 31).
-__global__ __launch_bounds__(256) void mxfp4_tile_kernel(const uint8_t* __restrict__ src,
-                                                         uint8_t* __restrict__ dst, int64_t rows,
-                                                         int64_t cols) {
-  const int64_t nchunk = cols / 128;
-  const int64_t units = rows / 16 * nchunk * 64;
+// Row-major weight bytes [rows][row_bytes] -> the tiled layout the streaming tiles of the narrow
+// formats read: per 16-row block and chunk of cb bytes of a row (128 elements: cb = 64 for MXFP4,
+// 128 for fp8), cb 16-byte units ordered [h < cb / 64][lane group g < 4][row r < 16], unit
+// (h, g, r) = bytes [cb c + (cb / 4) g + 16 h, +16) of row 16 nb + r.  One unit per thread.
+__global__ __launch_bounds__(256) void weight_tile_kernel(const uint8_t* __restrict__ src,
+                                                          uint8_t* __restrict__ dst, int64_t rows,
+                                                          int64_t row_bytes, int cb) {
+  const int64_t nchunk = row_bytes / cb;
+  const int64_t units = rows / 16 * nchunk * cb;
   for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < units;
        t += (int64_t)gridDim.x * 256) {
-    const int64_t blk = t / 64, l = t % 64;     // blk = nb * nchunk + c
+    const int64_t blk = t / cb, u = t % cb;  // blk = nb * nchunk + c
     const int64_t nb = blk / nchunk, c = blk % nchunk;
-    const int64_t row = nb * 16 + (l & 15), kg = l >> 4;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + row * (cols / 2) + c * 64 + kg * 16);
+    const int64_t h = u / 64, g = (u % 64) >> 4, r = u & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (nb * 16 + r) * row_bytes + c * cb +
+                                                    g * (cb / 4) + 16 * h);
     *reinterpret_cast<uint4*>(dst + t * 16) = v;
   }
 }
 
-hipError_t launch_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols,
-                             hipStream_t s) {
-  const int64_t units = rows / 16 * (cols / 128) * 64;
+hipError_t launch_weight_tile(const void* src, void* dst, int64_t rows, int64_t row_bytes, int cb,
+                              hipStream_t s) {
+  const int64_t units = rows / 16 * (row_bytes / cb) * cb;
   const int64_t grid = std::min<int64_t>((units + 255) / 256, 65536);
   if (grid > 0)
-    mxfp4_tile_kernel<<<(unsigned)grid, 256, 0, s>>>(static_cast<const uint8_t*>(src),
-                                                     static_cast<uint8_t*>(dst), rows, cols);
+    weight_tile_kernel<<<(unsigned)grid, 256, 0, s>>>(static_cast<const uint8_t*>(src),
+                                                      static_cast<uint8_t*>(dst), rows, row_bytes,
+                                                      cb);
   return hipGetLastError();
 }
 

@@ -68,7 +68,10 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
   // this lane's weight rows for row groups 0, 1
   uint32_t woff[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) woff[g] = (uint32_t)(n0 + wv * 32 + g * 16 + r16) * K + kg * 32;
+  // tiled weights (moe_fp8_tile): per 16-row block and 128-byte chunk of K, 2 KB ordered
+  // [half][lane group][row][16 bytes], so lane kg * 16 + r16 reads its row's 32 bytes of the chunk
+  // as two 16-byte loads 1 KB apart, and each load instruction reads 1 KB contiguously
+  for (int g = 0; g < 2; ++g) woff[g] = (uint32_t)(n0 + wv * 32 + g * 16) * K + lane * 16;
   uint32_t xoff[MQ];
   int srow[MQ];  // activation row of token column r16 in group q (for its scale)
 #pragma unroll
@@ -95,8 +98,8 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
     const uint32_t ko = (uint32_t)kb * 128;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      b.wg[g] = as_i32x8(gload16(sg.w0, woff[g] + ko), gload16(sg.w0, woff[g] + ko + 16));
-      b.wu[g] = as_i32x8(gload16(sg.w1, woff[g] + ko), gload16(sg.w1, woff[g] + ko + 16));
+      b.wg[g] = as_i32x8(gload16(sg.w0, woff[g] + ko * 16), gload16(sg.w0, woff[g] + ko * 16 + 1024));
+      b.wu[g] = as_i32x8(gload16(sg.w1, woff[g] + ko * 16), gload16(sg.w1, woff[g] + ko * 16 + 1024));
     }
 #pragma unroll
     for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
@@ -172,7 +175,7 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K, N = sg.N, nkb = K / 128;
-  const uint32_t woff = (uint32_t)(n0 + wv * 16 + r16) * K + kg * 32;
+  const uint32_t woff = (uint32_t)(n0 + wv * 16) * K + lane * 16;  // tiled weights, as gate/up
   uint32_t xoff[MQ];
   int srow[MQ];
 #pragma unroll
@@ -190,7 +193,7 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
   struct Blk { i32x8 w, xb[MQ]; float sw, sx[MQ]; };
   auto load = [&](Blk& b, int kb) {
     const uint32_t ko = (uint32_t)kb * 128;
-    b.w = as_i32x8(gload16(sg.w0, woff + ko), gload16(sg.w0, woff + ko + 16));
+    b.w = as_i32x8(gload16(sg.w0, woff + ko * 16), gload16(sg.w0, woff + ko * 16 + 1024));
 #pragma unroll
     for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
     b.sw = gload_f32(sg.s0, nb * nkb + kb);

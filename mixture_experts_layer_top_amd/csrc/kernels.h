@@ -143,9 +143,10 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
 // Launches the persistent kernel of each tile family of one GEMM (kGemmGateUp or kGemmDown) that
 // may hold tiles (the other's queue is empty).  max_rows bounds the rows of any one expert, max_k
 // the GEMM's K over all its segments.
-// Row-major MXFP4 bytes [rows][cols/2] -> tiled layout (rows % 16 == 0, cols % 128 == 0).
-hipError_t launch_mxfp4_tile(const void* src, void* dst, int64_t rows, int64_t cols,
-                             hipStream_t s);
+// Row-major weight bytes [rows][row_bytes] -> tiled layout in chunks of cb bytes per row
+// (rows % 16 == 0, row_bytes % cb == 0; cb = 64 for MXFP4, 128 for fp8).
+hipError_t launch_weight_tile(const void* src, void* dst, int64_t rows, int64_t row_bytes, int cb,
+                              hipStream_t s);
 // w4: mxfp4 weights (streaming tiles only; mfma must be false)
 hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
                              int max_k, bool stream, bool mfma, hipStream_t s, bool w4);

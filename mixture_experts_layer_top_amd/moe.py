@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(Routing), _vp, _sz, ctypes.POINTER(_vp), _i, _vp]),
             "moe_status_string": (ctypes.c_char_p, [_i]),
             "moe_mxfp4_tile": (_i, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
+            "moe_fp8_tile": (_i, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -83,7 +84,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
             "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
-            "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string", "moe_mxfp4_tile")
+            "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string", "moe_mxfp4_tile",
+            "moe_fp8_tile")
 
 TRACE_EVENTS = 8
 TRACE_PHASES = ("route", "permute", "quant", "select", "gate_up", "down", "combine")
@@ -208,6 +210,15 @@ def mxfp4_tile(w: torch.Tensor) -> torch.Tensor:
     rows = w.numel() // w.shape[-1]
     _check(lib().moe_mxfp4_tile(_ptr(w), _ptr(out), rows, 2 * w.shape[-1], _stream()),
            "moe_mxfp4_tile")
+    return out
+
+
+def fp8_tile(w: torch.Tensor) -> torch.Tensor:
+    """Row-major fp8 weight bytes [..., rows, cols] (uint8) -> the library's tiled layout."""
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    rows = w.numel() // w.shape[-1]
+    _check(lib().moe_fp8_tile(_ptr(w), _ptr(out), rows, w.shape[-1], _stream()), "moe_fp8_tile")
     return out
 
 

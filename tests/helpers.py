@@ -33,6 +33,12 @@ class Inputs:
         W = self.W
         kw = dict(gate=W["gate"], up=W["up"], down=W["down"])
         if self.p.wdtype == I.WDT_FP8:
+            # the library reads its tiled layout; the oracle keeps the generator's row-major bytes
+            from mixture_experts_layer_top_amd.moe import fp8_tile
+            if getattr(self, "_tiled", None) is None:
+                names = ("gate", "up", "down") + (("sh_gate", "sh_up", "sh_down") if self.p.shared else ())
+                self._tiled = {n: fp8_tile(W[n]) for n in names}
+            kw.update({n: self._tiled[n] for n in ("gate", "up", "down")})
             kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
         if self.p.wdtype == I.WDT_MXFP4:
             # the library reads its tiled layout; the oracle keeps the generator's row-major bytes
@@ -44,6 +50,7 @@ class Inputs:
         if self.p.shared:
             kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
             if self.p.wdtype == I.WDT_FP8:
+                kw.update({n: self._tiled[n] for n in ("sh_gate", "sh_up", "sh_down")})
                 kw.update(s_sh_gate=W["s_sh_gate"], s_sh_up=W["s_sh_up"], s_sh_down=W["s_sh_down"])
         return ExpertWeights(**kw)
 

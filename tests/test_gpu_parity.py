@@ -432,6 +432,25 @@ def test_mxfp4_tile_layout(moe):
     assert np.array_equal(got, want)
 
 
+def test_fp8_tile_layout(moe):
+    """The fp8 tiled layout, restated from its definition: 16-row blocks, 128-element chunks, 2 KB
+    per (block, chunk) ordered [h][g][row][elements 32 g + 16 h .. + 15]."""
+    rows, cols = 32, 256
+    src = np.random.default_rng(6).integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    got = moe.fp8_tile(torch.from_numpy(src).cuda()).cpu().numpy().reshape(-1)
+    want = np.empty(rows * cols, np.uint8)
+    o = 0
+    for nb in range(rows // 16):
+        for c in range(cols // 128):
+            for h in range(2):
+                for g in range(4):
+                    for r in range(16):
+                        b0 = 128 * c + 32 * g + 16 * h
+                        want[o:o + 16] = src[16 * nb + r, b0:b0 + 16]
+                        o += 16
+    assert np.array_equal(got, want)
+
+
 def test_mxfp4_rejects_mfma_config(moe):
     inp = Inputs(MXFP4_SMALL[0])
     with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
