@@ -1,7 +1,9 @@
 // OCP E4M3FN encoder for the device (bias 7, 3 mantissa bits, largest finite 448, S.1111.111 = NaN,
 // no infinities): round to nearest, ties to the even mantissa, saturate at +-448, keep the sign.
 // Written from the format definition with integer operations only, so its rounding does not depend
-// on a conversion instruction's modes.  Finite inputs only.
+// on a conversion instruction's modes.  Finite inputs only.  Host and device: the same source is
+// compiled into a CPU harness that compares it with an independent encoder on every finite fp32
+// bit pattern.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,10 +11,10 @@
 
 namespace moe {
 
-__device__ __forceinline__ uint8_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
+__host__ __device__ __forceinline__ uint8_t e4m3_encode(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
   const uint32_t sign = (u >> 31) << 7;
-  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  const float a = __builtin_bit_cast(float, u & 0x7FFFFFFFu);
   uint32_t mag;
   if (a >= 448.0f) {
     mag = 0x7E;

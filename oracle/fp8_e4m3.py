@@ -23,8 +23,8 @@ E4M3_MAX = 448.0
 NAN_CODE = 0x7F
 
 
-def decode(codes) -> np.ndarray:
-    """uint8 codes -> float64 values (NaN for S.1111.111)."""
+def _decode_formula(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for S.1111.111), from the bit layout above."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     s = c >> 7
     e = (c >> 3) & 15
@@ -37,8 +37,17 @@ def decode(codes) -> np.ndarray:
     return val
 
 
+# every code's value, from the formula (a lookup of this table is the decoder)
+_TABLE = _decode_formula(np.arange(256, dtype=np.uint8))
+
+
+def decode(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for S.1111.111)."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 # non-negative finite values, codes 0..126, strictly increasing in the code
-_POS = decode(np.arange(127, dtype=np.uint8))
+_POS = _TABLE[:127].copy()
 
 
 def encode(v) -> np.ndarray:

@@ -59,16 +59,19 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 
 
 def f64_to_bf16_f64(v) -> np.ndarray:
-    """Round float64 values to the nearest-even bfloat16 value (returned as float64).
+    """Round float64 values to the nearest bfloat16 value, ties to an even last bit (returned as
+    float64), in one rounding straight from float64.
 
-    Goes through float32 first only when that is exact for the bf16 decision; here the value is
-    rounded directly: bf16 keeps 8 significant bits, so the result is the nearest multiple of
-    2^(exponent - 7), ties to an even last bit."""
+    bfloat16 has 8 significant bits and float32's exponent range: a value v = m * 2^e with
+    0.5 <= |m| < 1 lies on the grid of its quantum 2^(e - 8) while e >= -125 (normal numbers,
+    down to 2^-126); below that the grid is the subnormal quantum 2^-133.  A result of magnitude
+    2^128 or more is out of range and becomes an infinity of the value's sign."""
     v = np.asarray(v, dtype=np.float64)
-    m, e = np.frexp(v)  # v = m * 2^e, 0.5 <= |m| < 1
-    scaled = np.ldexp(m, 8)  # 8 significant bits -> integer part
-    r = np.round(scaled)  # numpy rounds half to even
-    out = np.ldexp(r, e - 8)
+    _, e = np.frexp(v)
+    q = np.maximum(e, -125) - 8  # exponent of the quantum
+    r = np.round(np.ldexp(v, -q))  # scaling by a power of two is exact; numpy rounds half to even
+    out = np.ldexp(r, q)
+    out = np.where(np.abs(out) >= 2.0 ** 128, np.copysign(np.inf, v), out)
     return np.where(v == 0, v, out)
 
 
@@ -232,35 +235,53 @@ def moe_layer(logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: boo
     'gate', 'up' ([f, d]) and 'down' ([d, f]) of expert e (bf16 bits, or E4M3 codes plus
     's_gate', 's_up', 's_down' block scales); get_shared() -> the same for the shared expert.
     Returns a dict of every intermediate the boundary exports plus 'out' (float64 [T, d])."""
-    logits = np.asarray(logits, dtype=np.float32)
-    T, E = logits.shape
-    ids, w = route(logits, k)
-    counts, offsets = histogram(ids, E)
-    perm_src, slot_dst = permute(ids, E)
-    xin, xq, xs = layer_input(x_bits, act_fp8)
-    d = xin.shape[1]
-    Y = np.zeros((T * k, d), dtype=np.float64)
+    return moe_layers([(logits, x_bits)], k, get_weights, get_shared, act_fp8)[0]
+
+
+def moe_layers(batches, k: int, get_weights, get_shared=None, act_fp8: bool = False):
+    """Several calls of the layer with one set of expert weights (a sweep over batch sizes or
+    routing draws of one model layer), each computed exactly as moe_layer defines it; an expert's
+    weights are decoded once for all the calls that route rows to it.
+
+    batches: list of (logits float32 [T_i, E], x_bits bf16 bits [T_i, d]).  Returns one result dict
+    per call (see moe_layer)."""
+    res = []
+    for logits, x_bits in batches:
+        logits = np.asarray(logits, dtype=np.float32)
+        T, E = logits.shape
+        ids, w = route(logits, k)
+        counts, offsets = histogram(ids, E)
+        perm_src, slot_dst = permute(ids, E)
+        xin, xq, xs = layer_input(x_bits, act_fp8)
+        r = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm_src=perm_src,
+                 slot_dst=slot_dst, y_perm=np.zeros((T * k, xin.shape[1]), dtype=np.float64),
+                 xin=xin)
+        if act_fp8:
+            r["xq"], r["xs"] = xq, xs
+        res.append(r)
+    E = res[0]["counts"].size if res else 0
     for e in range(E):
-        c = int(counts[e])
-        if c == 0:
+        if all(int(r["counts"][e]) == 0 for r in res):
             continue
-        r0 = int(offsets[e])
-        tokens = perm_src[r0:r0 + c] // k
         Wg, Wu, Wd = _expert_mats(get_weights, e)
-        Y[r0:r0 + c] = expert_ffn(xin[tokens], Wg, Wu, Wd)
-    S = None
+        for r in res:
+            c = int(r["counts"][e])
+            if c == 0:
+                continue
+            r0 = int(r["offsets"][e])
+            tokens = r["perm_src"][r0:r0 + c] // k
+            r["y_perm"][r0:r0 + c] = expert_ffn(r["xin"][tokens], Wg, Wu, Wd)
+    sh = None
     if get_shared is not None:
         raw = get_shared()
-        S = expert_ffn(xin, decode_weight(raw["gate"], raw.get("s_gate")),
-                       decode_weight(raw["up"], raw.get("s_up")),
-                       decode_weight(raw["down"], raw.get("s_down")))
-    out = combine(Y, slot_dst, w, S)
-    res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm_src=perm_src,
-               slot_dst=slot_dst, out=out, y_perm=Y)
-    if act_fp8:
-        res["xq"], res["xs"] = xq, xs
-    if S is not None:
-        res["shared_y"] = S
+        sh = (decode_weight(raw["gate"], raw.get("s_gate")), decode_weight(raw["up"], raw.get("s_up")),
+              decode_weight(raw["down"], raw.get("s_down")))
+    for r in res:
+        S = expert_ffn(r["xin"], *sh) if sh is not None else None
+        r["out"] = combine(r["y_perm"], r["slot_dst"], r["w"], S)
+        if S is not None:
+            r["shared_y"] = S
+        del r["xin"]
     return res
 
 

@@ -23,11 +23,7 @@ E2M1_MAX = 6.0
 E8M0_NAN = 255
 
 
-def decode_e2m1(codes) -> np.ndarray:
-    """4-bit codes (0..15, any integer dtype) -> float64 values."""
-    c = np.asarray(codes).astype(np.int64)
-    if np.any((c < 0) | (c > 15)):
-        raise ValueError("E2M1 codes are 4-bit")
+def _e2m1_formula(c) -> np.ndarray:
     s = c >> 3
     e = (c >> 1) & 3
     m = c & 1
@@ -37,11 +33,27 @@ def decode_e2m1(codes) -> np.ndarray:
     return np.where(s == 1, -mag, mag)
 
 
-def decode_e8m0(x) -> np.ndarray:
-    """8-bit E8M0 scale codes -> float64 (NaN for 255)."""
-    a = np.asarray(x).astype(np.int64)
+def _e8m0_formula(a) -> np.ndarray:
     v = np.ldexp(1.0, a - 127)
     return np.where(a == E8M0_NAN, np.nan, v)
+
+
+# every code's value, from the formulas above (a lookup of these tables is the decoder)
+_E2M1 = _e2m1_formula(np.arange(16, dtype=np.int64))
+_E8M0 = _e8m0_formula(np.arange(256, dtype=np.int64))
+
+
+def decode_e2m1(codes) -> np.ndarray:
+    """4-bit codes (0..15, any integer dtype) -> float64 values."""
+    c = np.asarray(codes).astype(np.int64)
+    if np.any((c < 0) | (c > 15)):
+        raise ValueError("E2M1 codes are 4-bit")
+    return _E2M1[c]
+
+
+def decode_e8m0(x) -> np.ndarray:
+    """8-bit E8M0 scale codes -> float64 (NaN for 255)."""
+    return _E8M0[np.asarray(x, dtype=np.uint8)]
 
 
 def unpack(packed) -> np.ndarray:

@@ -395,3 +395,108 @@ def test_tolerance_attainable_fp8_small():
     emu = O.moe_layer_emulated(L, x, p.k, get, get_sh, act_fp8=True)
     err = np.abs(emu - ref).max() / np.abs(ref).max()
     assert err <= 6e-2 / 2, err
+
+
+# ------------------------------------------------------------------------------------------------
+# the emulated variant's rounding steps
+# ------------------------------------------------------------------------------------------------
+
+def _finite_f32_sample(n, seed):
+    """Random float32 bit patterns over the whole finite range (every binade, subnormals, both
+    signs), plus the values next to the bfloat16 overflow boundary."""
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> np.uint32(23)) & np.uint32(255)) != 255]
+    edge = np.arange(0x7F7F0000, 0x7F800000, 97, dtype=np.uint32)  # near float32 / bf16 max
+    sub = np.arange(0, 1 << 23, 4099, dtype=np.uint32)              # float32 subnormals
+    u = np.concatenate([u, edge, sub])
+    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    return u.view(np.float32)
+
+
+def test_bf16_rounding_matches_integer_rounding_and_torch():
+    """On float32-representable values the oracle's bf16 rounding equals the generator's integer
+    round-half-even on the bit pattern and torch's float32 -> bfloat16 conversion (two routes that
+    share nothing with the oracle's frexp/quantum arithmetic)."""
+    import torch
+    v = _finite_f32_sample(2_000_000, 21)
+    got = O.f64_to_bf16_f64(v.astype(np.float64))
+    via_bits = O.bf16_bits_to_f64(I.f32_to_bf16_bits(v))
+    via_torch = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, via_bits)
+    assert np.array_equal(got, via_torch)
+    assert np.array_equal(np.signbit(got), np.signbit(v))
+
+
+def test_bf16_rounding_hand_worked():
+    """Float64 values that float32 cannot hold: one rounding, straight from float64 (going through
+    float32 first would round twice and lose the sticky bits)."""
+    t = 2.0 ** -133  # bf16 subnormal quantum
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite bf16
+    cases = [
+        (1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 2.0 ** -7),  # above the midpoint: up (via fp32: tie -> 1)
+        (1.0 + 2.0 ** -8, 1.0),                          # tie, 1.0000000 is even
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),          # tie between ...001 and ...010: even
+        (1.0 + 2.0 ** -8 - 2.0 ** -40, 1.0),             # just below the midpoint
+        (1.5 * t, 2 * t),                                # subnormal tie: 1 (odd) vs 2 (even)
+        (0.5 * t, 0.0),                                  # tie with zero: zero is even
+        (0.5 * t + 2.0 ** -170, t),                      # just above it
+        (2.0 ** -126 - 2.0 ** -140, 2.0 ** -126),        # rounds up into the normal range
+        ((2.0 - 2.0 ** -8) * 2.0 ** 127, math.inf),      # tie between max (odd) and 2^128 (even)
+        ((2.0 - 2.0 ** -8 - 2.0 ** -20) * 2.0 ** 127, big),
+        (3.39e38, big),                                  # above max, below max + half a step
+        (1.0e39, math.inf),
+        (1e-300, 0.0),
+    ]
+    for v, want in cases:
+        for sgn in (1.0, -1.0):
+            got = float(O.f64_to_bf16_f64(np.array([sgn * v]))[0])
+            assert got == sgn * want, (sgn * v, got, sgn * want)
+            assert math.copysign(1.0, got) == sgn
+
+
+def test_requant_rows_matches_activation_quantiser():
+    """quant_rows_e4m3_f64 (the emulated fp8 requantisation of h) on bf16-representable rows equals
+    dequantising the activation quantiser's codes and scales, which takes the bits themselves."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((9, 640)) * np.array([1, 1e-3, 40, 1, 3e-6, 1, 1, 200, 1],
+                                                  np.float32)[:, None]).astype(np.float32)
+    x[3, 128:256] = 0.0
+    x[5, :128] = -0.0
+    x[6, 256:384] = rng.integers(-4, 5, 128)
+    bits = I.f32_to_bf16_bits(x)
+    q, s = O.quant_act_e4m3(bits)
+    want = O.dequant_act_e4m3(q, s)
+    got = O.quant_rows_e4m3_f64(O.bf16_bits_to_f64(bits))
+    assert np.array_equal(got, want)
+
+
+def test_requant_rows_hand_worked():
+    """One 128-wide group worked by hand: amax 896 gives s = 2 exactly; 896 -> 448 (code 0x7E);
+    3 -> 1.5; 2.3 -> 1.15 -> 1.125 (step 1/8 in [1, 2)); 0.01 -> 0.005 -> 3 * 2^-9 (subnormal step
+    2^-9: 0.005 / 2^-9 = 2.56); -700 -> -350 -> -352 (step 32 in [256, 448]).  Values are then
+    multiplied back by s."""
+    row = np.zeros((1, 128))
+    row[0, :5] = [896.0, 3.0, 2.3, 0.01, -700.0]
+    got = O.quant_rows_e4m3_f64(row)[0]
+    want = np.zeros(128)
+    want[:5] = [896.0, 3.0, 2.25, 2 * 3 * 2.0 ** -9, -704.0]
+    assert np.array_equal(got, want)
+
+
+def test_layers_sharing_weights_equal_separate_layers():
+    """moe_layers (several calls decoding each expert once) gives each call's moe_layer result,
+    computed here expert by expert without it: the per-token direct form for each call."""
+    rng = np.random.default_rng(23)
+    T_list, d, f, E, k = (1, 7, 30), 128, 128, 6, 2
+    W = {e: {n: I.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32) * 0.05)
+             for n, s in (("gate", (f, d)), ("up", (f, d)), ("down", (d, f)))} for e in range(E + 1)}
+    calls = [(rng.standard_normal((T, E)).astype(np.float32),
+              I.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))) for T in T_list]
+    for shared in (None, (lambda: W[E])):
+        got = O.moe_layers(calls, k, lambda e: W[e], shared)
+        for (L, x), r in zip(calls, got):
+            direct = O.moe_tokens(np.arange(L.shape[0]), L, x, k, lambda e: W[e], shared)
+            assert np.allclose(r["out"], direct["out"], rtol=1e-12, atol=1e-14)
+            ids, _ = O.route(L, k)
+            assert np.array_equal(r["ids"], ids)
