@@ -41,8 +41,13 @@
  *     on the host only (null pointers, sizes, 16-byte alignment, workspace size).  Device data is
  *     not validated: non-finite logits or out-of-range expert ids are undefined behaviour.
  *     T = 0 is a valid no-op.  A failed launch returns MOE_ERR_HIP.
- *   - Limits: 1 <= k <= 8, k <= E <= 512, d_model and d_ff multiples of 128, T*k < 2^31.
- *   - Calls are reentrant: no mutable global state; concurrent calls need distinct workspaces.
+ *   - Limits: 1 <= k <= 8, k <= E <= 512, d_model and d_ff multiples of 128, T*k < 2^31.  The
+ *     kernels address rows with 32-bit byte offsets, so moe_layer and moe_grouped_ffn also need
+ *     T*k*max(d_model, d_ff, d_ff_shared)*2 < 2^32 and d_model*max(d_ff, d_ff_shared)*2 < 2^32
+ *     (every activation, h and y buffer and each expert matrix below 4 GiB); moe_quant_act needs
+ *     T*d/128 < 2^31 and moe_permute's gather T*k*d/128 < 2^31.  Outside them: MOE_ERR_UNSUPPORTED.
+ *   - Calls are reentrant: no mutable global state (the device's compute-unit count is queried on
+ *     every call); concurrent calls need distinct workspaces.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -92,6 +97,15 @@ typedef struct moe_problem {
   int32_t config;      /* enum moe_config */
 } moe_problem;
 
+/* Storage layout of the expert weight bytes (moe_weights.layout).  bf16 weights are row-major; fp8
+ * and mxfp4 weight bytes must be in the library's tiled layout, made by moe_fp8_tile /
+ * moe_mxfp4_tile.  The two layouts have the same size, so the tag is what tells them apart: a
+ * mismatch gives MOE_ERR_INVALID_ARG instead of silently wrong outputs. */
+enum moe_layout {
+  MOE_LAYOUT_ROW_MAJOR = 0,
+  MOE_LAYOUT_TILED = 1
+};
+
 typedef struct moe_weights {
   const void* w_gate; /* [E][f][d] bf16 or e4m3 */
   const void* w_up;   /* [E][f][d] */
@@ -108,6 +122,8 @@ typedef struct moe_weights {
   const uint8_t* e_gate; /* mxfp4 only: E8M0 scales [E][f][d/32]; NULL otherwise */
   const uint8_t* e_up;
   const uint8_t* e_down; /* [E][d][f/32] */
+  int32_t layout;        /* enum moe_layout of w_* and sh_*: MOE_LAYOUT_TILED for fp8 and mxfp4,
+                            MOE_LAYOUT_ROW_MAJOR for bf16 */
 } moe_weights;
 
 /* Optional routing outputs of moe_layer (any member may be NULL to skip it). */

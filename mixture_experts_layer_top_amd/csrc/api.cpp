@@ -34,19 +34,18 @@ struct Carver {
   }
 };
 
-// Compute-unit count of the current device (read-only after the first query per device).
+// Compute units of the current device, queried on every call (the runtime answers from its cached
+// device properties); the library keeps no state between calls.  0 if the query fails.
 int device_cus() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n > 0 ? n : 0;
 }
+
+// The kernels address activation, h and y rows and one expert's weight matrix with 32-bit byte
+// offsets (one VGPR per address instead of two): every such buffer must stay below 4 GiB.
+constexpr int64_t kMaxOffsetBytes = int64_t(1) << 32;
 
 int check_route_shape(int T, int E, int k) {
   if (T < 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
@@ -69,11 +68,23 @@ int check_problem(const moe_problem* p) {
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
   if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) return MOE_ERR_INVALID_ARG;
+  // 32-bit byte offsets: x [T][d], h [T*k][f], y [T*k][d], shared h [T][f_sh] (2 bytes per value
+  // at most) and each expert's [f][d] matrices must stay below 4 GiB
+  const int64_t n = (int64_t)p->T * p->top_k;
+  const int64_t f_sh = p->has_shared ? p->d_ff_shared : 0;
+  const int64_t wide = std::max<int64_t>(std::max(p->d_model, p->d_ff), f_sh);
+  if (n * wide * 2 >= kMaxOffsetBytes) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->d_model * std::max<int64_t>(p->d_ff, f_sh) * 2 >= kMaxOffsetBytes)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) {
   if (!w) return MOE_ERR_INVALID_ARG;
+  // fp8 and mxfp4 weight bytes must be in the tiled layout (same size as the row-major one, so
+  // the tag is the only thing that tells them apart); bf16 weights are row-major
+  const int32_t want = p->wdtype == MOE_DTYPE_BF16 ? MOE_LAYOUT_ROW_MAJOR : MOE_LAYOUT_TILED;
+  if (w->layout != want) return MOE_ERR_INVALID_ARG;
   const void* need[] = {w->w_gate, w->w_up, w->w_down};
   for (const void* q : need)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
@@ -137,8 +148,7 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
 // no expert exceeds kFewTileRows rows and even one m-tile per expert that can hold rows would not
 // make 1.6 rounds of CUs.
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
-                        int64_t total_rows, hipStream_t s) {
-  const int cus = device_cus();
+                        int64_t total_rows, int cus, hipStream_t s) {
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
@@ -223,6 +233,7 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k, const void* x, con
     if (!x || d <= 0) return MOE_ERR_INVALID_ARG;
     if (d % 128) return MOE_ERR_UNSUPPORTED;
     if (act_dtype != MOE_DTYPE_BF16 && act_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)T * k * (d / 128) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;  // scale index
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
     if (act_dtype == MOE_DTYPE_FP8_E4M3 && x_perm_scale && !x_scale) return MOE_ERR_INVALID_ARG;
   }
@@ -247,6 +258,7 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k, const void* x, con
 int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t stream) {
   if (T < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
   if (d % 128) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * (d / 128) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;  // 32-bit group index
   if (T == 0) return MOE_OK;
   if (!x || !xq || !xs) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_quant_act(x, T, d, xq, xs, stream));
@@ -277,6 +289,8 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   Carver c{static_cast<uint8_t*>(ws)};
   FfnWs f;
   carve_ffn(c, p, false, f);
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_HIP;
   SelectArgs a;
   std::memset(&a, 0, sizeof(a));
   a.counts = counts;
@@ -288,7 +302,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.f = p->d_ff;
   a.has_shared = 0;
   a.config = p->config;
-  a.num_cus = device_cus();
+  a.num_cus = cus;
   a.fp8 = fp8;
   a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
   a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
@@ -302,8 +316,8 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   SelectOut o{f.segs, f.meta, f.split_cnt, f.split_part};
   hipError_t e = launch_select(a, o, stream);
   const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
-  if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, n, n, stream);
-  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, n, n, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, n, n, cus, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, n, n, cus, stream);
   return hip_status(e);
 }
 
@@ -379,6 +393,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   carve_layer(c, p, L);
   const int T = p->T, E = p->num_experts, k = p->top_k, d = p->d_model;
   const int fp8 = p->wdtype == MOE_DTYPE_FP8_E4M3;
+  const int cus = device_cus();
+  if (cus == 0) return MOE_ERR_HIP;
   int32_t* ids = (keep && keep->topk_ids) ? keep->topk_ids : L.ids;
   float* wts = (keep && keep->topk_w) ? keep->topk_w : L.w;
   int32_t* counts = (keep && keep->counts) ? keep->counts : L.counts;
@@ -402,7 +418,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.f_sh = p->has_shared ? p->d_ff_shared : 0;
   a.has_shared = p->has_shared;
   a.config = p->config;
-  a.num_cus = device_cus();
+  a.num_cus = cus;
   a.fp8 = fp8;
   a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
   a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
@@ -445,7 +461,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
     da.slot_dst = slot_dst;
     da.tok = L.tok;
     for (int i = 1; i <= 4 && e == hipSuccess; ++i) e = mark(i);
-    if (e == hipSuccess) e = launch_decode1_bf16(da, o, device_cus(), stream);
+    if (e == hipSuccess) e = launch_decode1_bf16(da, o, cus, stream);
   } else if (front_small_fits(T, k)) {
     // decode-sized: route, permute and select in one launch (phases 1, 2 and 4 share it)
     if (e == hipSuccess)
@@ -470,9 +486,9 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   }
   // each token routes to k distinct experts, so no expert (nor the shared one) holds more than T rows
   if (e == hipSuccess && !decode1)
-    e = launch_gemms(o, p, kGemmGateUp, T, (int64_t)T * p->top_k, stream);
+    e = launch_gemms(o, p, kGemmGateUp, T, (int64_t)T * p->top_k, cus, stream);
   if (e == hipSuccess) e = mark(5);
-  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, T, (int64_t)T * p->top_k, stream);
+  if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, T, (int64_t)T * p->top_k, cus, stream);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)
     e = launch_combine(L.y, slot_dst, wts, T, k, d, p->has_shared ? L.ffn.y_sh : nullptr, out,

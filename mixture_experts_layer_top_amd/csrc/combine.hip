@@ -1,7 +1,8 @@
 // Combine: gate-weighted gather-reduce back to token order (GC-MoE, summary: the combine step that
 // follows the grouped GEMMs).  out[t] = bf16(sum_{j<k} w[t][j] * y[slot_dst[t*k+j]] (+ shared[t])),
 // accumulated in fp32 in increasing j with the shared row last: deterministic, no atomics.
-// Each thread owns 8 consecutive channels (16-byte loads and stores); grid = (d/2048 blocks, T).
+// Each thread owns 8 consecutive channels (16-byte loads and stores); a one-dimensional grid of
+// T * ceil(d / 2048) workgroups (token-major), so T is not bound by the grid's y limit.
 #include "common.h"
 #include "kernels.h"
 
@@ -10,10 +11,10 @@ namespace moe {
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ slot_dst,
                                                       const float* __restrict__ w, int k, int d,
-                                                      const uint16_t* __restrict__ sh,
+                                                      int nbx, const uint16_t* __restrict__ sh,
                                                       uint16_t* __restrict__ out) {
-  const int t = blockIdx.y;
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  const int t = blockIdx.x / nbx;
+  const int c = ((blockIdx.x - t * nbx) * 256 + threadIdx.x) * 8;
   if (c >= d) return;
   // all k rows' indices and weights, then all k row loads, before any arithmetic (k <= 8)
   int row[kMaxTopK];
@@ -63,9 +64,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
                           int d, const void* shared_y, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((d / 8 + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(y), slot_dst, w, k, d,
-                                      static_cast<const uint16_t*>(shared_y),
+  const int nbx = (d / 8 + 255) / 256;
+  combine_kernel<<<(unsigned)((int64_t)T * nbx), 256, 0, s>>>(static_cast<const uint16_t*>(y),
+                                      slot_dst, w, k, d, nbx, static_cast<const uint16_t*>(shared_y),
                                       static_cast<uint16_t*>(out));
   return hipGetLastError();
 }

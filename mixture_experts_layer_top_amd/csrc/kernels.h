@@ -36,9 +36,10 @@ __host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ?
 constexpr int kStreamXlMaxK = 8192;
 constexpr int kSegCap = 1040;       // segment slots per (gemm, family); >= 2 * (E + 1)
 // fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
-// the weights from L2; 32 keeps the kernels' registers low enough for 3 or more wavefronts per
-// SIMD), h columns per gate/up tile (one whole 128-column requantisation block), y columns per
-// down tile
+// the weights from L2; with 32 the down kernel fits three wavefronts per SIMD, while the gate/up
+// kernel, which holds two K blocks of gate and up weights in flight, needs 256 VGPRs and runs one
+// wavefront per SIMD), h columns per gate/up tile (one whole 128-column requantisation block), y
+// columns per down tile
 constexpr int kStreamMaxRows8 = 32;
 constexpr int kStream8BNGateUp = 128;
 constexpr int kStream8BNDown = 64;

@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4 = 0, 1, 2
 CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
+LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 
@@ -30,11 +31,13 @@ class Problem(ctypes.Structure):
                 ("d_ff_shared", ctypes.c_int32), ("config", ctypes.c_int32)]
 
 
+WEIGHT_POINTERS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                   "sh_gate", "sh_up", "sh_down", "s_sh_gate", "s_sh_up", "s_sh_down",
+                   "e_gate", "e_up", "e_down")
+
+
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in (
-        "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-        "sh_gate", "sh_up", "sh_down", "s_sh_gate", "s_sh_up", "s_sh_down",
-        "e_gate", "e_up", "e_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_POINTERS] + [("layout", ctypes.c_int32)]
 
 
 class Routing(ctypes.Structure):
@@ -131,9 +134,17 @@ class ExpertWeights:
 
     def struct(self) -> Weights:
         w = Weights()
-        for name, _ in Weights._fields_:
+        for name in WEIGHT_POINTERS:
             key = {"w_gate": "gate", "w_up": "up", "w_down": "down"}.get(name, name)
             setattr(w, name, _ptr(getattr(self, key)))
+        w.layout = LAYOUT_ROW_MAJOR
+        if self.wdtype != DTYPE_BF16:
+            # fp8 / mxfp4 bytes count as tiled only if every weight tensor came from fp8_tile or
+            # mxfp4_tile (the library rejects row-major bytes of these formats)
+            mats = [self.gate, self.up, self.down] + (
+                [self.sh_gate, self.sh_up, self.sh_down] if self.has_shared else [])
+            if all(getattr(t, "_moe_tiled", False) for t in mats):
+                w.layout = LAYOUT_TILED
         return w
 
     @property
@@ -210,6 +221,7 @@ def mxfp4_tile(w: torch.Tensor) -> torch.Tensor:
     rows = w.numel() // w.shape[-1]
     _check(lib().moe_mxfp4_tile(_ptr(w), _ptr(out), rows, 2 * w.shape[-1], _stream()),
            "moe_mxfp4_tile")
+    out._moe_tiled = True
     return out
 
 
@@ -219,6 +231,7 @@ def fp8_tile(w: torch.Tensor) -> torch.Tensor:
     out = torch.empty_like(w)
     rows = w.numel() // w.shape[-1]
     _check(lib().moe_fp8_tile(_ptr(w), _ptr(out), rows, w.shape[-1], _stream()), "moe_fp8_tile")
+    out._moe_tiled = True
     return out
 
 

@@ -66,7 +66,8 @@ def test_host_side_argument_errors():
     assert L.moe_layer(ctypes.byref(p), 1024, 2048, ctypes.byref(w3), 4096, None, 8192, 16,
                        None) == moe.MOE_ERR_WORKSPACE
     fp8 = moe.problem(8, 256, 512, 8, 2, fp8=True)
-    assert L.moe_layer(ctypes.byref(fp8), 1024, 2048, ctypes.byref(w3), 4096, None, 8192, 1 << 40,
+    w3t = moe.Weights(w_gate=256, w_up=512, w_down=768, layout=moe.LAYOUT_TILED)
+    assert L.moe_layer(ctypes.byref(fp8), 1024, 2048, ctypes.byref(w3t), 4096, None, 8192, 1 << 40,
                        None) == moe.MOE_ERR_INVALID_ARG  # fp8 without scales
     T0 = moe.problem(0, 256, 512, 8, 2)
     assert L.moe_layer(ctypes.byref(T0), None, None, ctypes.byref(w3), None, None, None, 0,
@@ -82,16 +83,105 @@ def test_workspace_sizes_scale():
     assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(a)) > 0
 
 
-def test_mxfp4_tile_argument_errors():
-    """moe_mxfp4_tile rejects bad arguments on the host, before any launch."""
+@pytest.mark.parametrize("name,bytes_per_128", [("moe_mxfp4_tile", 64), ("moe_fp8_tile", 128)])
+def test_weight_tile_argument_errors(name, bytes_per_128):
+    """moe_mxfp4_tile and moe_fp8_tile reject bad arguments on the host, before any launch."""
     L = moe.lib()
+    fn = getattr(L, name)
     buf = ctypes.create_string_buffer(1 << 16)
     a = (ctypes.addressof(buf) + 15) // 16 * 16
     b = a + 8192
-    assert L.moe_mxfp4_tile(None, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_mxfp4_tile(a, None, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_mxfp4_tile(a + 8, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # misaligned
-    assert L.moe_mxfp4_tile(a, a + 16, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # overlap
-    assert L.moe_mxfp4_tile(a, b, 15, 128, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_mxfp4_tile(a, b, 16, 96, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_mxfp4_tile(a, b, -16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert fn(None, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert fn(a, None, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert fn(a + 8, b, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert fn(a, b + 8, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert fn(a, a + 16, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # overlap
+    assert fn(a + 512, a, 16, 128, None) == moe.MOE_ERR_INVALID_ARG  # overlap, dst below src
+    assert fn(a, b, 15, 128, None) == moe.MOE_ERR_UNSUPPORTED
+    assert fn(a, b, 16, 96, None) == moe.MOE_ERR_UNSUPPORTED
+    assert fn(a, b, -16, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert fn(a, b, 16, -128, None) == moe.MOE_ERR_INVALID_ARG
+    # 16 rows x 128 elements are 1 KB of MXFP4 and 2 KB of fp8: a destination 1 KB above the
+    # source overlaps only the fp8 source (the MXFP4 case would launch, so it is not called here)
+    if bytes_per_128 == 128:
+        assert fn(a, a + 1024, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(a, a + 2032, 16, 128, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_offset_limits():
+    """The kernels use 32-bit byte offsets: shapes whose activation, h or y buffers or one expert's
+    matrix reach 4 GiB are rejected (MOE_ERR_UNSUPPORTED), just below the limit they are not."""
+    L = moe.lib()
+    ws = L.moe_layer_workspace_bytes
+
+    def ok(*a, **kw):
+        return ws(ctypes.byref(moe.problem(*a, **kw))) > 0
+
+    # T*k*max(d, f)*2 against 2^32: n = T*k rows
+    assert ok(1 << 20, 128, 256, 8, 8) is False          # 2^23 * 256 * 2 = 2^32
+    assert ok(1 << 20, 128, 128, 8, 8) is True            # 2^31
+    assert ok((1 << 20) - 1, 256, 128, 8, 8) is True      # just below 2^32 (d is the wide one)
+    assert ok(131072, 7168, 2048, 384, 8) is False        # Kimi-shaped, 16x the workload's T
+    assert ok(8192, 7168, 2048, 384, 8) is True           # the Kimi-shaped workload itself
+    assert ok(37450, 7168, 2048, 384, 8) is False         # 299600 * 7168 * 2 >= 2^32
+    assert ok(37449, 7168, 2048, 384, 8) is True          # 299592 * 7168 * 2 < 2^32
+    # a shared expert's h [T][f_sh]
+    assert ok(1 << 16, 128, 128, 8, 1, shared_f=1 << 15) is False
+    # one expert's [f][d] matrix
+    assert ok(4, 65536, 32768, 8, 2) is False
+    assert ok(4, 65536, 32640, 8, 2) is True
+    big = moe.problem(131072, 7168, 2048, 384, 8)
+    w = moe.Weights(w_gate=256, w_up=512, w_down=768)
+    assert L.moe_layer(ctypes.byref(big), 1024, 2048, ctypes.byref(w), 4096, None, 8192, 1 << 40,
+                       None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_ffn(ctypes.byref(big), 1024, None, 2048, 4096, ctypes.byref(w), 8192,
+                             16384, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(big)) == 0
+    # activation quantisation: T * d / 128 groups; permute's gather: T * k * d / 128 scales
+    assert L.moe_quant_act(1024, 1 << 24, 128 * 128, 2048, 4096, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_permute(1024, 1 << 20, 8, 8, 2048, 4096, 256 * 128, moe.DTYPE_FP8, 256, 512, 768,
+                         1280, 8192, None, 16384, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_narrow_weight_formats_need_the_tiled_layout():
+    """fp8 and mxfp4 weight bytes have the same size in either layout, so the caller tags them:
+    row-major bytes of these formats (or bf16 weights tagged tiled) are rejected before any work."""
+    L = moe.lib()
+    ptrs = dict(w_gate=256, w_up=512, w_down=768, s_gate=1024, s_up=1280, s_down=1536,
+                e_gate=1792, e_up=2048, e_down=2304)
+    for wd in (moe.DTYPE_FP8, moe.DTYPE_MXFP4):
+        p = moe.problem(8, 256, 512, 8, 2, wdtype=wd)
+        row = moe.Weights(**ptrs, layout=moe.LAYOUT_ROW_MAJOR)
+        tiled = moe.Weights(**ptrs, layout=moe.LAYOUT_TILED)
+        assert L.moe_layer(ctypes.byref(p), 4096, 8192, ctypes.byref(row), 16384, None, 32768, 16,
+                           None) == moe.MOE_ERR_INVALID_ARG
+        # tagged tiled, the call gets as far as the (too small) workspace
+        assert L.moe_layer(ctypes.byref(p), 4096, 8192, ctypes.byref(tiled), 16384, None, 32768, 16,
+                           None) == moe.MOE_ERR_WORKSPACE
+        assert L.moe_grouped_ffn(ctypes.byref(p), 4096, 4352, 8192, 12288, ctypes.byref(row),
+                                 16384, 32768, 16, None) == moe.MOE_ERR_INVALID_ARG
+    bf = moe.problem(8, 256, 512, 8, 2)
+    assert L.moe_layer(ctypes.byref(bf), 4096, 8192,
+                       ctypes.byref(moe.Weights(w_gate=256, w_up=512, w_down=768,
+                                                layout=moe.LAYOUT_TILED)),
+                       16384, None, 32768, 16, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_tags_only_tiled_tensors():
+    """The binding sets the tiled tag only when every fp8 / mxfp4 weight tensor came from
+    fp8_tile / mxfp4_tile (marked by them); bf16 weights are always row-major."""
+    import torch
+    g = torch.zeros((2, 128, 128), dtype=torch.uint8)
+    u, dn = torch.zeros_like(g), torch.zeros_like(g)
+    s = torch.ones((2, 1, 1), dtype=torch.float32)
+    ew = moe.ExpertWeights(gate=g, up=u, down=dn, s_gate=s, s_up=s, s_down=s)
+    assert ew.struct().layout == moe.LAYOUT_ROW_MAJOR
+    for t in (g, u):
+        t._moe_tiled = True
+    assert ew.struct().layout == moe.LAYOUT_ROW_MAJOR  # down is still row-major
+    dn._moe_tiled = True
+    assert ew.struct().layout == moe.LAYOUT_TILED
+    bf = moe.ExpertWeights(gate=torch.zeros((2, 128, 128), dtype=torch.int16),
+                           up=torch.zeros((2, 128, 128), dtype=torch.int16),
+                           down=torch.zeros((2, 128, 128), dtype=torch.int16))
+    assert bf.struct().layout == moe.LAYOUT_ROW_MAJOR
