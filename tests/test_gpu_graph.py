@@ -1,9 +1,10 @@
 """GPU: the whole layer captured in a HIP graph (torch.cuda.graph over the library's launches on the
 capture stream) and replayed.  The library allocates, clears and synchronises nothing on the host
 side, so every launch of moe_layer is capturable; its counters and queues are cleared by its own
-kernels.  Each replay must give the eager call's output bit for bit, with eager work of other
-layers between the replays, and new inputs copied into the captured buffers must give the eager
-result for those inputs."""
+kernels.  Each replay must give the eager call's output bit for bit and lie within the tolerance
+of the oracle's output (2e-2 * max|ref|, 6e-2 for fp8 weights), with eager work of other layers
+between the replays; new inputs copied into the captured buffers must give the eager result for
+those inputs, again within the tolerance of the oracle's output for them."""
 from dataclasses import replace
 
 import numpy as np
@@ -11,8 +12,9 @@ import pytest
 import torch
 
 from mixture_experts_layer_top_amd import inputs as I
+from oracle import moe_oracle as O
 
-from helpers import Inputs
+from helpers import BF16_TOL, FP8_TOL, Inputs, bits_to_f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -51,12 +53,21 @@ def _layer(moe, inp):
     return moe.Layer(inp.expert_weights(), inp.p.T, inp.p.E, inp.p.k)
 
 
+def _oracle_out(inp):
+    p = inp.p
+    return O.moe_layer(inp.logits, inp.x, p.k, inp.get, inp.get_shared(),
+                       act_fp8=p.wdtype == I.WDT_FP8)["out"]
+
+
 @pytest.mark.parametrize("p", GRAPH_CASES, ids=lambda p: p.name)
 def test_layer_graph_replay(moe, p):
+    tol = FP8_TOL if p.wdtype == I.WDT_FP8 else BF16_TOL
     inp = Inputs(p)
+    ref = _oracle_out(inp)
     L = _layer(moe, inp)
     eager = L(inp.d_logits, inp.d_x).clone()
     torch.cuda.synchronize()
+    assert rel_err(bits_to_f64(eager), ref) <= tol
 
     static_logits = inp.d_logits.clone()
     static_x = inp.d_x.clone()
@@ -79,6 +90,7 @@ def test_layer_graph_replay(moe, p):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+        assert rel_err(bits_to_f64(out), ref) <= tol
         L_other(other.d_logits, other.d_x)
         torch.cuda.synchronize()
 
@@ -91,3 +103,4 @@ def test_layer_graph_replay(moe, p):
     torch.cuda.synchronize()
     assert torch.equal(out, fresh)
     assert not torch.equal(fresh, eager)
+    assert rel_err(bits_to_f64(out), _oracle_out(other)) <= tol
