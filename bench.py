@@ -2,13 +2,19 @@
 """Benchmark of the fused MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T T] [--alpha A]
+    python bench.py --select-sweep [--sweep-T 1,4,16,64,256] [--sweep-eeff 8,32,128,224]
 
 One step = one call of the whole layer (route -> permute -> [fp8 activation quantisation] ->
 tile selection -> gate/up GEMM + SwiGLU -> down GEMM -> combine) on one batch of synthetic inputs
-already resident in HBM.  The default workload is the Mixtral-8x7B-shaped prefill layer
-(T=4096, d=4096, f=14336, E=8, k=2, bf16).  Prints one JSON line with tokens/s, the roofline of the
-dominant kernel (timed with HIP events on the stream the library launches on) and the CPU oracle's
-throughput on a bounded sample of the same workload.
+already resident in HBM.  The default workload is the largest one that fits one GPU, the
+Kimi-K2-shaped prefill layer (T=8192, d=7168, f=2048, E=384, k=8, Dirichlet(0.3) routing, bf16).
+Before every step a 512 MiB read evicts L2 and the MALL; HIP events on the library's stream bracket
+each step, and the per-step median is the reported time.  Prints one JSON line with tokens/s, the
+roofline of the dominant kernel (timed with HIP events on the stream the library launches on) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+
+--select-sweep instead times the device's tile-family choice against each family forced, over a
+grid of batch sizes and routing skews on DeepSeek-V3-shaped layers, and prints a markdown table.
 """
 from __future__ import annotations
 
@@ -254,20 +260,86 @@ def vendor_dense(args, p, gu_ms, dn_ms, alg):
     return res
 
 
+def select_sweep(args) -> int:
+    """The device's per-expert tile choice against each family forced, over a grid of batch sizes
+    and routing skews, on DeepSeek-V3-shaped layers (d = 7168, f = 2048, E = 256, k = 8).
+
+    Skew is set by its effective expert count ("Decoding the Skew ...", Abstract: kernels are
+    chosen from the live routing histogram; skew is modelled with Dirichlet draws): each target
+    count fixes the Dirichlet concentration through the closed-form expected entropy
+    (inputs.alpha_for_eeff), and the table reports the count measured on the routed histogram as
+    well.  Each configuration: 3 warm-up calls, then --steps calls, each after a 512 MiB read that
+    evicts L2 and the MALL, HIP events around the layer, median.  The last column prices a static
+    token-count bucket (the dispatch the pages contrast with a distribution-aware one): T*k/E <= 8
+    -> every expert on the streaming tiles, else every expert on MFMA tiles."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_top_amd import inputs as I
+    from mixture_experts_layer_top_amd import moe
+    Ts = [int(v) for v in args.sweep_T.split(",")]
+    targets = [float(v) for v in args.sweep_eeff.split(",")]
+    base = I.DSV3
+    W = I.gen_weights(base, "cuda")
+    ew = moe.ExpertWeights(gate=W["gate"], up=W["up"], down=W["down"])
+    scratch = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def time_layer(layer, logits, x):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            layer(logits, x)
+        ts = []
+        for _ in range(args.steps):
+            scratch.view(torch.int64).sum()
+            e0.record()
+            layer(logits, x)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    print("| T | E_eff target | alpha | E_eff routed | n_active | device ms | stream ms | MFMA ms "
+          "| device / best | static bucket / device |")
+    print("|---|---|---|---|---|---|---|---|---|---|", flush=True)
+    for T in Ts:
+        for tgt in targets:
+            alpha = I.alpha_for_eeff(base.E, tgt)
+            p = I.Problem(f"sweep_T{T}_e{tgt:g}", base.cfg_index, T=T, d=base.d, f=base.f, E=base.E,
+                          k=base.k, routing="dirichlet", alpha=alpha)
+            logits = torch.from_numpy(I.gen_logits(p)).cuda()
+            x = torch.from_numpy(I.gen_x(p).view(np.int16)).cuda()
+            ms, counts = {}, None
+            for name, cfg in (("device", moe.CONFIG_AUTO), ("stream", 0), ("mfma", 1)):
+                layer = moe.Layer(ew, T, base.E, base.k, config=cfg)
+                if counts is None:
+                    kept = {"counts": torch.zeros(base.E, dtype=torch.int32, device="cuda")}
+                    layer(logits, x, kept)
+                    counts = kept["counts"].cpu().numpy()
+                ms[name] = time_layer(layer, logits, x)
+                del layer
+            best = min(ms["stream"], ms["mfma"])
+            static = ms["stream"] if T * base.k / base.E <= 8 else ms["mfma"]
+            print(f"| {T} | {tgt:g} | {alpha:.4g} | {I.effective_experts(counts):.1f} | "
+                  f"{int((counts > 0).sum())} | {ms['device']:.3f} | {ms['stream']:.3f} | "
+                  f"{ms['mfma']:.3f} | {ms['device'] / best:.3f} | {static / ms['device']:.3f} |",
+                  flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mixtral_prefill",
+    ap.add_argument("--config", default="kimi_prefill",
                     choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode",
                              "mxfp4_dsv3_decode"])
     ap.add_argument("--T", type=int, default=None, help="tokens (overrides the workload's batch)")
     ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
     ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
-    ap.add_argument("--flush", action="store_true",
-                    help="sweep a 512 MiB buffer before every step to evict L2 and the MALL; "
-                         "the value then comes from per-step events around the layer only")
+    ap.add_argument("--no-flush", dest="flush", action="store_false",
+                    help="do not sweep a 512 MiB buffer before every step (by default L2 and the "
+                         "MALL are evicted and the value comes from the per-step events' median)")
     ap.add_argument("--flush-mode", choices=["read", "write"], default="read",
                     help="read: sum the buffer (evicts with clean lines); write: overwrite it (the "
                          "dirty lines are then written back while the layer runs)")
@@ -283,6 +355,12 @@ def main() -> int:
     ap.add_argument("--select-control", action="store_true",
                     help="also time the layer with every expert forced onto one tile family (the "
                          "control arms of the device-side selection), same protocol, fewer steps")
+    ap.add_argument("--select-sweep", action="store_true",
+                    help="only run the tile-selection sweep over --sweep-T x --sweep-eeff (markdown "
+                         "table, no JSON line)")
+    ap.add_argument("--sweep-T", default="1,4,16,64,256")
+    ap.add_argument("--sweep-eeff", default="8,32,128,224",
+                    help="target effective expert counts (each fixes a Dirichlet concentration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -301,6 +379,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.select_sweep:
+        return select_sweep(args)
     p = workload(args)
     print(f"[bench] workload {p.name}: T={p.T} d={p.d} f={p.f} E={p.E} k={p.k} {p.wdtype}"
           f"{' +shared' if p.shared else ''}", file=sys.stderr, flush=True)
@@ -348,14 +428,16 @@ def main() -> int:
         layer(d_logits, d_x, keep={"counts": counts})
         torch.cuda.synchronize()
 
-    # Timed region: K steps.  Every timing event costs GPU time (a few microseconds, which matters
-    # at decode sizes), so odd steps record only the two events around the dominant kernel (the
-    # gate/up GEMM, for the roofline) and, when flushing, even steps only the layer's first and
-    # last event (for the per-step times); with K = 1 the one step records both.
+    # Timed region: K steps, each after the cache flush.  Every timing event costs GPU time (a few
+    # microseconds, which matters at decode sizes), so at decode sizes odd steps record only the
+    # two events around the dominant kernel (the gate/up GEMM, for the roofline) and even steps only
+    # the layer's first and last event (for the per-step times); prefill steps (T >= 512, where
+    # they are noise) record all four, and with K = 1 the one step records all four.
     GU0, GU1, LAST = 4, 5, moe.TRACE_EVENTS - 1
+    every = p.T >= 512 or K == 1
     def keep(i):
-        gu = i % 2 == 1 or K == 1
-        ends = args.flush and (i % 2 == 0)
+        gu = every or i % 2 == 1
+        ends = every or i % 2 == 0
         return ({GU0, GU1} if gu else set()) | ({0, LAST} if ends else set())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -421,17 +503,15 @@ def main() -> int:
 
     n_active = int((counts.cpu() > 0).sum())
     alg = algorithmic(p, n_active)
+    ms_per_step = statistics.median(step_ms)
+    q = statistics.quantiles(step_ms, n=10) if len(step_ms) >= 2 else [step_ms[0]] * 9
+    step_spread = {"p10_ms": round(q[0], 4), "p50_ms": round(ms_per_step, 4), "p90_ms": round(q[8], 4),
+                   "samples": len(step_ms), "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4)}
     if args.flush:
-        ms_per_step = statistics.median(step_ms)
-        timing = ("median of per-step events around the layer (steps without the gate/up events); "
-                  f"512 MiB cache flush ({args.flush_mode}) before each step")
-        q = statistics.quantiles(step_ms, n=10) if len(step_ms) >= 2 else [step_ms[0]] * 9
-        step_spread = {"p10_ms": round(q[0], 4), "p50_ms": round(ms_per_step, 4), "p90_ms": round(q[8], 4)}
+        timing = ("median of per-step HIP events around the layer; a 512 MiB read "
+                  f"({args.flush_mode}) evicts L2 and the MALL before each step")
     else:
-        ms_per_step = wall * 1e3 / K
-        timing = ("wall clock over the timed steps (synchronised before and after; every second "
-                  "step also records the two gate/up events)")
-        step_spread = None
+        timing = "median of per-step HIP events around the layer, no cache flush"
     value = p.T / (ms_per_step * 1e-3)
 
     peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" else PEAK_BF16_TFLOPS
@@ -482,8 +562,7 @@ def main() -> int:
                                 "timing event adds ~5 us of GPU time)",
                   "timing": timing},
     }
-    if step_spread:
-        out["layer"]["step_ms"] = step_spread
+    out["layer"]["step_ms"] = step_spread
     if graph:
         out["graph_replay"] = graph
     if args.vendor_dense and p.wdtype == "bf16":
@@ -497,7 +576,7 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 512}.get(p.name, p.T)
+        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 32}.get(p.name, p.T)
         print(f"[bench] CPU oracle on {sample} tokens ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, logits, x, W, sample)
     print(json.dumps(out), flush=True)
