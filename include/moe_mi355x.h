@@ -47,7 +47,8 @@
  *     (every activation, h and y buffer and each expert matrix below 4 GiB); moe_quant_act needs
  *     T*d/128 < 2^31 and moe_permute's gather T*k*d/128 < 2^31.  Outside them: MOE_ERR_UNSUPPORTED.
  *   - Calls are reentrant: no mutable global state (the device's compute-unit count is queried on
- *     every call); concurrent calls need distinct workspaces.
+ *     every call); concurrent calls need distinct workspaces.  The one exception is
+ *     moe_layer_noalloc, whose workspace is a static per-GPU array (see its declaration).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -222,6 +223,24 @@ size_t moe_layer_workspace_bytes(const moe_problem* p);
 int moe_layer_traced(const moe_problem* p, const float* logits, const void* x,
                      const moe_weights* w, void* out, const moe_routing* keep, void* ws,
                      size_t ws_bytes, hipEvent_t* events, int num_events, hipStream_t stream);
+
+/* moe_layer without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The workspace
+ * is a static device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU the
+ * library runs on, held until the process ends; the caller still passes inputs and outputs.
+ * Results are moe_layer's, bit for bit (same kernels).
+ *   - MOE_ERR_WORKSPACE if moe_layer_workspace_bytes(p) exceeds MOE_NOALLOC_SCRATCH_BYTES (bf16
+ *     DeepSeek-V3-shaped decode fits up to T = 256; Mixtral- or Kimi-shaped prefill does not).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents (the
+ *     layer clears what it needs at zero itself): calls that overlap on one GPU -- several
+ *     streams or host threads -- race and give wrong results.  Serialise them.
+ *   - The first call on a device looks up the array's address there (hipGetSymbolAddress, with that
+ *     device current) and keeps it; MOE_ERR_HIP if the lookup fails.  No hipMalloc, hipFree or
+ *     other allocation, no synchronisation. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int moe_layer_noalloc(const moe_problem* p, const float* logits, const void* x,
+                      const moe_weights* w, void* out, const moe_routing* keep,
+                      hipStream_t stream);
 
 /* Static name of a status code. */
 const char* moe_status_string(int status);

@@ -198,7 +198,9 @@ const char* moe_status_string(int status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null, misaligned or out-of-range argument";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype outside the supported limits";
-    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_WORKSPACE:
+      return "MOE_ERR_WORKSPACE: workspace missing or too small (moe_layer_noalloc: the problem "
+             "needs more than the library's static scratch)";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
     default: return "unknown moe status";
   }

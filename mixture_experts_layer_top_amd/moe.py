@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "moe_status_string": (ctypes.c_char_p, [_i]),
             "moe_mxfp4_tile": (_i, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
             "moe_fp8_tile": (_i, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
+            "moe_layer_noalloc": (_i, [ctypes.POINTER(Problem), _vp, _vp, ctypes.POINTER(Weights),
+                                       _vp, ctypes.POINTER(Routing), _vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -88,7 +90,9 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
             "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
             "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string", "moe_mxfp4_tile",
-            "moe_fp8_tile")
+            "moe_fp8_tile", "moe_layer_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 TRACE_EVENTS = 8
 TRACE_PHASES = ("route", "permute", "quant", "select", "gate_up", "down", "combine")
@@ -329,3 +333,24 @@ def layer(logits, x, weights: ExpertWeights, k: int, config: int = CONFIG_AUTO, 
                     slot_dst=torch.empty(n, dtype=torch.int32, device=dev))
     out = L(logits, x, keep)
     return (out, keep) if keep_routing else out
+
+
+def layer_noalloc(logits, x, weights: ExpertWeights, k: int, out=None, config: int = CONFIG_AUTO,
+                  keep: dict | None = None):
+    """The whole layer on the library's static per-GPU scratch (moe_layer_noalloc): nothing is
+    allocated for the call apart from `out` when the caller passes none."""
+    T, E = logits.shape
+    d = weights.d_model
+    f = weights.gate.shape[1]
+    shf = weights.sh_gate.shape[0] if weights.has_shared else 0
+    p = problem(T, d, f, E, k, shared_f=shf, config=config, wdtype=weights.wdtype)
+    w = weights.struct()
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.int16, device=logits.device)
+    r = Routing()
+    if keep:
+        for name in keep:
+            setattr(r, name, _ptr(keep[name]))
+    _check(lib().moe_layer_noalloc(ctypes.byref(p), _ptr(logits), _ptr(x), ctypes.byref(w),
+                                   _ptr(out), ctypes.byref(r), _stream()), "moe_layer_noalloc")
+    return out

@@ -185,3 +185,23 @@ def test_binding_tags_only_tiled_tensors():
                            up=torch.zeros((2, 128, 128), dtype=torch.int16),
                            down=torch.zeros((2, 128, 128), dtype=torch.int16))
     assert bf.struct().layout == moe.LAYOUT_ROW_MAJOR
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """moe_layer_noalloc checks the workspace its problem needs against the static scratch on the
+    host, before any device call."""
+    L = moe.lib()
+    ws = L.moe_layer_workspace_bytes
+    small = moe.problem(256, 7168, 2048, 256, 8)  # DeepSeek-V3-shaped decode, T = 256
+    big = moe.problem(512, 7168, 2048, 256, 8)
+    assert 0 < ws(ctypes.byref(small)) <= moe.NOALLOC_SCRATCH_BYTES < ws(ctypes.byref(big))
+    w = moe.Weights(w_gate=256, w_up=512, w_down=768)
+    assert L.moe_layer_noalloc(ctypes.byref(big), 1024, 2048, ctypes.byref(w), 4096, None,
+                               None) == moe.MOE_ERR_WORKSPACE
+    mixtral = moe.problem(4096, 4096, 14336, 8, 2)
+    assert L.moe_layer_noalloc(ctypes.byref(mixtral), 1024, 2048, ctypes.byref(w), 4096, None,
+                               None) == moe.MOE_ERR_WORKSPACE
+    bad = moe.problem(8, 250, 512, 8, 2)  # invalid problems keep moe_layer's codes
+    assert L.moe_layer_noalloc(ctypes.byref(bad), 1024, 2048, ctypes.byref(w), 4096, None,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    assert b"static scratch" in L.moe_status_string(moe.MOE_ERR_WORKSPACE)
