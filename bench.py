@@ -576,7 +576,7 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 32}.get(p.name, p.T)
+        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 128}.get(p.name, p.T)
         print(f"[bench] CPU oracle on {sample} tokens ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, logits, x, W, sample)
     print(json.dumps(out), flush=True)
