@@ -5,6 +5,7 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,15 +32,47 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# Every kernel must keep its registers: the compiler's resource-usage remarks are read back and a
+# kernel that spills to scratch memory fails the build.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def kernel_resources(remarks: str) -> dict[str, dict[str, str]]:
+    """Per-kernel fields of the compiler's kernel-resource-usage remarks (VGPRs, AGPRs,
+    ScratchSize [bytes/lane], Occupancy [waves/SIMD], ...)."""
+    out: dict[str, dict[str, str]] = {}
+    cur = None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: (.*?) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if not m:
+            continue
+        key, _, val = m.group(1).partition(":")
+        if key.strip() == "Function Name":
+            cur = out.setdefault(val.strip(), {})
+        elif cur is not None:
+            cur[key.strip()] = val.strip()
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *HIP_FLAGS, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *COMMON, RESOURCE_REMARKS, "-x", "hip", "-c", src, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if src.endswith(".hip"):
+        res = kernel_resources(r.stderr)
+        with open(obj + ".resources.txt", "w") as fh:
+            for name, f in sorted(res.items()):
+                fh.write(f"{name}: " + ", ".join(f"{k}={v}" for k, v in f.items()) + "\n")
+        spills = {n: f.get("ScratchSize [bytes/lane]") for n, f in res.items()
+                  if f.get("ScratchSize [bytes/lane]", "0") != "0"}
+        if spills:
+            raise RuntimeError(f"{os.path.basename(src)}: kernels use scratch memory (register "
+                               f"spills), bytes per lane: {spills}")
     return obj
 
 

@@ -111,7 +111,6 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 struct FfnWs {
   Seg* segs;
   int32_t* meta;
-  int32_t* split_cnt;
   float* split_part;
   void* h;
   float* hs;
@@ -125,12 +124,8 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
   const size_t wb = p->wdtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
   f.segs = c.take<Seg>((size_t)2 * kNumFam * kSegCap);
   f.meta = c.take<int32_t>(2 * kNumFam * kMetaStride);
-  f.split_cnt = nullptr;
   f.split_part = nullptr;
-  if (wb == 2) {
-    f.split_cnt = c.take<int32_t>((size_t)2 * kSplitMaxPieces);
-    f.split_part = c.take<float>((size_t)kSplitMaxPieces * kSplitSlotFloats);
-  }
+  if (wb == 2) f.split_part = c.take<float>((size_t)kSplitMaxPieces * kSplitSlotFloats);
   f.h = c.take<uint8_t>(n * p->d_ff * wb);
   f.hs = wb == 1 ? c.take<float>(n * (p->d_ff / 128)) : nullptr;
   f.h_sh = f.hs_sh = nullptr;
@@ -146,25 +141,32 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
 // kernel (whose queue would be empty) is not launched when no expert can pass the streaming
 // threshold, nor when the selection's few-tile rule must move every expert to the streaming tiles:
 // no expert exceeds kFewTileRows rows and even one m-tile per expert that can hold rows would not
-// make 1.6 rounds of CUs.
+// make 1.6 rounds of CUs.  The split epilogue follows the MFMA kernel unless no list can split: a
+// split needs fewer than kSplitMaxRounds rounds of MFMA tiles, and the MFMA rows are at least the
+// rows of every expert above the streaming threshold, so when those alone fill kSplitMaxRounds
+// rounds at full tile height no split can happen.
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, int cus, hipStream_t s) {
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
-    return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, s, true);
+    return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, false, s, true);
   const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
   const bool stream = p->config != MOE_CONFIG_MFMA;
   bool mfma = p->config == MOE_CONFIG_MFMA || (p->config == MOE_CONFIG_AUTO && max_rows > thr);
+  const int64_t nt = gemm == kGemmGateUp ? p->d_ff / kMfmaBNGateUp
+                                         : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
   if (mfma && p->config == MOE_CONFIG_AUTO && max_rows <= kFewTileRows && !p->has_shared) {
     const int64_t experts = std::min<int64_t>(p->num_experts, total_rows);
-    const int64_t nt = gemm == kGemmGateUp ? p->d_ff / kMfmaBNGateUp
-                                           : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
     if (5 * experts * nt < kFewTileRounds5 * (int64_t)cus) mfma = false;
   }
+  const int64_t light = p->config == MOE_CONFIG_MFMA ? 0 : (int64_t)thr * p->num_experts;
+  const int64_t min_tiles = (std::max<int64_t>(0, total_rows - light) + kMfmaBM - 1) / kMfmaBM * nt;
+  const bool maybe_split =
+      min_tiles < (int64_t)kSplitMaxRounds * std::min(cus, kSplitMaxPieces);
   const int max_k = gemm == kGemmGateUp ? p->d_model
                                          : std::max(p->d_ff, p->has_shared ? p->d_ff_shared : 0);
-  return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k, stream, mfma, s, false);
+  return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k, stream, mfma, maybe_split, s, false);
 }
 }  // namespace
 
@@ -315,7 +317,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
   a.h = f.h; a.hs = f.hs;
   a.y = y_perm;
-  SelectOut o{f.segs, f.meta, f.split_cnt, f.split_part};
+  SelectOut o{f.segs, f.meta, f.split_part};
   hipError_t e = launch_select(a, o, stream);
   const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
   if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, n, n, cus, stream);
@@ -434,7 +436,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.h = L.ffn.h; a.hs = L.ffn.hs;
   a.h_sh = L.ffn.h_sh; a.hs_sh = L.ffn.hs_sh;
   a.y = L.y; a.y_sh = L.ffn.y_sh;
-  SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_cnt, L.ffn.split_part};
+  SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_part};
 
   hipError_t e = mark(0);
   // a single bf16 token without a shared expert: routing runs inside the gate/up kernel, which

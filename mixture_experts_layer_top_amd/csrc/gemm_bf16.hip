@@ -441,11 +441,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define MOE_WAITCNT(vm, lg) \
   __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | 0x70 | (((lg) & 15) << 8))
 
+// The thread index through an opaque move: values the epilogues derive from it are computed there,
+// instead of being hoisted out of the persistent tile loop and kept alive (or spilled) across the
+// whole K loop.
+__device__ __forceinline__ uint32_t tid_here() {
+  uint32_t t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((uint32_t)threadIdx.x));
+  return t;
+}
+
 // Epilogue of one tile: out is the GEMM's output base ([.][N] bf16), row0 + m0 its first row.
 template <bool GU>
 __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], void* out, int N, int row0,
                                               int m0, int rows, int n0) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint32_t tid = tid_here();
+    const int lane = tid & 63, wv = tid >> 6;
     const int wm = wv & 1, wn = wv >> 1;
     const int l32 = lane & 31, khalf = lane >> 5;
     // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
@@ -493,7 +503,8 @@ __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], void* o
 template <bool GU, int TB>
 __device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], void* out, int N,
                                                    int row0, int m0, int rows, int n0) {
-  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const uint32_t tid = tid_here();
+  const int lane = tid & 63, wn = tid >> 6;
   const int l32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
@@ -582,11 +593,19 @@ __device__ __forceinline__ constexpr int full_a_blk(int a) {
 // memory operations of a wavefront complete in order; the short-tile pipeline waits for them
 // explicitly, and any vmcnt wait the compiler emits for its own loads can only be stronger than
 // needed.  No output registers: the data goes to LDS only.
-__device__ __forceinline__ void dma16(gchar* src, lds_void* dst) {
+// The address is a uniform 64-bit base in SGPRs plus the lane's 32-bit byte offset (the
+// instruction's scalar-base form), so a lane keeps one offset register per load slot instead of a
+// 64-bit address.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, lds_void* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  // (readfirstlane returns int: each half goes through uint32_t so that neither is sign-extended)
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds)
+               : "v"(off), "s"(sb), "s"(lds)
                : "memory", "m0");
 }
 
@@ -667,7 +686,7 @@ struct MfmaTile {
   __device__ __forceinline__ void issue_one(int j, uint32_t ko) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint8_t* st = stage64_ptr<S>() + wv * 8 * ROWB64;
-    dma16((gchar*)slot_base<8>(j) + off[j] + ko, (lds_void*)(st + j * 32 * ROWB64));
+    dma16(slot_base<8>(j) + ko, off[j], (lds_void*)(st + j * 32 * ROWB64));
   }
 
   template <int S>
@@ -765,7 +784,7 @@ struct MfmaTile {
     constexpr int kStage = (TB * 32 + BNW) * ROWB64;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint8_t* st = g_ring + stage * kStage + wv * 8 * ROWB64;
-    dma16((gchar*)slot_base<TB>(j) + off[j] + ko, (lds_void*)(st + j * 32 * ROWB64));
+    dma16(slot_base<TB>(j) + ko, off[j], (lds_void*)(st + j * 32 * ROWB64));
   }
 
   template <int TB>
@@ -918,19 +937,14 @@ __device__ __forceinline__ int interleave_tile(int p, int heavy, int ntiles) {
   return h1 > h0 ? h0 : heavy + (p - h0);
 }
 
-// A piece of a split tile (accumulator blocks a < NA, b < NB): writes its partial sums to its slot
-// of the tile's S slots, then counts itself done; the piece that finds the other S - 1 done adds
-// the S slots in piece order into acc (its own from registers, bit-identical to its slot) and
-// returns true, and only it runs the epilogue.  Release fence before the count, acquire fence
-// after it: the slots are written and read by CUs of different XCDs (different L2s).
+// A piece of a split tile (accumulator blocks a < NA, b < NB) writes its partial sums to its slot of
+// the tile's S slots; mfma_split_epilogue adds them later.  Slot layout: 4 accumulators (16 B) per
+// thread, threads adjacent, so each store is one contiguous kilobyte per wavefront; group (a, b, q)
+// of a slot starts at float (a*16+b*4+q)*1024.  Group bases are uniform; the lane's offset is one
+// register, produced by asm so that the compiler cannot fold it into 64 per-group addresses hoisted
+// out of the tile loop (they would not fit in registers).
 template <int NA, int NB>
-__device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* tile_part, int32_t* cnt,
-                                             int S, int piece, int* lds) {
-  // slot layout: 4 accumulators (16 B) per thread, threads adjacent, so each store is one
-  // contiguous kilobyte per wavefront; group (a, b, q) of a slot starts at float (a*16+b*4+q)*1024.
-  // Group bases are uniform; the lane's offset is one register, produced by asm so that the
-  // compiler cannot fold it into 64 per-group addresses hoisted out of the tile loop (they would
-  // not fit in registers).
+__device__ __forceinline__ void split_store(const f32x16 (&acc)[4][4], float* tile_part, int piece) {
   uint32_t lane_off;
   asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(lane_off) : "v"((uint32_t)threadIdx.x));
   float* mine = tile_part + (size_t)piece * kSplitSlotFloats;
@@ -947,43 +961,6 @@ __device__ __forceinline__ bool split_reduce(f32x16 (&acc)[4][4], float* tile_pa
         v.w = __float_as_uint(acc[a][b][q * 4 + 3]);
         gstore16(mine + ((a * 4 + b) * 4 + q) * 1024, lane_off, v);
       }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *lds = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int done = __builtin_amdgcn_readfirstlane(*lds);
-  __syncthreads();  // (the next tile's queue pop reuses *lds)
-  if (done != S - 1) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_barrier(0);  // one group's loads at a time (bounded registers)
-        const float* gb = tile_part + ((a * 4 + b) * 4 + q) * 1024;
-        float t[4];
-        for (int p = 0; p < S; ++p) {
-          float v[4];
-          if (p == piece) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[a][b][q * 4 + i];
-          } else {
-            const uint4 w = gload16(gb + (size_t)p * kSplitSlotFloats, lane_off);
-            v[0] = __uint_as_float(w.x);
-            v[1] = __uint_as_float(w.y);
-            v[2] = __uint_as_float(w.z);
-            v[3] = __uint_as_float(w.w);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = p == 0 ? v[i] : t[i] + v[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[a][b][q * 4 + i] = t[i];
-      }
-  return true;
 }
 
 // The claimed tile.  The epilogue's fields are copied here so that it reads no Seg memory after
@@ -1004,8 +981,7 @@ struct MfmaQueue {
 // The persistent tile loop.  Instantiated with and without the split-K epilogue, so that lists that
 // split nothing (the common case) run code whose registers the split path does not disturb.
 template <bool GU, bool kSplit>
-__device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, int32_t* split_cnt,
-                                                float* split_part, int* slot) {
+__device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split_part, int* slot) {
   int q = 0;
   MfmaTile<GU> tile;
   auto claim = [&](MfmaCur& c) -> bool {
@@ -1047,19 +1023,22 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, int32_t* spl
     // accumulators a shorter tile leaves unused are dead around the loop
     if (cur.h == BM) {
       tile.run_full(cur.nk);
-      if (!kSplit || cur.piece < 0 ||
-          split_reduce<4, 4>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+      if (!kSplit || cur.piece < 0)
         MfmaTileStore<GU>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      else
+        split_store<4, 4>(tile.acc, part(cur), cur.piece);
     } else if (cur.h == 128) {
       tile.template run_short<4>(cur.nk);
-      if (!kSplit || cur.piece < 0 ||
-          split_reduce<2, 4>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+      if (!kSplit || cur.piece < 0)
         MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      else
+        split_store<2, 4>(tile.acc, part(cur), cur.piece);
     } else {
       tile.template run_short<2>(cur.nk);
-      if (!kSplit || cur.piece < 0 ||
-          split_reduce<2, 2>(tile.acc, part(cur), split_cnt + cur.u, Q.S, cur.piece, slot))
+      if (!kSplit || cur.piece < 0)
         MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      else
+        split_store<2, 2>(tile.acc, part(cur), cur.piece);
     }
     if (!claim(cur)) break;
   }
@@ -1068,7 +1047,6 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, int32_t* spl
 template <bool GU>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__ segs,
                                                           int32_t* __restrict__ meta,
-                                                          int32_t* __restrict__ split_cnt,
                                                           float* __restrict__ split_part) {
   __shared__ int slot;
   __shared__ int seg_base[kSegCap];
@@ -1087,8 +1065,68 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   Q.chunk = max(1, (int)gridDim.x / kXcds);
   for (int i = threadIdx.x; i < Q.nseg; i += blockDim.x) seg_base[i] = segs[i].tile_base;
   __syncthreads();
-  if (Q.S > 1) mfma_persistent<GU, true>(Q, split_cnt, split_part, &slot);
-  else mfma_persistent<GU, false>(Q, split_cnt, split_part, &slot);
+  if (Q.S > 1) mfma_persistent<GU, true>(Q, split_part, &slot);
+  else mfma_persistent<GU, false>(Q, split_part, &slot);
+}
+
+// Epilogue of the tiles split in K: workgroup u adds the S partial-sum slots of split tile u (queue
+// position sbase + u) in piece order -- so the result does not depend on which piece finished
+// first -- and stores the tile as the MFMA kernel would have.  It runs after the GEMM's MFMA kernel
+// on the same stream; with no split tiles every workgroup returns at once.  num_cus: the MFMA
+// kernel's grid (its XCD chunk size enters the chunked tile order).
+template <bool GU>
+__global__ __launch_bounds__(256, 1) void mfma_split_epilogue(const Seg* __restrict__ segs,
+                                                               const int32_t* __restrict__ meta,
+                                                               const float* __restrict__ split_part,
+                                                               int num_cus) {
+  const int ntiles = meta[1], sbase = meta[kMetaSplitBase], S = meta[kMetaSplitS];
+  const int u = blockIdx.x;
+  if (S <= 1 || sbase + u >= ntiles) return;
+  const int tp = sbase + u, order = meta[kMetaOrder], ntiles0 = meta[kMetaClass0];
+  const int chunk = max(1, num_cus / kXcds);
+  const int t = order == kOrderLongestFirst ? tp
+                : order == kOrderChunks      ? chunked_interleave(tp, ntiles0, ntiles, chunk)
+                                             : interleave_tile(tp, ntiles0, ntiles);
+  int lo = 0, hi = meta[0] - 1;  // the last segment whose first tile is <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].tile_base <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const Seg& sg = segs[lo];
+  const int local = t - sg.tile_base;
+  const int mt = local % sg.mtiles, nt = local / sg.mtiles;
+  const int m0 = mt * BM, rows = min(BM, sg.rows - m0);
+  const int n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
+  const int h = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
+  const int NA = h == BM ? 4 : 2, NB = h == BM ? 4 : h / 32;
+  const float* part = split_part + (size_t)u * S * kSplitSlotFloats;
+  const uint32_t lane_off = threadIdx.x * 16;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float t4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a < NA && b < NB) {
+          const float* gb = part + ((a * 4 + b) * 4 + q) * 1024;
+          for (int p = 0; p < S; ++p) {
+            const uint4 w = gload16(gb + (size_t)p * kSplitSlotFloats, lane_off);
+            const float v[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                __uint_as_float(w.w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t4[i] = p == 0 ? v[i] : t4[i] + v[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][b][q * 4 + i] = t4[i];
+      }
+    }
+  if (h == BM) MfmaTileStore<GU>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
+  else if (h == 128) MfmaTileStoreShort<GU, 4>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
+  else MfmaTileStoreShort<GU, 2>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1268,18 +1306,22 @@ static void launch_stream_bf16(const Seg* ss, int32_t* ms, int num_cus, int64_t 
 }
 
 hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, int64_t max_rows, int max_k,
-                             bool stream, bool mfma, hipStream_t s, bool w4) {
+                             bool stream, bool mfma, bool maybe_split, hipStream_t s, bool w4) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
   const Seg* sm = o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap;
   int32_t* mm = o.meta + (g * kNumFam + kFamMfma) * kMetaStride;
-  int32_t* cnt = o.split_cnt ? o.split_cnt + g * kSplitMaxPieces : nullptr;
+  // split tiles: S >= 2 pieces each, all pieces within kSplitMaxPieces
+  constexpr int kSplitGrid = kSplitMaxPieces / 2;
+  const bool split = mfma && maybe_split && o.split_part;
   if (g == kGemmGateUp) {
     if (stream) launch_stream_bf16<true>(ss, ms, num_cus, max_rows, max_k, s, w4);
-    if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
+    if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, o.split_part);
+    if (split) mfma_split_epilogue<true><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part, num_cus);
   } else {
     if (stream) launch_stream_bf16<false>(ss, ms, num_cus, max_rows, max_k, s, w4);
-    if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, cnt, o.split_part);
+    if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, o.split_part);
+    if (split) mfma_split_epilogue<false><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part, num_cus);
   }
   return hipGetLastError();
 }

@@ -75,9 +75,10 @@ __device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
 }
 
 // Last-round split of an MFMA GEMM: when its tiles leave a last round of CUs partly idle, the
-// tiles of that round are split two or four ways in K, every piece writes its fp32 partial sums
-// to a slot of split_part, and the last piece of a tile to finish adds the slots in piece order
-// (so results do not depend on which piece finishes last) and runs the epilogue.
+// tiles of that round are split two or four ways in K, and every piece writes its fp32 partial sums
+// to a slot of split_part.  A separate epilogue kernel, launched after the MFMA kernel, adds each
+// split tile's slots in piece order (so results do not depend on which piece finished first) and
+// stores the tile.
 constexpr int kSplitMaxPieces = 256;  // partial-sum slots (one round of CUs)
 constexpr int kSplitSlotFloats = 256 * 256;  // one full tile's accumulators
 constexpr int kSplitMaxRounds = 3;    // longest-first order and split: fewer whole rounds than this
@@ -86,9 +87,8 @@ constexpr int kSplitMaxRounds = 3;    // longest-first order and split: fewer wh
 struct SelectOut {
   Seg* segs;           // [2 gemms][kNumFam][E + 1]
   int32_t* meta;       // [2 gemms][kNumFam][kMetaStride] (layout below)
-  int32_t* split_cnt;  // [2 gemms][kSplitMaxPieces] pieces finished per split tile (bf16 only)
-  float* split_part;   // [kSplitMaxPieces][kSplitSlotFloats] partial sums (bf16 only; the two
-                       // GEMMs run one after the other and share it)
+  float* split_part;   // [kSplitMaxPieces][kSplitSlotFloats] partial sums (bf16 only, else null:
+                       // no split; the two GEMMs run one after the other and share it)
 };
 
 // Everything the selection kernel needs to describe the two GEMMs.
@@ -148,9 +148,11 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
 // (rows % 16 == 0, row_bytes % cb == 0; cb = 64 for MXFP4, 128 for fp8).
 hipError_t launch_weight_tile(const void* src, void* dst, int64_t rows, int64_t row_bytes, int cb,
                               hipStream_t s);
-// w4: mxfp4 weights (streaming tiles only; mfma must be false)
+// w4: mxfp4 weights (streaming tiles only; mfma must be false).  maybe_split: the MFMA list may
+// hold tiles split in K (the host's bound), so the split epilogue kernel follows the MFMA kernel.
 hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
-                             int max_k, bool stream, bool mfma, hipStream_t s, bool w4);
+                             int max_k, bool stream, bool mfma, bool maybe_split, hipStream_t s,
+                             bool w4);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
 
 // Single-token decode (T = 1, bf16 weights, no shared expert, d <= kStreamXlMaxK): one kernel routes

@@ -261,16 +261,13 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     // (lpt[] is the same for every thread)
     m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : chunks[g] ? kOrderChunks
                                                                                       : kOrderMix;
-    if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_cnt && uniform_k) {
+    if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_part && uniform_k) {
       const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
       if (rem > 0) {
         if (rem * 4 <= C && nk % 8 == 0) S = 4;
         else if (rem * 2 <= C && nk % 4 == 0) S = 2;
       }
-      if (S > 1) {
-        base = ntl - rem;
-        for (int u = 0; u < rem; ++u) o.split_cnt[g * kSplitMaxPieces + u] = 0;
-      }
+      if (S > 1) base = ntl - rem;
     }
     m[kMetaSplitBase] = base;
     m[kMetaSplitS] = S;
