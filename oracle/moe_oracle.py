@@ -31,6 +31,9 @@ plainest reading of a top-k softmax-routed SwiGLU MoE layer:
            s = fp32(amax / 448) (s = 1 when amax = 0), q = e4m3(fp32(x / s)); the experts then see
            q * s.  The oracle runs the experts on these dequantised values in float64 and does not
            requantise H.
+  mxfp8    (MXFP4 weights with 8-bit activations) activations are quantised by the layer to OCP
+           MXFP8, per token and per 32 channels (oracle/mxfp8.py); the experts see the dequantised
+           values, and again H is not requantised.
 
 Every function below follows one of these steps; all arithmetic is float64 unless stated.
 """
@@ -38,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import fp8_e4m3, mxfp4
+from . import fp8_e4m3, mxfp4, mxfp8
 
 ACT_BLOCK = 128  # activation quantisation group (channels)
 W_BLOCK = 128  # weight scale block edge
@@ -208,11 +211,27 @@ def _expert_mats(get_weights, e):
             decode_weight(raw["down"], raw.get("s_down")))
 
 
-def layer_input(x_bits, act_fp8: bool):
-    """What the experts see: the bf16 activations, or their per-token fp8 quantisation."""
-    if act_fp8:
+ACTS = ("bf16", "fp8", "mxfp8")
+
+
+def _act(act_fp8, act):
+    """The activation format: act if given, else 'fp8' or 'bf16' from the older act_fp8 flag."""
+    a = act if act is not None else ("fp8" if act_fp8 else "bf16")
+    if a not in ACTS:
+        raise ValueError(f"activation format {a!r} not in {ACTS}")
+    return a
+
+
+def layer_input(x_bits, act_fp8: bool = False, act: str | None = None):
+    """What the experts see: the bf16 activations, their per-token fp8 quantisation (1x128, fp32
+    scales) or their MXFP8 quantisation (1x32, E8M0 scales).  Returns (values, codes, scales)."""
+    a = _act(act_fp8, act)
+    if a == "fp8":
         q, s = quant_act_e4m3(x_bits)
         return dequant_act_e4m3(q, s), q, s
+    if a == "mxfp8":
+        q, s = mxfp8.quant_act(x_bits)
+        return mxfp8.dequant_rows(q, s), q, s
     return bf16_bits_to_f64(x_bits), None, None
 
 
@@ -228,23 +247,27 @@ def combine(Y, slot_dst, w, S=None):
     return out
 
 
-def moe_layer(logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False):
+def moe_layer(logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False,
+              act: str | None = None):
     """The whole layer.
 
     logits float32 [T, E]; x_bits bf16 bits [T, d]; get_weights(e) -> dict with the stored
     'gate', 'up' ([f, d]) and 'down' ([d, f]) of expert e (bf16 bits, or E4M3 codes plus
     's_gate', 's_up', 's_down' block scales); get_shared() -> the same for the shared expert.
-    Returns a dict of every intermediate the boundary exports plus 'out' (float64 [T, d])."""
-    return moe_layers([(logits, x_bits)], k, get_weights, get_shared, act_fp8)[0]
+    Returns a dict of every intermediate the boundary exports plus 'out' (float64 [T, d]).
+    act: activation format ('bf16', 'fp8', 'mxfp8'; act_fp8=True is 'fp8')."""
+    return moe_layers([(logits, x_bits)], k, get_weights, get_shared, act_fp8, act)[0]
 
 
-def moe_layers(batches, k: int, get_weights, get_shared=None, act_fp8: bool = False):
+def moe_layers(batches, k: int, get_weights, get_shared=None, act_fp8: bool = False,
+               act: str | None = None):
     """Several calls of the layer with one set of expert weights (a sweep over batch sizes or
     routing draws of one model layer), each computed exactly as moe_layer defines it; an expert's
     weights are decoded once for all the calls that route rows to it.
 
     batches: list of (logits float32 [T_i, E], x_bits bf16 bits [T_i, d]).  Returns one result dict
     per call (see moe_layer)."""
+    a = _act(act_fp8, act)
     res = []
     for logits, x_bits in batches:
         logits = np.asarray(logits, dtype=np.float32)
@@ -252,11 +275,11 @@ def moe_layers(batches, k: int, get_weights, get_shared=None, act_fp8: bool = Fa
         ids, w = route(logits, k)
         counts, offsets = histogram(ids, E)
         perm_src, slot_dst = permute(ids, E)
-        xin, xq, xs = layer_input(x_bits, act_fp8)
+        xin, xq, xs = layer_input(x_bits, act=a)
         r = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm_src=perm_src,
                  slot_dst=slot_dst, y_perm=np.zeros((T * k, xin.shape[1]), dtype=np.float64),
                  xin=xin)
-        if act_fp8:
+        if a != "bf16":
             r["xq"], r["xs"] = xq, xs
         res.append(r)
     E = res[0]["counts"].size if res else 0
@@ -285,7 +308,8 @@ def moe_layers(batches, k: int, get_weights, get_shared=None, act_fp8: bool = Fa
     return res
 
 
-def moe_tokens(tokens, logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False):
+def moe_tokens(tokens, logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False,
+               act: str | None = None):
     """Output rows for a subset of tokens, computed token by token with no permutation:
     out[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x_t) (+ FFN_shared(x_t)).  Routing, the fp8
     activation quantisation and the experts all act row by row, so this needs only the chosen
@@ -294,7 +318,7 @@ def moe_tokens(tokens, logits, x_bits, k: int, get_weights, get_shared=None, act
     logits = np.asarray(logits, dtype=np.float32)[tokens]
     x_sel = np.asarray(x_bits)[tokens]
     ids, w = route(logits, k)
-    xin, _, _ = layer_input(x_sel, act_fp8)
+    xin, _, _ = layer_input(x_sel, act_fp8, act)
     out = np.zeros((tokens.size, xin.shape[1]), dtype=np.float64)
     for e in np.unique(ids):
         Wg, Wu, Wd = _expert_mats(get_weights, int(e))
@@ -326,22 +350,30 @@ def quant_rows_e4m3_f64(v):
     return (fp8_e4m3.decode(q) * s.astype(np.float64)[:, :, None]).reshape(R, C)
 
 
-def moe_layer_emulated(logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False):
+def moe_layer_emulated(logits, x_bits, k: int, get_weights, get_shared=None, act_fp8: bool = False,
+                       act: str | None = None):
     """Same layer with the rounding a GPU implementation may add: float32 GEMM results, H and Y
-    rounded to bf16 (H requantised to fp8 per 1x128 for fp8 weights), output rounded to bf16."""
+    rounded to bf16 (H requantised per 1x128 to fp8 for fp8 activations, per 1x32 to MXFP8 for
+    MXFP8 activations), output rounded to bf16."""
+    a = _act(act_fp8, act)
     logits = np.asarray(logits, dtype=np.float32)
     T, E = logits.shape
     ids, w = route(logits, k)
     w = w.astype(np.float32).astype(np.float64)
     counts, offsets = histogram(ids, E)
     perm_src, slot_dst = permute(ids, E)
-    xin, _, _ = layer_input(x_bits, act_fp8)
+    xin, _, _ = layer_input(x_bits, act=a)
 
     def ffn(X, Wg, Wu, Wd):
         G = (X @ Wg.T).astype(np.float32).astype(np.float64)
         U = (X @ Wu.T).astype(np.float32).astype(np.float64)
         H = silu(G) * U
-        H = quant_rows_e4m3_f64(H) if act_fp8 else f64_to_bf16_f64(H)
+        if a == "fp8":
+            H = quant_rows_e4m3_f64(H)
+        elif a == "mxfp8":
+            H = mxfp8.dequant_rows(*mxfp8.quant_rows(H.astype(np.float32).astype(np.float64)))
+        else:
+            H = f64_to_bf16_f64(H)
         return f64_to_bf16_f64((H @ Wd.T).astype(np.float32).astype(np.float64))
 
     Y = np.zeros((T * k, xin.shape[1]), dtype=np.float64)
