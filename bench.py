@@ -50,8 +50,8 @@ def workload(args):
         return I.dsv3_point(args.T or 256, args.alpha if args.alpha is not None else 1.0)
     if name == "fp8_dsv3_decode":
         return I.fp8_point(args.T or 128)
-    if name == "mxfp4_dsv3_decode":
-        base = I.MXFP4
+    if name in ("mxfp4_dsv3_decode", "mxfp4a8_dsv3_decode"):
+        base = I.MXFP4 if name == "mxfp4_dsv3_decode" else I.MXFP4_A8
         T = args.T or base.T
         return replace(base, T=T, name=f"{base.name}_T{T}")
     raise SystemExit(f"unknown --config {name}")
@@ -168,7 +168,7 @@ def cpu_baseline(p, logits, x, W, sample_tokens: int):
             sh.update({"s_" + n: W["s_sh_" + n].cpu().numpy() for n in ("gate", "up", "down")})
     t0 = time.perf_counter()
     O.moe_layer(L, xs, p.k, lambda e: host[e], (lambda: sh) if sh else None,
-                act_fp8=p.wdtype == "fp8")
+                act="fp8" if p.wdtype == "fp8" else "mxfp8" if p.act_mx8 else "bf16")
     dt = time.perf_counter() - t0
     return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"first {S} of {p.T} tokens of {p.name} ({len(needed)} experts), "
@@ -333,7 +333,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="kimi_prefill",
                     choices=["mixtral_prefill", "tiny", "kimi_prefill", "dsv3_decode", "fp8_dsv3_decode",
-                             "mxfp4_dsv3_decode"])
+                             "mxfp4_dsv3_decode", "mxfp4a8_dsv3_decode"])
     ap.add_argument("--T", type=int, default=None, help="tokens (overrides the workload's batch)")
     ap.add_argument("--alpha", type=float, default=None, help="Dirichlet concentration (dsv3_decode)")
     ap.add_argument("--tile-config", type=int, default=-1, help="-1 auto, 0 stream, 1 mfma")
@@ -396,7 +396,7 @@ def main() -> int:
         kw.update(s_gate=W["s_gate"], s_up=W["s_up"], s_down=W["s_down"])
     if p.wdtype == "mxfp4":  # the library's tiled weight layout (made once, untimed)
         kw.update({n: moe.mxfp4_tile(W[n]) for n in ("gate", "up", "down")})
-        kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
+        kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"], act_mx8=p.act_mx8)
     if p.shared:
         kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
         if p.wdtype == "fp8":
@@ -548,7 +548,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "fp8", "mxfp4": "mxfp4 weights, bf16 activations"}.get(p.wdtype, "bf16"),
+        "dtype": ("mxfp4 weights, mxfp8 activations" if p.act_mx8 else
+                  {"fp8": "fp8", "mxfp4": "mxfp4 weights, bf16 activations"}.get(p.wdtype, "bf16")),
         "data": "synthetic",
         "config": {"workload": p.name, "T": p.T, "d_model": p.d, "d_ff": p.f, "experts": p.E,
                    "top_k": p.k, "routing": p.routing + (f"(alpha={p.alpha:g})" if p.routing == "dirichlet" else ""),

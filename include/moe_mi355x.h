@@ -72,8 +72,12 @@ enum moe_status {
 enum moe_dtype {
   MOE_DTYPE_BF16 = 0,
   MOE_DTYPE_FP8_E4M3 = 1,
-  MOE_DTYPE_MXFP4 = 2  /* expert weights only: bf16 activations, no shared expert, streaming tiles
+  MOE_DTYPE_MXFP4 = 2, /* expert weights only: bf16 activations, no shared expert, streaming tiles
                           only (config MOE_CONFIG_MFMA and has_shared give MOE_ERR_UNSUPPORTED) */
+  MOE_DTYPE_MXFP4_A8 = 3 /* MXFP4 expert weights with MXFP8 activations: the layer quantises x (and
+                            the SwiGLU output h) per token and 32 channels to E4M3 with one E8M0
+                            scale each (the smallest scale 2^E with amax <= 448 * 2^E), and both
+                            GEMMs run on the scaled f8f6f4 MFMA.  Same limits as MOE_DTYPE_MXFP4 */
 };
 
 /* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert and per
@@ -164,10 +168,18 @@ size_t moe_permute_workspace_bytes(int T, int E, int k);
  *   x [T][d] bf16 -> xq [T][d] e4m3, xs [T][d/128] fp32. */
 int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t stream);
 
+/* MXFP8 activation quantisation (MOE_DTYPE_MXFP4_A8): per token and per 32 channels, the shared
+ * exponent E is the smallest integer with amax <= 448 * 2^E, clamped to [-127, 127] (amax = 0: E = 0);
+ * xe = E + 127 (the E8M0 code), xq = e4m3(x * 2^-E) with nearest-even rounding and the sign kept.
+ * (GC-MoE, summary: FP4 grouped GEMMs as block-scaled matrix multiplies.)
+ *   x [T][d] bf16 -> xq [T][d] e4m3, xe [T][d/32] bytes.  d % 128 == 0. */
+int moe_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t* xe, hipStream_t stream);
+
 /* Grouped expert FFN on expert-contiguous rows: for every expert e with counts[e] > 0, rows
  * [offsets[e], offsets[e]+counts[e]) of x_perm go through (SiLU(X Wg^T) * (X Wu^T)) Wd^T; the result
  * lands in the same rows of y_perm ([rows][d] bf16, rows = offsets[E]).  bf16 weights: x_perm is
- * bf16 and x_perm_scale NULL (also for mxfp4 weights).  fp8 weights: x_perm is e4m3 with x_perm_scale [rows][d/128]; the
+ * bf16 and x_perm_scale NULL (also for mxfp4 weights; MOE_DTYPE_MXFP4_A8 quantises those bf16 rows
+ * to MXFP8 itself).  fp8 weights: x_perm is e4m3 with x_perm_scale [rows][d/128]; the
  * SwiGLU output is requantised to e4m3 per row and 128 channels before the down GEMM.  Tile
  * shapes are chosen on the device from counts (p->config may force one family).  The shared expert
  * fields of p and w are ignored here.

@@ -54,6 +54,10 @@ int check_route_shape(int T, int E, int k) {
   return MOE_OK;
 }
 
+bool is_mxfp4(const moe_problem* p) {
+  return p->wdtype == MOE_DTYPE_MXFP4 || p->wdtype == MOE_DTYPE_MXFP4_A8;
+}
+
 int check_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   int st = check_route_shape(p->T, p->num_experts, p->top_k);
@@ -61,10 +65,9 @@ int check_problem(const moe_problem* p) {
   if (p->d_model <= 0 || p->d_ff <= 0) return MOE_ERR_INVALID_ARG;
   if (p->d_model % 128 || p->d_ff % 128) return MOE_ERR_UNSUPPORTED;
   if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3 &&
-      p->wdtype != MOE_DTYPE_MXFP4)
+      p->wdtype != MOE_DTYPE_MXFP4 && p->wdtype != MOE_DTYPE_MXFP4_A8)
     return MOE_ERR_UNSUPPORTED;
-  if (p->wdtype == MOE_DTYPE_MXFP4 && (p->has_shared || p->config == MOE_CONFIG_MFMA))
-    return MOE_ERR_UNSUPPORTED;
+  if (is_mxfp4(p) && (p->has_shared || p->config == MOE_CONFIG_MFMA)) return MOE_ERR_UNSUPPORTED;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
   if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) return MOE_ERR_INVALID_ARG;
@@ -91,7 +94,7 @@ int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) 
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) {
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_INVALID_ARG;
   }
-  if (p->wdtype == MOE_DTYPE_MXFP4) {
+  if (is_mxfp4(p)) {
     if (!w->e_gate || !w->e_up || !w->e_down) return MOE_ERR_INVALID_ARG;
   }
   if (with_shared && p->has_shared) {
@@ -114,25 +117,37 @@ struct FfnWs {
   float* split_part;
   void* h;
   float* hs;
+  uint8_t* he;
+  uint8_t* xq;   // grouped FFN with MXFP8 activations: its own quantisation of x_perm
+  uint8_t* xe;
   void* h_sh;
   float* hs_sh;
   void* y_sh;
 };
 
-void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
+// grouped_ffn: the grouped-FFN entry point (which quantises x_perm itself for MXFP8 activations)
+void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, bool grouped_ffn, FfnWs& f) {
   const size_t n = (size_t)p->T * p->top_k;
-  const size_t wb = p->wdtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
+  const bool a8 = p->wdtype == MOE_DTYPE_MXFP4_A8;
+  const size_t hb = (p->wdtype == MOE_DTYPE_FP8_E4M3 || a8) ? 1 : 2;  // bytes per h value
   f.segs = c.take<Seg>((size_t)2 * kNumFam * kSegCap);
   f.meta = c.take<int32_t>(2 * kNumFam * kMetaStride);
-  f.split_part = nullptr;
-  if (wb == 2) f.split_part = c.take<float>((size_t)kSplitMaxPieces * kSplitSlotFloats);
-  f.h = c.take<uint8_t>(n * p->d_ff * wb);
-  f.hs = wb == 1 ? c.take<float>(n * (p->d_ff / 128)) : nullptr;
+  f.split_part = nullptr;  // (only bf16 weights run MFMA tiles, which may split in K)
+  if (p->wdtype == MOE_DTYPE_BF16)
+    f.split_part = c.take<float>((size_t)kSplitMaxPieces * kSplitSlotFloats);
+  f.h = c.take<uint8_t>(n * p->d_ff * hb);
+  f.hs = p->wdtype == MOE_DTYPE_FP8_E4M3 ? c.take<float>(n * (p->d_ff / 128)) : nullptr;
+  f.he = a8 ? c.take<uint8_t>(n * (p->d_ff / 32)) : nullptr;
+  f.xq = f.xe = nullptr;
+  if (a8 && grouped_ffn) {
+    f.xq = c.take<uint8_t>(n * p->d_model);
+    f.xe = c.take<uint8_t>(n * (p->d_model / 32));
+  }
   f.h_sh = f.hs_sh = nullptr;
   f.y_sh = nullptr;
   if (with_shared && p->has_shared) {
-    f.h_sh = c.take<uint8_t>((size_t)p->T * p->d_ff_shared * wb);
-    f.hs_sh = wb == 1 ? c.take<float>((size_t)p->T * (p->d_ff_shared / 128)) : nullptr;
+    f.h_sh = c.take<uint8_t>((size_t)p->T * p->d_ff_shared * hb);
+    f.hs_sh = hb == 1 ? c.take<float>((size_t)p->T * (p->d_ff_shared / 128)) : nullptr;
     f.y_sh = c.take<uint16_t>((size_t)p->T * p->d_model);
   }
 }
@@ -148,6 +163,7 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, FfnWs& f) {
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, int cus, hipStream_t s) {
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
+  if (p->wdtype == MOE_DTYPE_MXFP4_A8) return moe::launch_gemms_mx(o, gemm, cus, max_rows, s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
     return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, false, s, true);
@@ -259,6 +275,15 @@ int moe_permute(const int32_t* topk_ids, int T, int E, int k, const void* x, con
   return hip_status(e);
 }
 
+int moe_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t* xe, hipStream_t stream) {
+  if (T < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 128) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * (d / 128) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;  // 32-bit group index
+  if (T == 0) return MOE_OK;
+  if (!x || !xq || !xe) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_act_mx(x, T, d, xq, xe, stream));
+}
+
 int moe_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t stream) {
   if (T < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
   if (d % 128) return MOE_ERR_UNSUPPORTED;
@@ -272,7 +297,7 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_problem* p) {
   if (check_problem(p)) return 0;
   Carver c{nullptr};
   FfnWs f;
-  carve_ffn(c, p, false, f);
+  carve_ffn(c, p, false, true, f);
   return c.used;
 }
 
@@ -292,7 +317,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   Carver c{static_cast<uint8_t*>(ws)};
   FfnWs f;
-  carve_ffn(c, p, false, f);
+  carve_ffn(c, p, false, true, f);
   const int cus = device_cus();
   if (cus == 0) return MOE_ERR_HIP;
   SelectArgs a;
@@ -308,9 +333,12 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.config = p->config;
   a.num_cus = cus;
   a.fp8 = fp8;
-  a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
+  a.w4 = is_mxfp4(p);
+  a.mx8 = p->wdtype == MOE_DTYPE_MXFP4_A8;
   a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
-  a.x = x_perm;
+  a.x = a.mx8 ? static_cast<const void*>(f.xq) : x_perm;
+  a.xe = f.xq ? f.xe : nullptr;
+  a.he = f.he;
   a.xs = fp8 ? x_perm_scale : nullptr;
   a.tok = nullptr;
   a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
@@ -318,8 +346,10 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
   a.h = f.h; a.hs = f.hs;
   a.y = y_perm;
   SelectOut o{f.segs, f.meta, f.split_part};
-  hipError_t e = launch_select(a, o, stream);
-  const int64_t n = (int64_t)p->T * p->top_k;  // caller-given counts: any expert may hold all rows
+  const int64_t n = (int64_t)p->T * p->top_k;
+  hipError_t e = hipSuccess;
+  if (a.mx8) e = launch_quant_act_mx(x_perm, (int)n, p->d_model, f.xq, f.xe, stream);
+  if (e == hipSuccess) e = launch_select(a, o, stream);  // caller-given counts: any expert may hold all rows
   if (e == hipSuccess) e = launch_gemms(o, p, kGemmGateUp, n, n, cus, stream);
   if (e == hipSuccess) e = launch_gemms(o, p, kGemmDown, n, n, cus, stream);
   return hip_status(e);
@@ -343,6 +373,7 @@ struct LayerWs {
   float* w;
   uint8_t* xq;
   float* xs;
+  uint8_t* xe;
   void* y;
   FfnWs ffn;
 };
@@ -359,14 +390,14 @@ void carve_layer(Carver& c, const moe_problem* p, LayerWs& L) {
   L.tok = c.take<int32_t>(n);
   L.rank = c.take<int32_t>(n);
   L.hist = c.take<int32_t>((size_t)permute_nchunk((int)n) * E);
-  if (p->wdtype == MOE_DTYPE_FP8_E4M3) {
+  L.xq = nullptr;
+  L.xs = nullptr;
+  L.xe = nullptr;
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3 || p->wdtype == MOE_DTYPE_MXFP4_A8)
     L.xq = c.take<uint8_t>((size_t)p->T * p->d_model);
-    L.xs = c.take<float>((size_t)p->T * (p->d_model / 128));
-  } else {
-    L.xq = nullptr;
-    L.xs = nullptr;
-  }
-  carve_ffn(c, p, true, L.ffn);
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3) L.xs = c.take<float>((size_t)p->T * (p->d_model / 128));
+  if (p->wdtype == MOE_DTYPE_MXFP4_A8) L.xe = c.take<uint8_t>((size_t)p->T * (p->d_model / 32));
+  carve_ffn(c, p, true, false, L.ffn);
   L.y = c.take<uint16_t>(n * p->d_model);
 }
 }  // namespace
@@ -424,10 +455,13 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.config = p->config;
   a.num_cus = cus;
   a.fp8 = fp8;
-  a.w4 = p->wdtype == MOE_DTYPE_MXFP4;
+  a.w4 = is_mxfp4(p);
+  a.mx8 = p->wdtype == MOE_DTYPE_MXFP4_A8;
   a.e_gate = w->e_gate; a.e_up = w->e_up; a.e_down = w->e_down;
-  a.x = fp8 ? static_cast<const void*>(L.xq) : x;
+  a.x = (fp8 || a.mx8) ? static_cast<const void*>(L.xq) : x;
   a.xs = L.xs;
+  a.xe = L.xe;
+  a.he = L.ffn.he;
   a.tok = L.tok;
   a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
   a.s_gate = w->s_gate; a.s_up = w->s_up; a.s_down = w->s_down;
@@ -474,6 +508,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+    if (e == hipSuccess && a.mx8) e = launch_quant_act_mx(x, T, d, L.xq, L.xe, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = mark(4);
   } else {
@@ -484,6 +519,7 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
                          L.hist, stream);
     if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess && fp8) e = launch_quant_act(x, T, d, L.xq, L.xs, stream);
+    if (e == hipSuccess && a.mx8) e = launch_quant_act_mx(x, T, d, L.xq, L.xe, stream);
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess) e = launch_select(a, o, stream);
     if (e == hipSuccess) e = mark(4);

@@ -43,7 +43,10 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 //   16x16x32 bf16: lane l holds 8 bf16 of row/column (l % 16); C: lane l holds C[4*(l/16)+r][l%16].
 //   32x32x16 bf16: lane l holds 8 bf16 of row/column (l % 32);
 //                  C: lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15.
-//   16x16x128 fp8: lane l holds 32 e4m3 bytes of row/column (l % 16); C as 16x16x32.
+//   16x16x128 fp8: lane l holds 32 e4m3 bytes of row/column (l % 16); C as 16x16x32.  In hardware
+//                  lane group g = l / 16 holds K values 16 g .. + 15 and 64 + 16 g .. + 15 (an fp4
+//                  operand: 32 g .. + 31); with unit E8M0 scales only the product matters, so two
+//                  fp8 operands loaded alike (32 contiguous bytes at 32 g) still multiply correctly.
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

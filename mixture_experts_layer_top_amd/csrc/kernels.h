@@ -56,8 +56,10 @@ struct Seg {
   const float* s1;      // fp8 block scales of w1
   const uint8_t* e0;    // mxfp4: E8M0 scales of w0, [N][K/32] (w0 then holds [N][K/2] bytes)
   const uint8_t* e1;    // mxfp4: E8M0 scales of w1
-  void* out;            // output base [.][N] (bf16, or e4m3 for the fp8 gate/up GEMM)
+  const uint8_t* ae;    // mxfp8 activations: E8M0 scales [.][K/32] of the rows of `a`
+  void* out;            // output base [.][N] (bf16, or e4m3 for the fp8 and mxfp8 gate/up GEMMs)
   float* outs;          // fp8 gate/up: output scales [.][N/128]
+  uint8_t* oute;        // mxfp8 gate/up: output E8M0 scales [.][N/32]
   int32_t row0, rows, N, K;
   int32_t tile_base, mtiles, ntiles, expert;
   int32_t tn;           // output columns per tile
@@ -96,8 +98,11 @@ struct SelectArgs {
   const int32_t* counts;   // [E]
   const int32_t* offsets;  // [E + 1]
   int E, T, k, d, f, f_sh, has_shared, config, fp8;
-  int w4;                  // mxfp4 expert weights (streaming tiles, bf16 activations)
+  int w4;                  // mxfp4 expert weights (streaming tiles)
+  int mx8;                 // with mxfp8 activations (x and h quantised per 32; else bf16)
   const uint8_t* e_gate; const uint8_t* e_up; const uint8_t* e_down;  // their E8M0 scales
+  const uint8_t* xe;       // mx8: E8M0 scales of the gate/up activations [.][d/32]
+  uint8_t* he;             // mx8: E8M0 scales of h [T*k][f/32]
   int num_cus;              // compute units of the device (one MFMA-tile round)
   const void* x;           // gate/up activations (bf16 x, or e4m3 xq)
   const float* xs;         // fp8 activation scales
@@ -154,6 +159,13 @@ hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t 
                              int max_k, bool stream, bool mfma, bool maybe_split, hipStream_t s,
                              bool w4);
 hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
+// MXFP4 weights with MXFP8 activations (streaming tiles on the scaled f8f6f4 MFMA); max_rows
+// bounds any expert's rows.
+hipError_t launch_gemms_mx(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
+                           hipStream_t s);
+// x [T][d] bf16 -> MXFP8: xq [T][d] e4m3, xe [T][d/32] E8M0 (smallest scale with no saturation).
+hipError_t launch_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t* xe,
+                               hipStream_t s);
 
 // Single-token decode (T = 1, bf16 weights, no shared expert, d <= kStreamXlMaxK): one kernel routes
 // the token in every workgroup (the k selected experts are then known without a dispatch step),

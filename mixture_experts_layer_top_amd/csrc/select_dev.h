@@ -184,6 +184,8 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       sg.a = a.x;
       sg.as = a.xs;
       sg.tok = shared ? nullptr : a.tok;
+      sg.ae = a.mx8 ? a.xe : nullptr;
+      sg.oute = a.mx8 ? a.he : nullptr;
       if (shared) {
         sg.w0 = a.sh_gate;
         sg.w1 = a.sh_up;
@@ -214,6 +216,8 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       sg.s1 = nullptr;
       sg.e1 = nullptr;
       sg.outs = nullptr;
+      sg.ae = a.mx8 && !shared ? a.he : nullptr;
+      sg.oute = nullptr;
       if (shared) {
         sg.a = a.h_sh;
         sg.as = a.hs_sh;

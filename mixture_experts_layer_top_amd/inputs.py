@@ -67,6 +67,7 @@ class Problem:
     shared: bool = False
     shared_f: int = 0
     w_sigma: float = 0.02
+    act_mx8: bool = False  # mxfp4 weights: the layer quantises activations to MXFP8 (per 32)
 
     def with_T(self, T: int) -> "Problem":
         return replace(self, T=T)
@@ -87,7 +88,10 @@ FP8 = Problem("fp8_dsv3_decode", 4, T=32, d=7168, f=2048, E=256, k=8, routing="d
 MXFP4 = Problem("mxfp4_dsv3_decode", 5, T=64, d=7168, f=2048, E=256, k=8, routing="dirichlet",
                 alpha=1.0, wdtype=WDT_MXFP4)
 
-CONFIGS = {p.name: p for p in (TINY, MIXTRAL, DSV3, KIMI, FP8, MXFP4)}
+# the same layer (weights and routing draws) with MXFP8 activations on the scaled f8f6f4 MFMA
+MXFP4_A8 = replace(MXFP4, name="mxfp4a8_dsv3_decode", act_mx8=True)
+
+CONFIGS = {p.name: p for p in (TINY, MIXTRAL, DSV3, KIMI, FP8, MXFP4, MXFP4_A8)}
 
 
 def dsv3_point(T: int, alpha: float) -> Problem:

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4 = 0, 1, 2
+DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4, DTYPE_MXFP4_A8 = 0, 1, 2, 3
 CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
 LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
 
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
                                  _vp, _sz, _vp]),
             "moe_permute_workspace_bytes": (_sz, [_i, _i, _i]),
             "moe_quant_act": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+            "moe_quant_act_mx": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
             "moe_grouped_ffn": (_i, [ctypes.POINTER(Problem), _vp, _vp, _vp, _vp,
                                      ctypes.POINTER(Weights), _vp, _vp, _sz, _vp]),
             "moe_grouped_ffn_workspace_bytes": (_sz, [ctypes.POINTER(Problem)]),
@@ -88,6 +89,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_quant_act",
+            "moe_quant_act_mx",
             "moe_grouped_ffn", "moe_grouped_ffn_workspace_bytes", "moe_combine", "moe_layer",
             "moe_layer_workspace_bytes", "moe_layer_traced", "moe_status_string", "moe_mxfp4_tile",
             "moe_fp8_tile", "moe_layer_noalloc")
@@ -135,6 +137,7 @@ class ExpertWeights:
     e_gate: torch.Tensor | None = None  # mxfp4: uint8 E8M0 scales [E, f, d/32] / [E, d, f/32]
     e_up: torch.Tensor | None = None
     e_down: torch.Tensor | None = None
+    act_mx8: bool = False  # mxfp4 weights: quantise activations (and h) to MXFP8 (MOE_DTYPE_MXFP4_A8)
 
     def struct(self) -> Weights:
         w = Weights()
@@ -154,7 +157,7 @@ class ExpertWeights:
     @property
     def wdtype(self) -> int:
         if self.e_gate is not None:
-            return DTYPE_MXFP4
+            return DTYPE_MXFP4_A8 if self.act_mx8 else DTYPE_MXFP4
         return DTYPE_FP8 if self.gate.dtype == torch.uint8 else DTYPE_BF16
 
     @property
@@ -164,7 +167,7 @@ class ExpertWeights:
     @property
     def d_model(self) -> int:
         """d from the gate weights' last dim (two mxfp4 elements per byte)."""
-        return self.gate.shape[2] * (2 if self.wdtype == DTYPE_MXFP4 else 1)
+        return self.gate.shape[2] * (2 if self.wdtype in (DTYPE_MXFP4, DTYPE_MXFP4_A8) else 1)
 
     @property
     def has_shared(self) -> bool:
@@ -246,6 +249,16 @@ def quant_act(x: torch.Tensor):
     xs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
     _check(lib().moe_quant_act(_ptr(x), T, d, _ptr(xq), _ptr(xs), _stream()), "moe_quant_act")
     return xq, xs
+
+
+def quant_act_mx(x: torch.Tensor):
+    """bf16 [T, d] (int16 bits) -> MXFP8: e4m3 codes [T, d] and E8M0 scale codes [T, d/32]."""
+    T, d = x.shape
+    dev = _dev(x)
+    xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+    xe = torch.empty((T, d // 32), dtype=torch.uint8, device=dev)
+    _check(lib().moe_quant_act_mx(_ptr(x), T, d, _ptr(xq), _ptr(xe), _stream()), "moe_quant_act_mx")
+    return xq, xe
 
 
 def grouped_ffn(x_perm, x_perm_scale, counts, offsets, weights: ExpertWeights, T: int, k: int,

@@ -10,6 +10,16 @@ BF16_TOL = 2e-2
 FP8_TOL = 6e-2
 
 
+def act_of(p) -> str:
+    """The oracle's activation format for a workload."""
+    return "fp8" if p.wdtype == I.WDT_FP8 else "mxfp8" if p.act_mx8 else "bf16"
+
+
+def tol_of(p) -> float:
+    """8-bit activations (fp8, MXFP8) take the fp8 bar, bf16 activations the bf16 one."""
+    return FP8_TOL if act_of(p) != "bf16" else BF16_TOL
+
+
 def bits_to_f64(t) -> np.ndarray:
     """bf16 bit patterns (int16 tensor / uint16 array) -> float64 (test-side decode)."""
     a = t.cpu().numpy() if isinstance(t, torch.Tensor) else np.asarray(t)
@@ -46,7 +56,7 @@ class Inputs:
             if getattr(self, "_tiled", None) is None:
                 self._tiled = {n: mxfp4_tile(W[n]) for n in ("gate", "up", "down")}
             kw.update(self._tiled)
-            kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"])
+            kw.update(e_gate=W["s_gate"], e_up=W["s_up"], e_down=W["s_down"], act_mx8=self.p.act_mx8)
         if self.p.shared:
             kw.update(sh_gate=W["sh_gate"], sh_up=W["sh_up"], sh_down=W["sh_down"])
             if self.p.wdtype == I.WDT_FP8:

@@ -20,7 +20,7 @@ import torch
 from mixture_experts_layer_top_amd import inputs as I
 from oracle import moe_oracle as O
 
-from helpers import BF16_TOL, FP8_TOL, Inputs, bits_to_f64, rel_err
+from helpers import BF16_TOL, FP8_TOL, Inputs, act_of, bits_to_f64, rel_err, tol_of
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -76,11 +76,11 @@ def _check_whole(moe, inp, ref, tol):
     return err
 
 
-def _oracle_points(inps, act_fp8=False):
+def _oracle_points(inps):
     """Whole-layer oracle results of several workload points that share one set of weights."""
     first = inps[0]
     return O.moe_layers([(i.logits, i.x) for i in inps], first.p.k, first.get,
-                        first.get_shared(), act_fp8=act_fp8)
+                        first.get_shared(), act=act_of(first.p))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -125,7 +125,7 @@ FP8_POINTS = [I.fp8_point(T) for T in I.FP8_TS]
 def fp8(moe):
     first = Inputs(FP8_POINTS[0])
     inps = [first] + [Inputs(p, weights=first.W) for p in FP8_POINTS[1:]]
-    refs = _oracle_points(inps, act_fp8=True)
+    refs = _oracle_points(inps)
     return {i.p.name: (i, r) for i, r in zip(inps, refs)}
 
 
@@ -157,6 +157,27 @@ def mxfp4(moe):
 def test_mxfp4_decode_full(moe, mxfp4, p):
     inp, ref = mxfp4[p.name]
     _check_whole(moe, inp, ref, BF16_TOL)
+
+
+# ------------------------------------------------------------------------------------------------
+# MXFP4 experts with MXFP8 activations (scaled f8f6f4 MFMA): T = 1, 16, 64, 256, every token
+# ------------------------------------------------------------------------------------------------
+
+MXA8_POINTS = [replace(I.MXFP4_A8, T=T, name=f"{I.MXFP4_A8.name}_T{T}") for T in I.DSV3_TS]
+
+
+@pytest.fixture(scope="module")
+def mxa8(moe, mxfp4):
+    W = next(iter(mxfp4.values()))[0].W  # the same weights as the W4A16 points
+    inps = [Inputs(p, weights=W) for p in MXA8_POINTS]
+    refs = _oracle_points(inps)
+    return {i.p.name: (i, r) for i, r in zip(inps, refs)}
+
+
+@pytest.mark.parametrize("p", MXA8_POINTS, ids=lambda p: p.name)
+def test_mxfp4_a8_decode_full(moe, mxa8, p):
+    inp, ref = mxa8[p.name]
+    _check_whole(moe, inp, ref, tol_of(p))
 
 
 # ------------------------------------------------------------------------------------------------

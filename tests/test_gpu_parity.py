@@ -10,7 +10,8 @@ import torch
 from mixture_experts_layer_top_amd import inputs as I
 from oracle import moe_oracle as O
 
-from helpers import BF16_TOL, FP8_TOL, Inputs, bits_to_f64, rel_err
+from helpers import BF16_TOL, FP8_TOL, Inputs, act_of, bits_to_f64, rel_err, tol_of
+from oracle import mxfp8
 
 pytestmark = pytest.mark.gpu
 
@@ -176,7 +177,7 @@ def _check_layer(moe, inp, config=-1, tol=BF16_TOL, runs=1):
     p = inp.p
     out, keep = moe.layer(inp.d_logits, inp.d_x, inp.expert_weights(), p.k, config=config,
                           keep_routing=True)
-    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, inp.get_shared(), act_fp8=p.wdtype == I.WDT_FP8)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, inp.get_shared(), act=act_of(p))
     assert np.array_equal(keep["topk_ids"].cpu().numpy(), ref["ids"])
     assert np.abs(keep["topk_w"].cpu().numpy() - ref["w"]).max() <= 2e-6
     assert np.array_equal(keep["counts"].cpu().numpy(), ref["counts"])
@@ -453,5 +454,74 @@ def test_fp8_tile_layout(moe):
 
 def test_mxfp4_rejects_mfma_config(moe):
     inp = Inputs(MXFP4_SMALL[0])
+    with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
+        moe.Layer(inp.expert_weights(), inp.p.T, inp.p.E, inp.p.k, config=1)(inp.d_logits, inp.d_x)
+
+
+# ------------------------------------------------------------------------------------------------
+# MXFP4 experts with MXFP8 activations on the scaled f8f6f4 MFMA: x and h quantised per 32 channels
+# (E4M3 codes, E8M0 scales; bit-exact quantiser), outputs at the 8-bit bar.  Same K-loop cases as
+# the W4A16 tiles: one chunk per wavefront or none (d = 256, 384), whole pipelined pairs plus an
+# odd chunk (d = 1536, 4096), one token, passes of up to 16, 32 and 64 rows.
+# ------------------------------------------------------------------------------------------------
+
+def test_quant_act_mx_exhaustive_bf16(moe):
+    """A 448 in every block of 32 gives scale code 127 (E = 0): every other element's code is then
+    the oracle's encoding of it -- all finite bf16 values of magnitude <= 448."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = (b.astype(np.uint32) << 16).view(np.float32)
+    vals = b[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    per, d = 31, 1024
+    nblk = (vals.size + per - 1) // per
+    nblk += (-nblk) % (d // 32)
+    body = np.concatenate([vals, np.full(nblk * per - vals.size, 0x3F80, np.uint16)]).reshape(nblk, per)
+    x = np.concatenate([np.full((nblk, 1), 0x43E0, np.uint16), body], axis=1).reshape(-1, d)
+    xq, xe = moe.quant_act_mx(torch.from_numpy(x.view(np.int16)).cuda())
+    rq, re = mxfp8.quant_act(x)
+    assert np.all(re == 127)
+    assert np.array_equal(xe.cpu().numpy(), re)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("scale", [1.0, 1e-3, 300.0, 1e-30, 1e30])
+def test_quant_act_mx_random(moe, scale):
+    rng = np.random.default_rng(int(min(scale, 1e6) * 1000) + 7)
+    x = (rng.standard_normal((41, 640)) * scale).astype(np.float32)
+    x[3, 32:64] = 0.0
+    x[5, :32] = -0.0
+    x[7, 64:96] = rng.integers(-3, 4, 32)
+    x[9, 96:128] = 448.0 * scale
+    bits = I.f32_to_bf16_bits(x)
+    xq, xe = moe.quant_act_mx(torch.from_numpy(bits.view(np.int16)).cuda())
+    rq, re = mxfp8.quant_act(bits)
+    assert np.array_equal(xe.cpu().numpy(), re)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+MXA8_SMALL = [replace(p, name=p.name + "_a8", act_mx8=True) for p in MXFP4_SMALL]
+
+
+@pytest.mark.parametrize("config", [-1, 0])
+@pytest.mark.parametrize("p", MXA8_SMALL, ids=lambda p: p.name)
+def test_mxfp4_a8_layer_matches_oracle(moe, p, config):
+    _check_layer(moe, Inputs(p), config=config, tol=FP8_TOL, runs=2)
+
+
+def test_mxfp4_a8_grouped_ffn_matches_oracle(moe):
+    p = MXA8_SMALL[2]
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    x_perm = torch.from_numpy(np.ascontiguousarray(inp.x[perm_src // p.k]).view(np.int16)).cuda()
+    y = moe.grouped_ffn(x_perm, None, torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, act="mxfp8")["y_perm"]
+    assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
+
+
+def test_mxfp4_a8_rejects_mfma_config(moe):
+    inp = Inputs(MXA8_SMALL[0])
     with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
         moe.Layer(inp.expert_weights(), inp.p.T, inp.p.E, inp.p.k, config=1)(inp.d_logits, inp.d_x)
