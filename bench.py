@@ -326,6 +326,163 @@ def select_sweep(args) -> int:
     return 0
 
 
+def _policy_table_text(table, command, note):
+    rows = ",\n".join("    {" + ", ".join(str(v) for v in r) + "}" for r in table)
+    return f"""// Policy table of the device-side selection: kPolicyTable[T bucket][effective-expert bucket] is the
+// index of the policy (select_policy.h) the selection applies.  Written by bench.py --tune-select:
+//   {command}
+// {note}
+#pragma once
+
+namespace moe {{
+
+constexpr unsigned char kPolicyTable[kTBuckets][kEeffBuckets] = {{
+{rows},
+}};
+
+}}  // namespace moe
+"""
+
+
+def tune_select(args) -> int:
+    """Offline tuning of the selection policy table ("Decoding the Skew ...", Abstract: the live
+    routing histogram is matched to distributions tuned offline).  For each sweep point (a layer
+    shape, a batch size and a Dirichlet concentration set from a target effective expert count)
+    every policy is timed with its config forced (16 + i), besides the automatic choice and a
+    static token-count bucket, under the flushed protocol (a 512 MiB read before each step, HIP
+    events around the layer, median).  The point falls in the table cell of its T and its routed
+    histogram's effective expert count (the values the device computes); each cell takes the
+    policy with the lowest mean time relative to the point's best.  Cells with no point copy the
+    nearest measured cell of their T row (else policy 0).  Prints the per-point markdown table;
+    --table-out writes the header."""
+    import math
+    import numpy as np
+    import torch
+    from dataclasses import replace as dc_replace
+    from mixture_experts_layer_top_amd import inputs as I
+    from mixture_experts_layer_top_amd import moe
+    scratch = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def time_layer(layer, logits, x, steps, warm=3, each=False):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(warm):
+            layer(logits, x)
+        ts = []
+        for _ in range(steps):
+            scratch.view(torch.int64).sum()
+            e0.record()
+            layer(logits, x)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return ts if each else statistics.median(ts)
+
+    def t_bucket(T):
+        for i, lim in enumerate((1, 2, 4, 8, 16, 32, 64, 128, 256, 1024)):
+            if T <= lim:
+                return i
+        return 10
+
+    def e_bucket(e):
+        for i, lim in enumerate((6, 12, 24, 48, 96, 192)):
+            if e <= lim:
+                return i
+        return 6
+
+    points = []
+    base = I.DSV3
+    for T in [int(v) for v in args.sweep_T.split(",")]:
+        for tgt in [float(v) for v in args.sweep_eeff.split(",")]:
+            if tgt >= base.E or tgt <= 1:
+                continue
+            alpha = I.alpha_for_eeff(base.E, tgt)
+            points.append(I.Problem(f"tune_T{T}_e{tgt:g}", base.cfg_index, T=T, d=base.d, f=base.f,
+                                    E=base.E, k=base.k, routing="dirichlet", alpha=alpha))
+    if args.tune_prefill:
+        points += [dc_replace(I.MIXTRAL, T=T, name=f"mixtral_T{T}") for T in (512, 2048, 4096)]
+        points += [I.KIMI]
+    weights = {}
+    n_pol = moe.NUM_POLICIES
+    table_score, table_count = {}, {}
+    print("| workload | T | E_eff routed | cell | auto (ms) | " +
+          " | ".join(f"P{i}" for i in range(n_pol)) + " | static bucket | best |")
+    print("|---|---|---|---|---|" + "---|" * n_pol + "---|---|", flush=True)
+    for p in points:
+        key = (p.cfg_index, p.d, p.f, p.E)
+        if key not in weights:
+            weights.clear()
+            torch.cuda.empty_cache()
+            W = I.gen_weights(p, "cuda")
+            weights[key] = moe.ExpertWeights(gate=W["gate"], up=W["up"], down=W["down"])
+        ew = weights[key]
+        logits = torch.from_numpy(I.gen_logits(p)).cuda()
+        x = torch.from_numpy(I.gen_x(p).view(np.int16)).cuda()
+        steps = args.steps if p.T <= 256 else max(5, args.steps // 3)
+        auto = moe.Layer(ew, p.T, p.E, p.k)
+        kept = {"counts": torch.zeros(p.E, dtype=torch.int32, device="cuda")}
+        auto(logits, x, kept)
+        counts = kept["counts"].cpu().numpy()
+        eeff = I.effective_experts(counts)
+        static_cfg = moe.CONFIG_STREAM if p.T * p.k / p.E <= 8 else moe.CONFIG_MFMA
+        confs = [moe.Layer(ew, p.T, p.E, p.k, config=moe.CONFIG_POLICY0 + i) for i in range(n_pol)]
+        confs += [auto, moe.Layer(ew, p.T, p.E, p.k, config=static_cfg)]
+        # interleaved: rounds of a few steps per configuration, the order rotated (and reversed
+        # every other round), so no configuration always runs first after a pause; the median
+        # over all of a configuration's steps
+        samples = [[] for _ in confs]
+        rounds = 4
+        for r in range(rounds):
+            order = list(range(len(confs)))
+            order = order[r % len(order):] + order[:r % len(order)]
+            if r % 2:
+                order.reverse()
+            for c in order:
+                samples[c] += time_layer(confs[c], logits, x, max(1, steps // rounds), warm=1, each=True)
+        med = [statistics.median(v) for v in samples]
+        ms, ms_auto, ms_static = med[:n_pol], med[n_pol], med[n_pol + 1]
+        del confs, auto
+        best = min(ms)
+        cell = (t_bucket(p.T), e_bucket(eeff))
+        sc = table_score.setdefault(cell, [0.0] * n_pol)
+        table_count[cell] = table_count.get(cell, 0) + 1
+        for i in range(n_pol):
+            sc[i] += math.log(ms[i] / best)
+        print(f"| {p.name} | {p.T} | {eeff:.1f} | {cell} | {ms_auto:.3f} | " +
+              " | ".join(f"{v:.3f}" for v in ms) + f" | {ms_static:.3f} | P{ms.index(best)} |",
+              flush=True)
+    # a cell leaves policy 0 (the hand rules) only for a mean gain above the margin
+    table = [[0] * 7 for _ in range(11)]
+    measured = {}
+    for c, v in table_score.items():
+        mean = [t / table_count[c] for t in v]
+        i = int(np.argmin(mean))
+        measured[c] = i if mean[0] - mean[i] > math.log(1.0 + args.tune_margin) else 0
+    for tb in range(11):
+        row = {eb: pol for (t, eb), pol in measured.items() if t == tb}
+        for eb in range(7):
+            if eb in row:
+                table[tb][eb] = row[eb]
+            elif row:
+                table[tb][eb] = row[min(row, key=lambda r: (abs(r - eb), r))]
+    print("\ncells measured (T bucket, E_eff bucket) -> policy:",
+          {f"{c}": p_ for c, p_ in sorted(measured.items())}, flush=True)
+    if args.table_out:
+        argv, skip = [], False
+        for a in sys.argv[1:]:  # the command without the output path
+            if skip or a.startswith("--table-out"):
+                skip = a == "--table-out"
+                continue
+            argv.append(a)
+        cmd = " ".join(["python bench.py"] + argv + ["--table-out <file>"])
+        note = (f"A cell leaves policy 0 only for a mean gain above {100 * args.tune_margin:g}%; cells "
+                "with no sweep point copy the nearest measured cell of their T row; rows with none "
+                "hold policy 0.")
+        with open(args.table_out, "w") as fh:
+            fh.write(_policy_table_text(table, cmd, note))
+        print(f"wrote {args.table_out}", flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +515,13 @@ def main() -> int:
     ap.add_argument("--select-sweep", action="store_true",
                     help="only run the tile-selection sweep over --sweep-T x --sweep-eeff (markdown "
                          "table, no JSON line)")
+    ap.add_argument("--tune-select", action="store_true",
+                    help="only run the selection-policy tuner over --sweep-T x --sweep-eeff (and, with "
+                         "--tune-prefill, prefill shapes) and print its table")
+    ap.add_argument("--tune-prefill", action="store_true")
+    ap.add_argument("--tune-margin", type=float, default=0.02,
+                    help="--tune-select: smallest mean gain over policy 0 that changes a cell")
+    ap.add_argument("--table-out", default=None, help="--tune-select: write the policy table header here")
     ap.add_argument("--sweep-T", default="1,4,16,64,256")
     ap.add_argument("--sweep-eeff", default="8,32,128,224",
                     help="target effective expert counts (each fixes a Dirichlet concentration)")
@@ -381,6 +545,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.select_sweep:
         return select_sweep(args)
+    if args.tune_select:
+        return tune_select(args)
     p = workload(args)
     print(f"[bench] workload {p.name}: T={p.T} d={p.d} f={p.f} E={p.E} k={p.k} {p.wdtype}"
           f"{' +shared' if p.shared else ''}", file=sys.stderr, flush=True)
@@ -577,7 +743,7 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 128}.get(p.name, p.T)
+        sample = args.cpu_sample or {"mixtral_prefill": 4096, "kimi_prefill": 256}.get(p.name, p.T)
         print(f"[bench] CPU oracle on {sample} tokens ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, logits, x, W, sample)
     print(json.dumps(out), flush=True)

@@ -81,14 +81,20 @@ enum moe_dtype {
 };
 
 /* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert and per
- * GEMM from the live histogram; the others force one family for every expert (used by tests to
- * cover each).  Block-scaled fp8 weights always use the weight-streaming family. */
+ * GEMM from the live histogram: for bf16 weights it computes the histogram's effective expert count
+ * (exp of its entropy) and looks up, by T and that count, a selection policy tuned offline ("Decoding
+ * the Skew", Abstract: the live distribution matched to offline-tuned configurations).  The others
+ * force one family for every expert, or (MOE_CONFIG_POLICY0 + i, bf16 only) force policy i; tests
+ * use them to cover each.  Block-scaled fp8 and mxfp4 weights always use the streaming family. */
 enum moe_config {
   MOE_CONFIG_AUTO = -1,
   MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
-  MOE_CONFIG_MFMA = 1    /* LDS-tiled MFMA tiles: 64, 128 or 256 rows (from the rows a tile
+  MOE_CONFIG_MFMA = 1,   /* LDS-tiled MFMA tiles: 64, 128 or 256 rows (from the rows a tile
                             holds) x 256 weight rows */
+  MOE_CONFIG_POLICY0 = 16 /* 16 + i (i < MOE_NUM_POLICIES): selection policy i, whatever the
+                             histogram (other values: MOE_ERR_INVALID_ARG) */
 };
+#define MOE_NUM_POLICIES 8
 
 typedef struct moe_problem {
   int32_t T;           /* tokens */
@@ -139,6 +145,9 @@ typedef struct moe_routing {
   int32_t* offsets;  /* [E+1] */
   int32_t* perm_src; /* [T*k] */
   int32_t* slot_dst; /* [T*k] */
+  float* eeff;        /* [1]: the live effective expert count the bf16 selection computed */
+  int32_t* policy;    /* [1]: the policy it applied (-1 when a family was forced); neither is
+                         written for fp8 / mxfp4 weights or the single-token bf16 path */
 } moe_routing;
 
 /* Route: topk_ids[t][j] = j-th largest logit's expert (ties -> lower id), topk_w[t][j] = its

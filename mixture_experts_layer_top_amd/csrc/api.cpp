@@ -10,10 +10,13 @@
 #include <cstring>
 
 #include "kernels.h"
+#include "select_policy.h"
 
 namespace {
 
 using namespace moe;
+
+static_assert(MOE_NUM_POLICIES == kNumPolicies, "the header's policy count");
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxExperts = 512;
@@ -70,7 +73,10 @@ int check_problem(const moe_problem* p) {
   if (is_mxfp4(p) && (p->has_shared || p->config == MOE_CONFIG_MFMA)) return MOE_ERR_UNSUPPORTED;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
-  if (p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) return MOE_ERR_INVALID_ARG;
+  const bool policy = p->config >= kConfigPolicy0 && p->config < kConfigPolicy0 + kNumPolicies;
+  if ((p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) && !policy)
+    return MOE_ERR_INVALID_ARG;
+  if (policy && p->wdtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;  // (streaming only)
   // 32-bit byte offsets: x [T][d], h [T*k][f], y [T*k][d], shared h [T][f_sh] (2 bytes per value
   // at most) and each expert's [f][d] matrices must stay below 4 GiB
   const int64_t n = (int64_t)p->T * p->top_k;
@@ -160,6 +166,30 @@ void carve_ffn(Carver& c, const moe_problem* p, bool with_shared, bool grouped_f
 // split needs fewer than kSplitMaxRounds rounds of MFMA tiles, and the MFMA rows are at least the
 // rows of every expert above the streaming threshold, so when those alone fill kSplitMaxRounds
 // rounds at full tile height no split can happen.
+// The streaming thresholds of the policies the device may apply to a bf16 problem (the table row
+// of its T bucket in automatic mode, else the forced one), and whether all of them use the few-tile
+// rule: the host's launch decisions must hold for whichever one the live histogram picks.
+struct PolicyBounds {
+  int thr_min[2], thr_max[2];
+  bool all_few;
+};
+PolicyBounds policy_bounds(const moe_problem* p) {
+  PolicyBounds b{{1 << 30, 1 << 30}, {0, 0}, true};
+  auto add = [&](int i) {
+    const SelectPolicy& P = kPolicies[i];
+    const int t[2] = {P.thr_gu, P.thr_dn};
+    for (int g = 0; g < 2; ++g) {
+      b.thr_min[g] = std::min(b.thr_min[g], t[g]);
+      b.thr_max[g] = std::max(b.thr_max[g], t[g]);
+    }
+    b.all_few = b.all_few && P.few_tile;
+  };
+  if (p->config >= kConfigPolicy0) add(p->config - kConfigPolicy0);
+  else
+    for (int j = 0; j < kEeffBuckets; ++j) add(kPolicyTable[t_bucket(p->T)][j]);
+  return b;
+}
+
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, int cus, hipStream_t s) {
   if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
@@ -167,16 +197,17 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
     return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, false, s, true);
-  const int thr = gemm == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown;
+  const bool auto_mode = p->config == MOE_CONFIG_AUTO || p->config >= kConfigPolicy0;
+  const PolicyBounds pb = policy_bounds(p);
   const bool stream = p->config != MOE_CONFIG_MFMA;
-  bool mfma = p->config == MOE_CONFIG_MFMA || (p->config == MOE_CONFIG_AUTO && max_rows > thr);
+  bool mfma = p->config == MOE_CONFIG_MFMA || (auto_mode && max_rows > pb.thr_min[gemm]);
   const int64_t nt = gemm == kGemmGateUp ? p->d_ff / kMfmaBNGateUp
                                          : (p->d_model + kMfmaBNDown - 1) / kMfmaBNDown;
-  if (mfma && p->config == MOE_CONFIG_AUTO && max_rows <= kFewTileRows && !p->has_shared) {
+  if (mfma && auto_mode && pb.all_few && max_rows <= kFewTileRows && !p->has_shared) {
     const int64_t experts = std::min<int64_t>(p->num_experts, total_rows);
     if (5 * experts * nt < kFewTileRounds5 * (int64_t)cus) mfma = false;
   }
-  const int64_t light = p->config == MOE_CONFIG_MFMA ? 0 : (int64_t)thr * p->num_experts;
+  const int64_t light = p->config == MOE_CONFIG_MFMA ? 0 : (int64_t)pb.thr_max[gemm] * p->num_experts;
   const int64_t min_tiles = (std::max<int64_t>(0, total_rows - light) + kMfmaBM - 1) / kMfmaBM * nt;
   const bool maybe_split =
       min_tiles < (int64_t)kSplitMaxRounds * std::min(cus, kSplitMaxPieces);
@@ -436,6 +467,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   int32_t* offsets = (keep && keep->offsets) ? keep->offsets : L.offsets;
   int32_t* perm_src = (keep && keep->perm_src) ? keep->perm_src : L.perm_src;
   int32_t* slot_dst = (keep && keep->slot_dst) ? keep->slot_dst : L.slot_dst;
+  float* out_eeff = keep ? keep->eeff : nullptr;
+  int32_t* out_policy = keep ? keep->policy : nullptr;
 
   auto mark = [&](int i) -> hipError_t {
     return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
@@ -470,6 +503,8 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   a.h = L.ffn.h; a.hs = L.ffn.hs;
   a.h_sh = L.ffn.h_sh; a.hs_sh = L.ffn.hs_sh;
   a.y = L.y; a.y_sh = L.ffn.y_sh;
+  a.out_eeff = out_eeff;
+  a.out_policy = out_policy;
   SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_part};
 
   hipError_t e = mark(0);

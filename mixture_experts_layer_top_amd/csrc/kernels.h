@@ -14,13 +14,12 @@ constexpr int kMaxTopK = 8;  // experts per token (the boundary rejects more)
 
 constexpr int kStreamMaxRows = 64;  // rows per weight-streaming pass
 // Automatic selection: an expert takes the weight-streaming family for a GEMM while its row
-// count is at most this, the LDS-tiled MFMA family above it (whose short tiles stream the
-// weights of even a one-row gate/up expert faster, given enough tiles; see select.hip).
-constexpr int kStreamRowsGateUp = 0;
-constexpr int kStreamRowsDown = 8;
-// Few-tile rule: a GEMM whose MFMA tiles would fill fewer than kFewTileRounds5 / 5 rounds of CUs
-// runs wholly on the streaming tiles when none of its MFMA experts holds more than kFewTileRows
-// rows (one 16-row MFMA pass per weight load); a larger expert keeps the whole GEMM on MFMA.
+// count is at most the policy's threshold for that GEMM (select_policy.h), the LDS-tiled MFMA
+// family above it.
+// Few-tile rule (policies that use it): a GEMM whose MFMA tiles would fill fewer than
+// kFewTileRounds5 / 5 rounds of CUs runs wholly on the streaming tiles when none of its MFMA
+// experts holds more than kFewTileRows rows (one 16-row MFMA pass per weight load); a larger
+// expert keeps the whole GEMM on MFMA.
 constexpr int kFewTileRows = 16;
 constexpr int kFewTileRounds5 = 8;
 constexpr int kMfmaBM = 256;        // rows per full LDS-tiled MFMA tile
@@ -114,6 +113,8 @@ struct SelectArgs {
   void* h; float* hs;      // routed gate/up output [T*k][f] (+ fp8 scales [T*k][f/128])
   void* h_sh; float* hs_sh;  // shared gate/up output [T][f_sh]
   void* y; void* y_sh;     // down outputs [T*k][d], [T][d]
+  float* out_eeff;         // optional: the live effective expert count (bf16 selection)
+  int32_t* out_policy;     // optional: the policy the selection applied (-1: a family was forced)
 };
 
 // ints per (gemm, family): nseg, ntiles, then kXcds queue counters (the stream family uses the

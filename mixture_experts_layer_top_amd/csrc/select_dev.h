@@ -5,18 +5,37 @@
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
+#include "select_policy.h"
 
 namespace moe {
 
 constexpr int kSelThreads = 1024;  // one thread per expert (E + 1 <= kSelThreads)
 static_assert(kSegCap >= 2 * (kSelThreads / 2 + 1), "two segments per expert (E <= 512)");
 
-__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8) {
+// config: -1 or a forced policy (>= kConfigPolicy0): the policy's thresholds; 0 / 1: that family.
+__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8, const SelectPolicy& P) {
   if (c <= 0) return -1;
-  if (fp8) return kFamStream;  // block-scaled fp8 experts: streaming family only
+  if (fp8) return kFamStream;  // block-scaled fp8 and mxfp4 experts: streaming family only
   if (config == 0) return kFamStream;
-  if (config >= 1) return kFamMfma;
-  return c <= (g == kGemmGateUp ? kStreamRowsGateUp : kStreamRowsDown) ? kFamStream : kFamMfma;
+  if (config == 1) return kFamMfma;
+  return c <= (g == kGemmGateUp ? P.thr_gu : P.thr_dn) ? kFamStream : kFamMfma;
+}
+
+// The live effective expert count exp(-sum_e q_e ln q_e), q_e = c_e / N, N = sum_e c_e, as
+// exp(ln N - (sum_e c_e ln c_e) / N): one value per thread (c, 0 past the experts), summed in a
+// fixed order (wavefront butterflies, then the wavefront totals in order).  Every thread of the
+// block must call it; all get the result.
+__device__ __forceinline__ float block_eeff(int c, int N) {
+  __shared__ float part[kSelThreads / 64];
+  float v = c > 1 ? (float)c * logf((float)c) : 0.f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float S = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) S += part[w];
+  __syncthreads();  // (part may be reused by the next call)
+  return N > 0 ? expf(logf((float)N) - S / (float)N) : 0.f;
 }
 
 // Per expert (one thread each, blockDim.x = kSelThreads >= E + 1) and per GEMM: family, tile
@@ -52,9 +71,24 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   if (e < nexp) c = (e < a.E) ? (lds_counts ? lds_counts[e] : gload_i32(a.counts, e)) : a.T;
   const bool shared = e == a.E;
   const int ffe = shared ? a.f_sh : a.f;
+  // The policy ("Decoding the Skew", Abstract: the live histogram matched to offline-tuned
+  // configurations): bf16 problems in automatic mode look it up by T and the live effective expert
+  // count; config >= kConfigPolicy0 forces one; forced families (config 0 / 1) and the streaming-only
+  // formats use none.
+  const bool bf16 = !a.fp8 && !a.w4;
+  const float eeff = bf16 ? block_eeff(e < a.E ? c : 0, a.T * a.k) : 0.f;
+  const bool auto_mode = a.config < 0 || a.config >= kConfigPolicy0;
+  const int pol = !bf16 || !auto_mode ? -1
+                  : a.config >= kConfigPolicy0 ? a.config - kConfigPolicy0
+                                               : kPolicyTable[t_bucket(a.T)][eeff_bucket(eeff)];
+  const SelectPolicy P = kPolicies[pol < 0 ? 0 : pol];
+  if (e == 0) {
+    if (a.out_eeff) a.out_eeff[0] = eeff;
+    if (a.out_policy) a.out_policy[0] = pol;
+  }
   int fm[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8 || a.w4) : -1;
+  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8 || a.w4, P) : -1;
   // The down GEMM's light experts (<= kStreamRowsDown rows) take the streaming tiles only while its
   // heavier experts' MFMA tiles fill less than one round of CUs; with a round or more they join the
   // MFMA list, where their short tiles fill the rounds' gaps instead of running as a second launch
@@ -85,17 +119,18 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       w[2 + g] = fm[g] == kFamMfma && c > kMfmaBM ? 1 : 0;
       w[4 + g] = fm[g] == kFamMfma && c > kFewTileRows ? 1 : 0;
     }
-    w[6] = a.config < 0 && fm[kGemmDown] == kFamStream ? nt_dn : 0;  // c <= kStreamRowsDown < kMfmaBM
+    // (streamed down experts hold at most P.thr_dn <= 64 < kMfmaBM rows: one m-tile each)
+    w[6] = auto_mode && P.promote && fm[kGemmDown] == kFamStream ? nt_dn : 0;
     w[7] = 0;
     block_scan<8, 16>(w, wex, wtot, scan_lds);
-    if (a.config < 0 && wtot[kGemmDown] >= a.num_cus) {
+    if (auto_mode && P.promote && wtot[kGemmDown] >= a.num_cus) {
       if (w[6]) fm[kGemmDown] = kFamMfma;
       wtot[kGemmDown] += wtot[6];
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      if (a.config < 0 && fm[g] == kFamMfma && 5 * wtot[g] < kFewTileRounds5 * a.num_cus &&
-          wtot[4 + g] == 0)
+      if (auto_mode && P.few_tile && fm[g] == kFamMfma &&
+          5 * wtot[g] < kFewTileRounds5 * a.num_cus && wtot[4 + g] == 0)
         fm[g] = kFamStream;
       const int C = min(a.num_cus, kSplitMaxPieces);
       lpt[g] = wtot[g] >= C && wtot[g] < kSplitMaxRounds * C;

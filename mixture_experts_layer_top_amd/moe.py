@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4, DTYPE_MXFP4_A8 = 0, 1, 2, 3
 CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
+CONFIG_POLICY0, NUM_POLICIES = 16, 8  # config = 16 + i forces selection policy i (bf16)
 LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -42,7 +43,7 @@ class Weights(ctypes.Structure):
 
 class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "topk_ids", "topk_w", "counts", "offsets", "perm_src", "slot_dst")]
+        "topk_ids", "topk_w", "counts", "offsets", "perm_src", "slot_dst", "eeff", "policy")]
 
 
 class MoEError(RuntimeError):

@@ -205,3 +205,18 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     assert L.moe_layer_noalloc(ctypes.byref(bad), 1024, 2048, ctypes.byref(w), 4096, None,
                                None) == moe.MOE_ERR_UNSUPPORTED
     assert b"static scratch" in L.moe_status_string(moe.MOE_ERR_WORKSPACE)
+
+
+def test_policy_configs():
+    """config 16 + i forces selection policy i for bf16 weights; other values are rejected, and the
+    streaming-only formats reject policies."""
+    L = moe.lib()
+    ws = L.moe_layer_workspace_bytes
+    for i in range(moe.NUM_POLICIES):
+        assert ws(ctypes.byref(moe.problem(64, 256, 512, 8, 2, config=moe.CONFIG_POLICY0 + i))) > 0
+    for bad in (2, 15, moe.CONFIG_POLICY0 + moe.NUM_POLICIES, -2):
+        assert ws(ctypes.byref(moe.problem(64, 256, 512, 8, 2, config=bad))) == 0
+    fp8 = moe.problem(64, 256, 512, 8, 2, fp8=True, config=moe.CONFIG_POLICY0)
+    w = moe.Weights(w_gate=256, w_up=512, w_down=768)
+    assert L.moe_layer(ctypes.byref(fp8), 1024, 2048, ctypes.byref(w), 4096, None, 8192, 16,
+                       None) == moe.MOE_ERR_UNSUPPORTED
