@@ -103,11 +103,13 @@ def algorithmic(p, n_active: int):
         w_gu += (n_active * 2 * p.f * p.d + (2 * sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
         w_dn += (n_active * p.f * p.d + (sh_f * p.d if p.shared else 0)) / (128 * 128) * 4
     x_bytes = p.T * p.d * 2.0
+    # gate/up reads the activations as bf16, or as MXFP8 codes plus one scale byte per 32
+    x_gu = p.T * p.d * (1 + 1 / 32) if p.act_mx8 else x_bytes
     out_bytes = p.T * p.d * 2.0
     logit_bytes = p.T * p.E * 4.0
     return dict(flop=flop_gu + flop_dn, flop_gu=flop_gu, flop_dn=flop_dn,
                 bytes=w_gu + w_dn + x_bytes + out_bytes + logit_bytes,
-                bytes_gu=w_gu + x_bytes, bytes_dn=w_dn + out_bytes)
+                bytes_gu=w_gu + x_gu, bytes_dn=w_dn + out_bytes)
 
 
 TRAFFIC_SOURCES = ("mixture_experts_layer_top_amd/csrc/gemm_bf16.hip",
