@@ -85,12 +85,14 @@ enum moe_dtype {
  * (exp of its entropy) and looks up, by T and that count, a selection policy tuned offline ("Decoding
  * the Skew", Abstract: the live distribution matched to offline-tuned configurations).  The others
  * force one family for every expert, or (MOE_CONFIG_POLICY0 + i, bf16 only) force policy i; tests
- * use them to cover each.  Block-scaled fp8 and mxfp4 weights always use the streaming family. */
+ * use them to cover each.  Block-scaled fp8 weights in automatic mode put experts of more than 128
+ * rows on the MFMA tiles when a GEMM's MFMA tiles fill at least one round of compute units, the
+ * others on the streaming tiles (no policy table); mxfp4 weights always stream. */
 enum moe_config {
   MOE_CONFIG_AUTO = -1,
   MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
-  MOE_CONFIG_MFMA = 1,   /* LDS-tiled MFMA tiles: 64, 128 or 256 rows (from the rows a tile
-                            holds) x 256 weight rows */
+  MOE_CONFIG_MFMA = 1,   /* LDS-tiled MFMA tiles: bf16 64, 128 or 256 rows (from the rows a tile
+                            holds) x 256 weight rows; fp8 256 x 256 (mxfp4: MOE_ERR_UNSUPPORTED) */
   MOE_CONFIG_POLICY0 = 16 /* 16 + i (i < MOE_NUM_POLICIES): selection policy i, whatever the
                              histogram (other values: MOE_ERR_INVALID_ARG) */
 };

@@ -192,7 +192,11 @@ PolicyBounds policy_bounds(const moe_problem* p) {
 
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, int cus, hipStream_t s) {
-  if (p->wdtype == MOE_DTYPE_FP8_E4M3) return moe::launch_gemms_fp8(o, gemm, cus, s);
+  if (p->wdtype == MOE_DTYPE_FP8_E4M3)
+    return moe::launch_gemms_fp8(o, gemm, cus, p->config != MOE_CONFIG_MFMA,
+                                 p->config == MOE_CONFIG_MFMA ||
+                                     (p->config == MOE_CONFIG_AUTO && max_rows > kFp8MfmaRows),
+                                 s);
   if (p->wdtype == MOE_DTYPE_MXFP4_A8) return moe::launch_gemms_mx(o, gemm, cus, max_rows, s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only

@@ -259,12 +259,17 @@ __global__ __launch_bounds__(256) void gemm_stream_fp8(const Seg* __restrict__ s
   }
 }
 
-hipError_t launch_gemms_fp8(const SelectOut& o, int g, int num_cus, hipStream_t s) {
-  // fp8 experts use the streaming family only (select.hip routes every fp8 expert there)
+hipError_t launch_gemms_fp8(const SelectOut& o, int g, int num_cus, bool stream, bool mfma,
+                            hipStream_t s) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
-  if (g == kGemmGateUp) gemm_stream_fp8<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-  else gemm_stream_fp8<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+  if (stream) {
+    if (g == kGemmGateUp) gemm_stream_fp8<true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    else gemm_stream_fp8<false><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+  }
+  if (mfma)
+    launch_mfma_fp8(o.segs + (size_t)(g * kNumFam + kFamMfma) * kSegCap,
+                    o.meta + (g * kNumFam + kFamMfma) * kMetaStride, g, num_cus, s);
   return hipGetLastError();
 }
 

@@ -34,7 +34,10 @@ __host__ __device__ constexpr int stream_bn(int K) { return K >= kStreamSplitK ?
 // Longest K whose one-row activations a streaming tile stages in LDS (16 KB).
 constexpr int kStreamXlMaxK = 8192;
 constexpr int kSegCap = 1040;       // segment slots per (gemm, family); >= 2 * (E + 1)
-// fp8 weights (streaming family only): rows per pass (more rows take more passes, which re-read
+// fp8 experts of more than kFp8MfmaRows rows take the LDS-staged MFMA tiles in automatic mode (when
+// the GEMM's MFMA tiles fill at least one round of CUs), the others the streaming tiles.
+constexpr int kFp8MfmaRows = 128;
+// fp8 weight-streaming tiles: rows per pass (more rows take more passes, which re-read
 // the weights from L2; with 32 the down kernel fits three wavefronts per SIMD, while the gate/up
 // kernel, which holds two K blocks of gate and up weights in flight, needs 256 VGPRs and runs one
 // wavefront per SIMD), h columns per gate/up tile (one whole 128-column requantisation block), y
@@ -159,7 +162,11 @@ hipError_t launch_weight_tile(const void* src, void* dst, int64_t rows, int64_t 
 hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
                              int max_k, bool stream, bool mfma, bool maybe_split, hipStream_t s,
                              bool w4);
-hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, hipStream_t s);
+// fp8: the streaming kernel and/or the LDS-staged MFMA kernel of one GEMM (each launched only when
+// its list may hold tiles).
+hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, bool stream, bool mfma,
+                            hipStream_t s);
+void launch_mfma_fp8(const Seg* segs, int32_t* meta, int gemm, int num_cus, hipStream_t s);
 // MXFP4 weights with MXFP8 activations (streaming tiles on the scaled f8f6f4 MFMA); max_rows
 // bounds any expert's rows.
 hipError_t launch_gemms_mx(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,

@@ -13,11 +13,15 @@ constexpr int kSelThreads = 1024;  // one thread per expert (E + 1 <= kSelThread
 static_assert(kSegCap >= 2 * (kSelThreads / 2 + 1), "two segments per expert (E <= 512)");
 
 // config: -1 or a forced policy (>= kConfigPolicy0): the policy's thresholds; 0 / 1: that family.
-__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8, const SelectPolicy& P) {
+// mxfp4 experts stream; fp8 experts in automatic mode take the MFMA tiles above kFp8MfmaRows rows
+// (subject to the one-round check in select_block).
+__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8, int w4,
+                                           const SelectPolicy& P) {
   if (c <= 0) return -1;
-  if (fp8) return kFamStream;  // block-scaled fp8 and mxfp4 experts: streaming family only
+  if (w4) return kFamStream;
   if (config == 0) return kFamStream;
   if (config == 1) return kFamMfma;
+  if (fp8) return c > kFp8MfmaRows ? kFamMfma : kFamStream;
   return c <= (g == kGemmGateUp ? P.thr_gu : P.thr_dn) ? kFamStream : kFamMfma;
 }
 
@@ -88,7 +92,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   }
   int fm[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8 || a.w4, P) : -1;
+  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8, a.w4, P) : -1;
   // The down GEMM's light experts (<= kStreamRowsDown rows) take the streaming tiles only while its
   // heavier experts' MFMA tiles fill less than one round of CUs; with a round or more they join the
   // MFMA list, where their short tiles fill the rounds' gaps instead of running as a second launch
@@ -104,7 +108,22 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   // same (block-wide) totals give the list's ordering mode: one to kSplitMaxRounds rounds ->
   // longest first (below one round every tile starts at once and order does not matter); else XCD
   // chunks when K >= kLongK and some expert spans several m-tiles.
+  // fp8 (automatic mode): a GEMM whose MFMA tiles would fill less than one round of CUs runs wholly
+  // on the streaming tiles (one CU per weight tile draws too little of the chip's bandwidth).
   bool lpt[2] = {false, false}, chunks[2] = {false, false};
+  if (a.fp8 && a.config < 0) {
+    const int nt_dn = (a.d + kMfmaBNDown - 1) / kMfmaBNDown;
+    int w[2], wex[2], wtot[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      w[g] = fm[g] == kFamMfma
+                 ? (c + kMfmaBM - 1) / kMfmaBM * (g == 0 ? ffe / kMfmaBNGateUp : nt_dn)
+                 : 0;
+    block_scan<2, 16>(w, wex, wtot, scan_lds);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      if (fm[g] == kFamMfma && wtot[g] < a.num_cus) fm[g] = kFamStream;
+  }
   if (!a.fp8 && !a.w4) {
     // w[0..1]: MFMA tiles per GEMM; w[2..3]: MFMA experts of more than one m-tile per GEMM;
     // w[4..5]: MFMA experts of more than kFewTileRows rows per GEMM; w[6]: down tiles of the light
@@ -159,13 +178,12 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
       r0[j] = part == 0 ? 0 : c - tail;
       nr[j] = part == 0 ? (split ? c - tail : c) : tail;
       const bool st = fam[j] == kFamStream;
-      const int tm = a.fp8 ? kStreamMaxRows8 : st ? kStreamMaxRows : kMfmaBM;
+      const int tm = st ? (a.fp8 ? kStreamMaxRows8 : kStreamMaxRows) : kMfmaBM;
       if (g == kGemmGateUp) {
-        tn[j] = a.fp8 ? kStream8BNGateUp
-                      : st ? (a.w4 ? 2 : 1) * stream_bn(a.d) : kMfmaBNGateUp;
+        tn[j] = !st ? kMfmaBNGateUp : a.fp8 ? kStream8BNGateUp : (a.w4 ? 2 : 1) * stream_bn(a.d);
         nt[j] = ffe / tn[j];  // f is a multiple of 128
       } else {
-        tn[j] = a.fp8 ? kStream8BNDown : st ? (a.w4 ? 2 : 1) * stream_bn(ffe) : kMfmaBNDown;
+        tn[j] = !st ? kMfmaBNDown : a.fp8 ? kStream8BNDown : (a.w4 ? 2 : 1) * stream_bn(ffe);
         // (a down tile of 256 columns may be half full at the edge)
         nt[j] = (a.d + tn[j] - 1) / tn[j];
       }

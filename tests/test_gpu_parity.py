@@ -376,6 +376,47 @@ def test_fp8_grouped_ffn_matches_oracle(moe):
     assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
 
 
+# fp8 experts on the LDS-staged MFMA tiles (256 token rows x 256 weight rows, one 128-wide K block
+# per stage).  Forced (config 1) on every fp8 shape above plus: several 256-row m-tiles per expert
+# with ragged tails and the shared expert's T rows (T = 600, k = 2, E = 4), an odd number of K
+# blocks and a down tile whose second 128 columns lie past d (d = 384), five gate/up tiles
+# (f = 640), and a longer K (d = 2048) under skewed routing.  Automatic selection puts experts of
+# more than 128 rows on the MFMA tiles when a GEMM's MFMA tiles fill a round of CUs: on the
+# prefill-shaped case the gate/up GEMM qualifies (512 tiles) and the down GEMM (128) streams.
+FP8_MFMA = [
+    I.Problem("fp8_mfma_ragged", 113, T=600, d=384, f=640, E=4, k=2, wdtype=I.WDT_FP8,
+              shared=True, shared_f=384),
+    I.Problem("fp8_mfma_long_k", 114, T=520, d=2048, f=256, E=8, k=2, routing="dirichlet",
+              alpha=0.3, wdtype=I.WDT_FP8),
+]
+FP8_PREFILL = I.Problem("fp8_prefill", 115, T=4096, d=1024, f=2048, E=8, k=2, wdtype=I.WDT_FP8)
+
+
+@pytest.mark.parametrize("p", FP8_SMALL + FP8_MFMA, ids=lambda p: p.name)
+def test_fp8_mfma_layer_matches_oracle(moe, p):
+    _check_layer(moe, Inputs(p), config=1, tol=FP8_TOL, runs=2)
+
+
+def test_fp8_prefill_auto_matches_oracle(moe):
+    _check_layer(moe, Inputs(FP8_PREFILL), config=-1, tol=FP8_TOL, runs=2)
+
+
+def test_fp8_mfma_grouped_ffn_matches_oracle(moe):
+    p = FP8_MFMA[0]
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    xq, xs = O.quant_act_e4m3(inp.x)
+    y = moe.grouped_ffn(torch.from_numpy(xq[perm_src // p.k]).cuda(),
+                        torch.from_numpy(xs[perm_src // p.k]).cuda(),
+                        torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k, config=1)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, None, act_fp8=True)["y_perm"]
+    assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
+
+
 # ------------------------------------------------------------------------------------------------
 # MXFP4 experts (E2M1 pairs with E8M0 scales per 32; bf16 activations; streaming tiles only).  The
 # tile converts the weights to bf16 exactly, so the bar is the bf16 one.  K-loop cases: K / WK / 32
