@@ -521,7 +521,7 @@ struct MfmaTile {
 
   // kt0: first 64-wide K-step of the tile's K range (a piece of a split tile starts past 0)
   __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0, int kt0) {
-    const int lane = threadIdx.x & 63;
+    const int lane = tid_here() & 63;  // (lane constants stay in the claim, not held across tiles)
     wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     bm = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
     const int nts = bm >> 5;
@@ -826,19 +826,23 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split
   int q = 0;
   MfmaTile<GU> tile;
   auto claim = [&](MfmaCur& c) -> bool {
-    const int pos = pop_tile_xcd(Q.queues, kSplit ? Q.nq : Q.ntiles, Q.chunk, slot, q);
+    // (the queue's counts go through opaque moves: the reciprocals of its integer divisions are
+    // then computed here per claim instead of being hoisted and held across the K loops)
+    const int ntiles = opaque_s(Q.ntiles), ntiles0 = opaque_s(Q.ntiles0), chunk = opaque_s(Q.chunk);
+    const int pos = pop_tile_xcd(Q.queues, kSplit ? opaque_s(Q.nq) : ntiles, chunk, slot, q);
     if (pos < 0) return false;
     int tp = pos;
     c.piece = -1;
     c.u = 0;
     if (kSplit && pos >= Q.sbase) {
-      c.u = (pos - Q.sbase) / Q.S;
-      c.piece = pos - Q.sbase - c.u * Q.S;
+      const int S = opaque_s(Q.S);
+      c.u = (pos - Q.sbase) / S;
+      c.piece = pos - Q.sbase - c.u * S;
       tp = Q.sbase + c.u;
     }
     const int t = Q.order == kOrderLongestFirst ? tp
-                  : Q.order == kOrderChunks      ? chunked_interleave(tp, Q.ntiles0, Q.ntiles, Q.chunk)
-                                                 : interleave_tile(tp, Q.ntiles0, Q.ntiles);
+                  : Q.order == kOrderChunks      ? chunked_interleave(tp, ntiles0, ntiles, chunk)
+                                                 : interleave_tile(tp, ntiles0, ntiles);
     const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(Q.seg_base, Q.nseg, t));
     const Seg& sg = Q.segs[si];
     const int local = t - sg.tile_base;
@@ -861,7 +865,9 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split
   if (!claim(cur)) return;
   for (;;) {
     // run, then this tile's epilogue, then the next claim; each height has its own branch so the
-    // accumulators a shorter tile leaves unused are dead around the loop
+    // accumulators a shorter tile leaves unused are dead around the loop.  (Claiming the next tile
+    // before the epilogue, so that its prologue loads fly during the stores, measured 1% slower
+    // on the Mixtral- and Kimi-shaped prefill layers.)
     if (cur.h == BM) {
       tile.run_full(cur.nk);
       if (!kSplit || cur.piece < 0)
