@@ -197,7 +197,9 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
                                  p->config == MOE_CONFIG_MFMA ||
                                      (p->config == MOE_CONFIG_AUTO && max_rows > kFp8MfmaRows),
                                  s);
-  if (p->wdtype == MOE_DTYPE_MXFP4_A8) return moe::launch_gemms_mx(o, gemm, cus, max_rows, s);
+  if (p->wdtype == MOE_DTYPE_MXFP4_A8)
+    return moe::launch_gemms_mx(o, gemm, cus, max_rows,
+                                gemm == kGemmGateUp ? p->d_model : p->d_ff, s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
     return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, false, s, true);

@@ -89,6 +89,9 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
   };
   const int nsteps = kq / 32;             // K-steps of this wavefront (>= 1)
   const int nfull = nsteps / U * U;        // pipelined part: whole batches only
+  // (Pinning the load groups with scheduling barriers and branch-free loads, as the MXFP4 tiles
+  // do, measured neutral here -- DeepSeek-V3-shaped decode within 1%, the down GEMM up to 2.5%
+  // slower at T = 64: four wavefronts per SIMD cover the drained waits.)
   Batch b0, b1;
   if (nfull > 0) load(b0, 0);
   if (XL == 1) {
@@ -151,20 +154,49 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// Stages the E8M0 scales of the workgroup's wrows weight rows from n0 (gate, then up) into LDS (sc),
+// KB bytes each at a row stride of w4_scale_stride(KB) bytes, by direct global->LDS loads (a dword
+// per lane, 256 bytes per instruction; lanes past the row re-read its last dword into the
+// padding).  Read per batch and lane from global memory instead, each scale load touched 16 rows'
+// cache lines.  The caller waits for the loads (vmcnt(0)) and holds a barrier before reading; the
+// previous pass's reads of sc are behind the barriers of its split-K reduction.
+__device__ __forceinline__ int w4_scale_stride(int KB) { return (KB + 255) & ~255; }
+
+template <bool GU>
+__device__ __forceinline__ void stage_scales_w4(const Seg& sg, int n0, int wrows, int KB,
+                                                uint8_t* sc) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KW = KB / 4, RS = w4_scale_stride(KB);
+  const int nrow = (GU ? 2 : 1) * wrows;
+  for (int r = wv; r < nrow; r += 4) {
+    const uint8_t* base = GU && r >= wrows ? sg.e1 : sg.e0;
+    const uint32_t row = (uint32_t)(n0 + (r < wrows ? r : r - wrows));
+    for (int i = 0; i < RS / 256; ++i) {
+      const int c = min(64 * i + lane, KW - 1);
+      dma4(reinterpret_cast<const char*>(base), row * (uint32_t)KB + 4 * c,
+           (lds_void*)(sc + r * RS + 256 * i));
+    }
+  }
+}
+
 template <int MQ, bool GU, int WK>
-__device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, int n0, float* red) {
+__device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, int n0, float* red,
+                                               uint8_t* sc) {
   constexpr int NR = 2;  // sets of 16 weight rows per wavefront group
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
-  const int K = sg.K;
+  const int K = sg.K, KB = K / 32, RS = w4_scale_stride(KB);
   const int grp = wv / WK, kw = wv % WK;
+  const int wrows = 16 * NR * (4 / WK);  // weight rows of the workgroup
+  const int n0wg = n0;
   n0 += 16 * NR * grp;
-  uint32_t wblk[NR], srow[NR];  // byte offsets of each 16-row block; this lane's scale rows
+  uint32_t wblk[NR], srow[NR];  // byte offsets of each 16-row block; this lane's scale rows in LDS
 #pragma unroll
   for (int h = 0; h < NR; ++h) {
     wblk[h] = (uint32_t)(n0 + 16 * h) * (uint32_t)(K / 2);
-    srow[h] = (uint32_t)(n0 + 16 * h + r16) * (uint32_t)(K / 32);
+    srow[h] = (uint32_t)(16 * NR * grp + 16 * h + r16) * (uint32_t)RS;
   }
+  const uint32_t srow1 = (uint32_t)(wrows * RS);  // the up matrix's scales follow the gate's
   uint32_t xrow[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
@@ -174,6 +206,8 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
     const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
     xrow[q] = (uint32_t)src * K * 2;
   }
+  MOE_WAITCNT(0, 15);  // (the row gathers have landed: no wait behind the staging loads later)
+  stage_scales_w4<GU>(sg, n0wg, wrows, KB, sc);
   f32x4 acc0[NR][MQ], acc1[NR][MQ];
 #pragma unroll
   for (int h = 0; h < NR; ++h)
@@ -184,7 +218,7 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
     }
   constexpr int U = (MQ == 1) ? 8 : 4;  // K-steps (of 32) per batch
   constexpr int NW = U / 4;              // 16-byte weight loads (32 values, one scale) per batch
-  struct Batch { uint4 w0[NR][NW], w1[NR][NW]; uint32_t s0[NR][NW], s1[NR][NW]; uint4 b[U][MQ]; };
+  struct Batch { uint4 w0[NR][NW], w1[NR][NW]; uint4 b[U][MQ]; uint32_t c0; };
   constexpr int CK = 32 * U;             // K of one batch of the 4 lane groups (a chunk)
   const int nchunk = K / CK / WK;        // chunks per wavefront: chunk c = j * WK + kw (interleaved)
   const int kr0 = nchunk * WK * CK;      // remainder [kr0, K), split contiguously
@@ -192,18 +226,14 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
   const int kr = kr0 + kw * rsteps * 32;
   auto load = [&](Batch& bt, int j) {
     const uint32_t c0 = (uint32_t)(j * WK + kw) * NW;  // first 128-value chunk of this batch
+    bt.c0 = c0;
 #pragma unroll
     for (int h = 0; h < NR; ++h)
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         const uint32_t wo = wblk[h] + (c0 + i) * 1024 + lane * 16;
-        const uint32_t so = srow[h] + (c0 + i) * 4 + kg;
         bt.w0[h][i] = gload16(sg.w0, wo);
-        bt.s0[h][i] = gload_u8(sg.e0, so);
-        if (GU) {
-          bt.w1[h][i] = gload16(sg.w1, wo);
-          bt.s1[h][i] = gload_u8(sg.e1, so);
-        }
+        if (GU) bt.w1[h][i] = gload16(sg.w1, wo);
       }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -214,13 +244,22 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
     }
   };
   auto compute = [&](const Batch& bt) {
+    // the scales of the batch's pieces: block 4 (c0 + i) + kg of the lane's rows
+    uint32_t s0[NR][NW], s1[NR][NW];
+#pragma unroll
+    for (int h = 0; h < NR; ++h)
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t so = srow[h] + (bt.c0 + i) * 4 + kg;
+        s0[h][i] = sc[so];
+        if (GU) s1[h][i] = sc[srow1 + so];
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int h = 0; h < NR; ++h) {
-        const uint4 a0 = decode_e2m1x8(dword_of(bt.w0[h][u >> 2], u & 3), bt.s0[h][u >> 2]);
-        const uint4 a1 =
-            GU ? decode_e2m1x8(dword_of(bt.w1[h][u >> 2], u & 3), bt.s1[h][u >> 2]) : a0;
+        const uint4 a0 = decode_e2m1x8(dword_of(bt.w0[h][u >> 2], u & 3), s0[h][u >> 2]);
+        const uint4 a1 = GU ? decode_e2m1x8(dword_of(bt.w1[h][u >> 2], u & 3), s1[h][u >> 2]) : a0;
 #pragma unroll
         for (int q = 0; q < MQ; ++q) {
           acc0[h][q] = mfma16(as_bf16x8(a0), as_bf16x8(bt.b[u][q]), acc0[h][q]);
@@ -228,14 +267,26 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
         }
       }
   };
+  // Two batches in registers, the next one's loads in flight while one is computed; scheduling
+  // barriers and branch-free loads (past the last batch: a re-read, never computed) keep the loads
+  // where they are written (see the bf16 streaming tile).  The first batch's loads go out before
+  // the wait for the staged scales.
   Batch b0, b1;
   if (nchunk > 0) load(b0, 0);
-  for (int j = 0; j < nchunk; j += 2) {
-    if (j + 1 < nchunk) load(b1, j + 1);
+  MOE_WAITCNT(0, 0);
+  __syncthreads();
+  int j = 0;
+  for (; j + 2 <= nchunk; j += 2) {
+    load(b1, j + 1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(b0);
-    if (j + 2 < nchunk) load(b0, j + 2);
-    if (j + 1 < nchunk) compute(b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, min(j + 2, nchunk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (j < nchunk) compute(b0);
   for (int ks = 0; ks < rsteps; ++ks) {  // remainder: lane kg takes K [32 st + 8 kg, +8)
     const uint32_t st = (uint32_t)(kr / 32 + ks);  // global 32-step: chunk st / 4, slot st % 4
     const uint32_t kl = 32 * st + 8 * kg;
@@ -246,9 +297,8 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
 #pragma unroll
     for (int h = 0; h < NR; ++h) {
       const uint32_t sb = srow[h] + st;
-      const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wblk[h] + wo), gload_u8(sg.e0, sb));
-      const uint4 a1 =
-          GU ? decode_e2m1x8(gload4(sg.w1, wblk[h] + wo), gload_u8(sg.e1, sb)) : a0;
+      const uint4 a0 = decode_e2m1x8(gload4(sg.w0, wblk[h] + wo), sc[sb]);
+      const uint4 a1 = GU ? decode_e2m1x8(gload4(sg.w1, wblk[h] + wo), sc[srow1 + sb]) : a0;
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
         acc0[h][q] = mfma16(as_bf16x8(a0), as_bf16x8(b[q]), acc0[h][q]);
@@ -269,15 +319,15 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
 // kStreamXlMaxK): rows one at a time, each staging its activations in LDS (xs) for the MFMA loop.
 template <bool GU, int WK, int MQMAX, bool W4>
 __device__ __forceinline__ void stream_rows_bf16(const Seg& sg, int m0, int rows, int n0,
-                                                 float* red, const char* xs) {
+                                                 float* red, const char* xs, uint8_t* sc) {
   static_assert(!(W4 && MQMAX == 0), "mxfp4 tiles do not stage a row in LDS");
   if (W4) {
     constexpr int MQ = MQMAX > 0 ? MQMAX : 1;
     for (int sub = 0; sub < rows; sub += 16 * MQ) {
       const int r = min(16 * MQ, rows - sub);
-      if (MQ == 1 || r <= 16) stream_tile_w4<1, GU, WK>(sg, m0 + sub, r, n0, red);
-      else if (MQ == 2 || r <= 32) stream_tile_w4<MQ >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red);
-      else stream_tile_w4<MQ, GU, WK>(sg, m0 + sub, r, n0, red);
+      if (MQ == 1 || r <= 16) stream_tile_w4<1, GU, WK>(sg, m0 + sub, r, n0, red, sc);
+      else if (MQ == 2 || r <= 32) stream_tile_w4<MQ >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red, sc);
+      else stream_tile_w4<MQ, GU, WK>(sg, m0 + sub, r, n0, red, sc);
     }
     return;
   }
@@ -313,6 +363,7 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
   __shared__ float red[3 * MQ * 4 * 2 * 64];
   // MQMAX = 0: the activations of a one-row tile
   __shared__ __attribute__((aligned(16))) char xs[MQMAX == 0 ? kStreamXlMaxK * 2 : 16];
+  extern __shared__ __attribute__((aligned(16))) uint8_t w4_sc[];  // mxfp4: staged scales
   const int nseg = meta[0], ntiles = meta[1];
   if ((int)blockIdx.x >= ntiles) return;
   for (int i = threadIdx.x; i < nseg; i += 256) seg_base[i] = segs[i].tile_base;
@@ -327,8 +378,10 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
     const int n0 = nt * sg.tn;
     // long K: 16 columns per wavefront group, 4-way split in K; else 32 columns, wavefront pairs
     // (mxfp4 tiles are twice as wide)
-    if ((W4 ? sg.tn / 2 : sg.tn) == 16) stream_rows_bf16<GU, 4, MQMAX, W4>(sg, m0, rows, n0, red, xs);
-    else stream_rows_bf16<GU, 2, MQMAX, W4>(sg, m0, rows, n0, red, xs);
+    if ((W4 ? sg.tn / 2 : sg.tn) == 16)
+      stream_rows_bf16<GU, 4, MQMAX, W4>(sg, m0, rows, n0, red, xs, w4_sc);
+    else
+      stream_rows_bf16<GU, 2, MQMAX, W4>(sg, m0, rows, n0, red, xs, w4_sc);
     t = gridDim.x + __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
     if (t >= ntiles) break;
   }
@@ -1146,9 +1199,12 @@ static void launch_stream_bf16(const Seg* ss, int32_t* ms, int num_cus, int64_t 
   if (w4) {
     // passes of at most 32 rows: the 64-row pass needs 222 VGPRs (one wavefront per SIMD);
     // heavier experts take more passes (flushed: 1.075 -> 0.94 ms at T = 64, 1.63 -> 1.50 ms at
-    // T = 256 on DeepSeek-V3-shaped layers)
-    if (max_rows <= 16) gemm_stream_bf16<GU, 1, true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-    else gemm_stream_bf16<GU, 2, true><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+    // T = 256 on DeepSeek-V3-shaped layers).  Dynamic LDS: the staged scales of the workgroup's
+    // weight rows (32 for K >= kStreamSplitK, else 64; gate and up) at a 256-byte-rounded stride.
+    const size_t lds = (size_t)(GU ? 2 : 1) * (max_k >= kStreamSplitK ? 32 : 64) *
+                       ((max_k / 32 + 255) / 256 * 256);
+    if (max_rows <= 16) gemm_stream_bf16<GU, 1, true><<<num_cus * 4, 256, lds, s>>>(ss, ms);
+    else gemm_stream_bf16<GU, 2, true><<<num_cus * 4, 256, lds, s>>>(ss, ms);
     return;
   }
   if (GU && max_rows <= 1 && max_k <= kStreamXlMaxK)  // (down tiles are too short to gain)

@@ -24,6 +24,7 @@
 #include "common.h"
 #include "fp8_codec.h"
 #include "kernels.h"
+#include "mfma_dev.h"
 #include "stream_dev.h"
 
 namespace moe {
@@ -173,32 +174,84 @@ __device__ __forceinline__ void mx_gateup_store(const Seg& sg, int m0, int rows,
   }
 }
 
+// Stages the E8M0 scales a pass reads into LDS (sc): the workgroup's wrows weight rows from n0 (gate,
+// then up), then the pass's 16 MQ token rows (padded rows as the first operand loads clamp them),
+// KB bytes each at a row stride of RS = KB rounded up to 256 bytes.  Read per K block and lane from
+// global memory instead, the scale bytes cost one load instruction touching 16 rows' cache lines
+// per chunk and operand: with them the gate/up tile streamed at 54% of HBM on a DeepSeek-V3-shaped
+// layer at T = 256, 79% in a timing build without them.  Each wavefront copies whole rows with
+// direct global->LDS loads (a dword per lane, 256 bytes per instruction; lanes past the row re-read
+// its last dword into the padding); the caller waits for them (vmcnt(0)) and holds a barrier
+// before reading.  (The previous pass's reads of sc are behind the barriers of its split-K
+// reduction.)
+__device__ __forceinline__ int mx_scale_stride(int KB) { return (KB + 255) & ~255; }
+
+template <int MQ, bool GU>
+__device__ __forceinline__ void stage_scales_mx(const Seg& sg, int n0, int wrows, int KB,
+                                                const int (&src)[MQ], uint8_t* sc) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KW = KB / 4;  // dwords per row (K is a multiple of 128)
+  const int RS = mx_scale_stride(KB);
+  const int nw = (GU ? 2 : 1) * wrows, nrow = nw + 16 * MQ;
+  for (int r = wv; r < nrow; r += 4) {
+    const uint8_t* base;
+    uint32_t row;
+    if (r < nw) {
+      base = GU && r >= wrows ? sg.e1 : sg.e0;
+      row = (uint32_t)(n0 + (r < wrows ? r : r - wrows));
+    } else {
+      // token row t's source: lane t % 16 of src[t / 16] (uniform, so no per-row vector load --
+      // whose wait would also wait for every staging load before it)
+      const int t = r - nw;
+      int v = src[0];
+#pragma unroll
+      for (int q = 1; q < MQ; ++q) v = t >= 16 * q ? src[q] : v;
+      base = sg.ae;
+      row = (uint32_t)__builtin_amdgcn_readlane(v, t & 15);
+    }
+    for (int i = 0; i < RS / 256; ++i) {
+      const int c = min(64 * i + lane, KW - 1);
+      dma4(reinterpret_cast<const char*>(base), row * (uint32_t)KB + 4 * c,
+           (lds_void*)(sc + r * RS + 256 * i));
+    }
+  }
+}
+
 // Rows [m0, m0 + rows) (rows <= 16 * MQ) of segment sg, weight rows n0 + 32 grp .. + 31 of the
 // calling group.  Wavefront kw takes the 128-value chunks kw, kw + WK, kw + 2 WK, ... of K.
 template <int MQ, bool GU, int WK>
-__device__ __forceinline__ void stream_tile_mx(const Seg& sg, int m0, int rows, int n0, float* red) {
+__device__ __forceinline__ void stream_tile_mx(const Seg& sg, int m0, int rows, int n0, float* red,
+                                               uint8_t* sc) {
   constexpr int NR = 2;  // sets of 16 weight rows per group
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int K = sg.K, KB = K / 32;  // scale bytes per row
   const int grp = wv / WK, kw = wv % WK;
+  const int wrows = 32 * (4 / WK);  // weight rows of the workgroup
+  const int RS = mx_scale_stride(KB);
+  const int n0wg = n0;
   n0 += 32 * grp;
-  uint32_t wblk[NR], wsc[NR];  // this lane's unit in each set's 16-row block; its scale byte
+  uint32_t wblk[NR], wsc[NR];  // this lane's unit in each set's 16-row block; its scale byte in LDS
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
     wblk[s] = (uint32_t)(n0 + 16 * s) * (uint32_t)(K / 2) + lane * 16;
-    wsc[s] = (uint32_t)(n0 + 16 * s + r16) * (uint32_t)KB + kg;
+    wsc[s] = (uint32_t)(32 * grp + 16 * s + r16) * (uint32_t)RS + kg;
   }
-  uint32_t xo[MQ], xso[MQ];  // this lane's activation bytes and scale bytes per token group
+  const uint32_t wsc1 = (uint32_t)(wrows * RS);  // the up matrix's scales follow the gate's
+  uint32_t xo[MQ], xso[MQ];  // this lane's activation bytes; its scale byte in LDS
+  const uint32_t xs0 = (uint32_t)((GU ? 2 : 1) * wrows * RS);
+  int src[MQ];
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
     int r = q * 16 + r16;
     r = r < rows ? r : rows - 1;  // padded columns re-read a valid row; never stored
     const int gr = sg.row0 + m0 + r;
-    const int src = sg.tok ? gload_i32(sg.tok, gr) : gr;
-    xo[q] = (uint32_t)src * (uint32_t)K + kg * 16;  // B halves: bytes [16 kg, +16) and [64 + 16 kg, +16)
-    xso[q] = (uint32_t)src * (uint32_t)KB + kg;
+    src[q] = sg.tok ? gload_i32(sg.tok, gr) : gr;
+    xo[q] = (uint32_t)src[q] * (uint32_t)K + kg * 16;  // B halves: bytes [16 kg, +16) and [64 + 16 kg, +16)
+    xso[q] = xs0 + (uint32_t)(q * 16 + r16) * (uint32_t)RS + kg;
   }
+  MOE_WAITCNT(0, 15);  // (the row gathers have landed: no wait behind the staging loads later)
+  stage_scales_mx<MQ, GU>(sg, n0wg, wrows, KB, src, sc);
   f32x4 acc0[NR][MQ], acc1[NR][MQ];
 #pragma unroll
   for (int s = 0; s < NR; ++s)
@@ -207,49 +260,75 @@ __device__ __forceinline__ void stream_tile_mx(const Seg& sg, int m0, int rows, 
       acc0[s][q] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc1[s][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  struct Blk { i32x4 w0[NR], w1[NR]; i32x8 x[MQ]; uint32_t s0[NR], s1[NR], sx[MQ]; };
+  // (a buffer holds the chunk's operands and its index; the scale bytes are read from LDS when the
+  // chunk is computed)
+  struct Blk { i32x4 w0[NR], w1[NR]; i32x8 x[MQ]; uint32_t c; };
   auto load = [&](Blk& b, int j) {
     const uint32_t c = (uint32_t)(j * WK + kw);
+    b.c = c;
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
       b.w0[s] = gload16i(sg.w0, wblk[s] + c * 1024);
-      b.s0[s] = gload_u8(sg.e0, wsc[s] + 4 * c);
-      if (GU) {
-        b.w1[s] = gload16i(sg.w1, wblk[s] + c * 1024);
-        b.s1[s] = gload_u8(sg.e1, wsc[s] + 4 * c);
-      }
+      if (GU) b.w1[s] = gload16i(sg.w1, wblk[s] + c * 1024);
     }
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
       const i32x4 lo = gload16i(sg.a, xo[q] + c * 128), hi = gload16i(sg.a, xo[q] + c * 128 + 64);
       b.x[q] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      b.sx[q] = gload_u8(sg.ae, xso[q] + 4 * c);
     }
   };
   auto compute = [&](const Blk& b) {
+    const uint32_t c4 = 4 * b.c;
+    uint32_t s0[NR], s1[NR], sx[MQ];
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      s0[s] = sc[wsc[s] + c4];
+      if (GU) s1[s] = sc[wsc1 + wsc[s] + c4];
+    }
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) sx[q] = sc[xso[q] + c4];
 #pragma unroll
     for (int s = 0; s < NR; ++s)
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        acc0[s][q] = mfma_mx(b.w0[s], b.s0[s], b.x[q], b.sx[q], acc0[s][q]);
-        if (GU) acc1[s][q] = mfma_mx(b.w1[s], b.s1[s], b.x[q], b.sx[q], acc1[s][q]);
+        acc0[s][q] = mfma_mx(b.w0[s], s0[s], b.x[q], sx[q], acc0[s][q]);
+        if (GU) acc1[s][q] = mfma_mx(b.w1[s], s1[s], b.x[q], sx[q], acc1[s][q]);
       }
   };
-  // the next chunk's loads are in flight while a chunk is computed (two buffers, unrolled by two)
+  // The next two chunks' loads are in flight while a chunk is computed (three buffers, unrolled by
+  // three; at the top of each round b0 and b1 hold chunks j and j + 1).  Scheduling barriers keep
+  // each load group where it is written: hoisted above the computes, the later groups' loads sat
+  // ahead of the chunk a compute waits for, and with in-order wait counts that wait drained them
+  // too.  Loads past the wavefront's last chunk re-read that chunk (never computed), so the loop
+  // body has no branch for the compiler to move the MFMAs across (with branches it also kept
+  // duplicate buffers: 224 instead of 172 VGPRs).  Flushed, DeepSeek-V3-shaped, with the scales
+  // staged in LDS: gate/up 0.827 -> 0.612 ms at T = 256 and 0.550 -> 0.458 ms at T = 64.
   const int nchunk = K / 128;
   const int nmine = (nchunk - kw + WK - 1) / WK;
-  if (nmine > 0) {
-    Blk b0, b1;
-    load(b0, 0);
-    int j = 0;
-    for (; j + 1 < nmine; j += 2) {
-      load(b1, j + 1);
-      compute(b0);
-      if (j + 2 < nmine) load(b0, j + 2);
-      compute(b1);
-    }
-    if (j < nmine) compute(b0);
+  Blk b0, b1, b2;
+  if (nmine > 0) load(b0, 0);
+  if (nmine > 1) load(b1, 1);
+  // (the first chunks' operand loads go out before the wait for the staged scales, so that their
+  // latencies overlap)
+  MOE_WAITCNT(0, 0);
+  __syncthreads();
+  int j = 0;
+  for (; j + 3 <= nmine; j += 3) {
+    load(b2, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, min(j + 3, nmine - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b1, min(j + 4, nmine - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b2);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (j < nmine) compute(b0);
+  if (j + 1 < nmine) compute(b1);
   if (GU) {
 #pragma unroll
     for (int s = 0; s < NR; ++s) mx_reduce_set<MQ, WK>(red, grp, kw, acc0[s], acc1[s]);
@@ -266,12 +345,13 @@ __device__ __forceinline__ void stream_tile_mx(const Seg& sg, int m0, int rows, 
 // Rows [m0, m0 + rows) of a tile in passes of at most 16 * MQMAX rows (the host instantiates MQMAX
 // from a bound on any expert's rows, which sets the kernel's register budget).
 template <bool GU, int WK, int MQMAX>
-__device__ __forceinline__ void stream_rows_mx(const Seg& sg, int m0, int rows, int n0, float* red) {
+__device__ __forceinline__ void stream_rows_mx(const Seg& sg, int m0, int rows, int n0, float* red,
+                                               uint8_t* sc) {
   for (int sub = 0; sub < rows; sub += 16 * MQMAX) {
     const int r = min(16 * MQMAX, rows - sub);
-    if (MQMAX == 1 || r <= 16) stream_tile_mx<1, GU, WK>(sg, m0 + sub, r, n0, red);
-    else if (MQMAX == 2 || r <= 32) stream_tile_mx<MQMAX >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red);
-    else stream_tile_mx<MQMAX, GU, WK>(sg, m0 + sub, r, n0, red);
+    if (MQMAX == 1 || r <= 16) stream_tile_mx<1, GU, WK>(sg, m0 + sub, r, n0, red, sc);
+    else if (MQMAX == 2 || r <= 32) stream_tile_mx<MQMAX >= 2 ? 2 : 1, GU, WK>(sg, m0 + sub, r, n0, red, sc);
+    else stream_tile_mx<MQMAX, GU, WK>(sg, m0 + sub, r, n0, red, sc);
   }
 }
 
@@ -283,6 +363,7 @@ __global__ __launch_bounds__(256) void gemm_stream_mx(const Seg* __restrict__ se
   __shared__ int slot;
   __shared__ int seg_base[kSegCap];
   __shared__ float red[3 * MQMAX * 8 * 64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t mx_sc[];  // staged scales (launch-sized)
   const int nseg = meta[0], ntiles = meta[1];
   if ((int)blockIdx.x >= ntiles) return;
   for (int i = threadIdx.x; i < nseg; i += 256) seg_base[i] = segs[i].tile_base;
@@ -296,8 +377,8 @@ __global__ __launch_bounds__(256) void gemm_stream_mx(const Seg* __restrict__ se
     const int rows = min(kStreamMaxRows, sg.rows - m0);
     const int n0 = nt * sg.tn;
     // long K: one group of 32 columns, 4-way split in K; else two groups of 32, wavefront pairs
-    if (sg.tn == 32) stream_rows_mx<GU, 4, MQMAX>(sg, m0, rows, n0, red);
-    else stream_rows_mx<GU, 2, MQMAX>(sg, m0, rows, n0, red);
+    if (sg.tn == 32) stream_rows_mx<GU, 4, MQMAX>(sg, m0, rows, n0, red, mx_sc);
+    else stream_rows_mx<GU, 2, MQMAX>(sg, m0, rows, n0, red, mx_sc);
     t = gridDim.x + __builtin_amdgcn_readfirstlane(pop_tile(&meta[kMetaQueue], &slot));
     if (t >= ntiles) break;
   }
@@ -306,19 +387,28 @@ __global__ __launch_bounds__(256) void gemm_stream_mx(const Seg* __restrict__ se
 // Passes of at most 32 rows: the 64-row pass needs 227 VGPRs, one wavefront per SIMD, and an
 // expert of up to 64 rows is rare in decode; a heavier expert takes more passes over its weights
 // (DeepSeek-V3-shaped, flushed: 1.065 -> 0.903 ms at T = 64 and 1.573 -> 1.348 ms at T = 256).
-template <bool GU>
-static void launch_stream_mx(const Seg* ss, int32_t* ms, int num_cus, int64_t max_rows,
-                             hipStream_t s) {
-  if (max_rows <= 16) gemm_stream_mx<GU, 1><<<num_cus * 4, 256, 0, s>>>(ss, ms);
-  else gemm_stream_mx<GU, 2><<<num_cus * 4, 256, 0, s>>>(ss, ms);
+// Dynamic LDS of a launch: the staged scales of one pass (the GEMM's K is the same for every
+// segment: no shared expert with mxfp4 weights).
+constexpr size_t mx_scale_lds(bool gu, int K, int mq) {
+  return (size_t)(((gu ? 2 : 1) * (K >= kStreamSplitK ? 32 : 64) + 16 * mq) *
+                  ((K / 32 + 255) / 256 * 256));
 }
 
-hipError_t launch_gemms_mx(const SelectOut& o, int g, int num_cus, int64_t max_rows,
+template <bool GU>
+static void launch_stream_mx(const Seg* ss, int32_t* ms, int num_cus, int64_t max_rows, int K,
+                             hipStream_t s) {
+  if (max_rows <= 16)
+    gemm_stream_mx<GU, 1><<<num_cus * 4, 256, mx_scale_lds(GU, K, 1), s>>>(ss, ms);
+  else
+    gemm_stream_mx<GU, 2><<<num_cus * 4, 256, mx_scale_lds(GU, K, 2), s>>>(ss, ms);
+}
+
+hipError_t launch_gemms_mx(const SelectOut& o, int g, int num_cus, int64_t max_rows, int K,
                            hipStream_t s) {
   const Seg* ss = o.segs + (size_t)(g * kNumFam + kFamStream) * kSegCap;
   int32_t* ms = o.meta + (g * kNumFam + kFamStream) * kMetaStride;
-  if (g == kGemmGateUp) launch_stream_mx<true>(ss, ms, num_cus, max_rows, s);
-  else launch_stream_mx<false>(ss, ms, num_cus, max_rows, s);
+  if (g == kGemmGateUp) launch_stream_mx<true>(ss, ms, num_cus, max_rows, K, s);
+  else launch_stream_mx<false>(ss, ms, num_cus, max_rows, K, s);
   return hipGetLastError();
 }
 

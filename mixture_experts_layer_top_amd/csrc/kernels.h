@@ -168,8 +168,8 @@ hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, bool stre
                             hipStream_t s);
 void launch_mfma_fp8(const Seg* segs, int32_t* meta, int gemm, int num_cus, hipStream_t s);
 // MXFP4 weights with MXFP8 activations (streaming tiles on the scaled f8f6f4 MFMA); max_rows
-// bounds any expert's rows.
-hipError_t launch_gemms_mx(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
+// bounds any expert's rows, K is the GEMM's (d for gate/up, f for down).
+hipError_t launch_gemms_mx(const SelectOut& o, int gemm, int num_cus, int64_t max_rows, int K,
                            hipStream_t s);
 // x [T][d] bf16 -> MXFP8: xq [T][d] e4m3, xe [T][d/32] E8M0 (smallest scale with no saturation).
 hipError_t launch_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t* xe,
