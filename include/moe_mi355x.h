@@ -93,6 +93,19 @@ enum moe_config {
   MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
   MOE_CONFIG_MFMA = 1,   /* LDS-tiled MFMA tiles: bf16 64, 128 or 256 rows (from the rows a tile
                             holds) x 256 weight rows; fp8 256 x 256 (mxfp4: MOE_ERR_UNSUPPORTED) */
+  MOE_CONFIG_FUSED = 2,  /* moe_layer of one bf16 token without a shared expert, d_model and d_ff
+                            <= 8192: the whole layer in one launch ("Weave", Abstract:
+                            an MoE layer as one persistent megakernel; GC-MoE, summary: a decode
+                            step launched as one graph).  Every workgroup routes the token and
+                            takes gate/up, then down tiles from a device queue; a down tile waits
+                            for its row's gate/up tiles and the last down tile of each column
+                            block combines it, through device counters that live
+                            in the first 36 KB of the workspace.  Those 36 KB must be zero before
+                            the first such call (zero the workspace once when allocating it);
+                            every call leaves them zero, and no other call writes them.  A wait
+                            that does not end within about a second sets the int at byte offset
+                            32768 of the workspace and gives up (the output is then wrong).  Other
+                            problems, and moe_grouped_ffn, give MOE_ERR_UNSUPPORTED */
   MOE_CONFIG_POLICY0 = 16 /* 16 + i (i < MOE_NUM_POLICIES): selection policy i, whatever the
                              histogram (other values: MOE_ERR_INVALID_ARG) */
 };

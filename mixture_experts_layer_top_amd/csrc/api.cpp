@@ -74,8 +74,12 @@ int check_problem(const moe_problem* p) {
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
   const bool policy = p->config >= kConfigPolicy0 && p->config < kConfigPolicy0 + kNumPolicies;
-  if ((p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_MFMA) && !policy)
+  if ((p->config < MOE_CONFIG_AUTO || p->config > MOE_CONFIG_FUSED) && !policy)
     return MOE_ERR_INVALID_ARG;
+  if (p->config == MOE_CONFIG_FUSED &&
+      (p->T > 1 || p->wdtype != MOE_DTYPE_BF16 || p->has_shared || p->d_model > kStreamXlMaxK ||
+       p->d_ff > kStreamXlMaxK))
+    return MOE_ERR_UNSUPPORTED;
   if (policy && p->wdtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;  // (streaming only)
   // 32-bit byte offsets: x [T][d], h [T*k][f], y [T*k][d], shared h [T][f_sh] (2 bytes per value
   // at most) and each expert's [f][d] matrices must stay below 4 GiB
@@ -343,6 +347,7 @@ int moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_per
                     void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_problem(p);
   if (st) return st;
+  if (p->config == MOE_CONFIG_FUSED) return MOE_ERR_UNSUPPORTED;  // (a layer-only path)
   st = check_weights(p, w, false);
   if (st) return st;
   if (p->T == 0) return MOE_OK;
@@ -406,7 +411,7 @@ int moe_combine(const void* y_perm, const int32_t* slot_dst, const float* topk_w
 // Workspace of the whole layer (see carve_layer for the order).
 namespace {
 struct LayerWs {
-  int32_t *ids, *counts, *offsets, *perm_src, *slot_dst, *tok, *rank, *hist;
+  int32_t *sync, *ids, *counts, *offsets, *perm_src, *slot_dst, *tok, *rank, *hist;
   float* w;
   uint8_t* xq;
   float* xs;
@@ -418,6 +423,9 @@ struct LayerWs {
 void carve_layer(Carver& c, const moe_problem* p, LayerWs& L) {
   const size_t n = (size_t)p->T * p->top_k;
   const int E = p->num_experts;
+  // the fused single-token launch's counters come first, in every layer workspace, so that no
+  // other layer call writes them
+  L.sync = c.take<int32_t>(kFusedSyncInts);
   L.ids = c.take<int32_t>(n);
   L.w = c.take<float>(n);
   L.counts = c.take<int32_t>(E);
@@ -514,6 +522,34 @@ int layer_impl(const moe_problem* p, const float* logits, const void* x, const m
   SelectOut o{L.ffn.segs, L.ffn.meta, L.ffn.split_part};
 
   hipError_t e = mark(0);
+  if (p->config == MOE_CONFIG_FUSED) {  // (check_problem admitted one bf16 token, no shared expert)
+    Decode1Args da;
+    std::memset(&da, 0, sizeof(da));
+    da.logits = logits;
+    da.E = E;
+    da.k = k;
+    da.d = d;
+    da.f = p->d_ff;
+    da.x = x;
+    da.w_gate = w->w_gate;
+    da.w_up = w->w_up;
+    da.w_down = w->w_down;
+    da.h = L.ffn.h;
+    da.y = L.y;
+    da.ids = ids;
+    da.w = wts;
+    da.counts = counts;
+    da.offsets = offsets;
+    da.perm_src = perm_src;
+    da.slot_dst = slot_dst;
+    da.tok = L.tok;
+    da.sync = L.sync;
+    da.out = out;
+    for (int i = 1; i <= 6 && e == hipSuccess; ++i) e = mark(i);
+    if (e == hipSuccess) e = launch_decode1_fused(da, cus, stream);
+    if (e == hipSuccess) e = mark(7);
+    return hip_status(e);
+  }
   // a single bf16 token without a shared expert: routing runs inside the gate/up kernel, which
   // also writes the routing outputs and the down GEMM's segments (phases 1 to 4 are empty)
   const bool decode1 = T == 1 && p->wdtype == MOE_DTYPE_BF16 && !p->has_shared &&

@@ -103,5 +103,30 @@ __device__ __forceinline__ void gstore_f32(float* p, size_t i, float v) {
   reinterpret_cast<__attribute__((address_space(1))) float*>((gwchar*)p)[i] = v;
 }
 
+// Device-coherent accesses (relaxed atomics at agent scope: global loads and stores with sc1): data
+// written by one XCD and read by another within one kernel, whose L2s are not coherent.  The
+// writer's stores are complete (acknowledged at the coherence point) once its vmcnt drains; a
+// reader that then observes the writer's counter sees them with coherent loads.
+__device__ __forceinline__ void gstore8_coh(void* base, size_t off, uint2 v) {
+  const uint64_t x = ((uint64_t)v.y << 32) | v.x;
+  __hip_atomic_store(reinterpret_cast<__attribute__((address_space(1))) uint64_t*>((gwchar*)base + off),
+                     x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 gload8_coh(const void* base, size_t off) {
+  const uint64_t x = __hip_atomic_load(
+      reinterpret_cast<const __attribute__((address_space(1))) uint64_t*>((gchar*)base + off),
+      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return uint2{(uint32_t)x, (uint32_t)(x >> 32)};
+}
+__device__ __forceinline__ int32_t counter_load(int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t counter_add(int32_t* p, int32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void counter_store(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 }  // namespace moe

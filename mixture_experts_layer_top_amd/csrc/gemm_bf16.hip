@@ -16,6 +16,8 @@
 //    of 128x128, MFMA 32x32x16.
 // Both are persistent: a fixed grid pops tiles from device queues (zeroed by the selection
 // kernel), heaviest experts first, m-tiles of one weight tile adjacent in the queue.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
@@ -27,7 +29,7 @@ namespace moe {
 // XL > 0: the tile has one row, whose activations (K bf16) the MFMA loop reads from LDS (xs): with
 // XL = 1 the tile stages them from xrow once its first weight loads are in flight, with XL = 2 the
 // caller has staged them.
-template <int MQ, bool GU, int WK, int XL = 0>
+template <int MQ, bool GU, int WK, int XL = 0, bool COH = false>
 __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows, int n0,
                                                  float* red, const char* xs = nullptr,
                                                  const void* xrow = nullptr) {
@@ -119,7 +121,7 @@ __device__ __forceinline__ void stream_tile_bf16(const Seg& sg, int m0, int rows
       if (GU) acc1[q] = mfma16(as_bf16x8(a1), as_bf16x8(b), acc1[q]);
     }
   }
-  stream_tile_finish<MQ, GU, WK>(sg, m0, rows, n0, red, acc0, acc1);
+  stream_tile_finish<MQ, GU, WK, COH>(sg, m0, rows, n0, red, acc0, acc1);
 }
 
 // MXFP4 weights (W4A16), in the library's tiled layout (moe_mxfp4_tile): per 16-row block and
@@ -1144,6 +1146,212 @@ __global__ __launch_bounds__(256) void decode1_gate_up_bf16(Decode1Args a, Selec
     sg.tn = tn;
     stream_tile_bf16<1, true, WK, 2>(sg, 0, 1, (t - r * per_exp) * tn, red, xs);
   }
+}
+
+// ------------------------------------------------------------------------------------------------
+// The whole single-token layer in one launch (MOE_CONFIG_FUSED): Weave (Abstract) runs an MoE layer
+// as one persistent megakernel whose workers are scheduled over its phases, and GC-MoE (summary)
+// launches its decode path as one graph.  Here every workgroup routes the token itself (as the
+// single-token gate/up kernel does), takes its gate/up tiles, then its down tiles, each waiting for
+// the gate/up tiles of its row through a device counter; the last down tile of each column block
+// (a counter again) does the combine of that block.  Cooperative launch: every workgroup is
+// resident, so the static tile assignment cannot wait on a workgroup that has not started.  Data
+// that crosses XCDs (h, y) goes through device-coherent stores and loads (common.h), with the
+// writer's stores drained before its counter increment; no fence writes back or invalidates an L2.
+// The counters live in the first kFusedSyncInts ints of the workspace (zero before the first
+// launch); each launch returns them to zero: the last down tile of a row past its wait clears that
+// row's counters, the combining tile its column block's.  (A variant that handed the tiles out
+// from a device ticket queue under a plain launch did not finish its first test on the GPU; its
+// cause was not found, so it was dropped.)
+// Counter layout (ints): the polled per-row counters 4 KB apart (so that a thousand workgroups
+// polling them do not all load one memory channel), gate/up tiles finished of row r at
+// kFusedSyncRow r and its down tiles past their wait 32 ints further; the error flag at
+// kFusedSyncErr; down tiles finished of column block b at kFusedSyncDn + b.
+constexpr int kFusedSyncRow = 1024;
+constexpr int kFusedSyncErr = kMaxTopK * kFusedSyncRow;
+constexpr int kFusedSyncDn = kFusedSyncErr + 32;
+constexpr int kFusedMaxSpins = 1 << 20;  // ~1 s of polls: then the flag is set and the wait ends
+static_assert(kFusedSyncDn + kStreamXlMaxK / 16 <= kFusedSyncInts, "fused counters");
+
+template <int VPL, int WKG, int WKD>
+__global__ __launch_bounds__(256) void decode1_fused_bf16(Decode1Args a) {
+  constexpr int tn = WKG == 4 ? 16 : 32;   // gate/up tile columns
+  constexpr int dtn = WKD == 4 ? 16 : 32;  // down tile columns
+  __shared__ int s_ids[kMaxTopK];   // the routing, in slot order
+  __shared__ float s_w[kMaxTopK];
+  __shared__ int s_exp[kMaxTopK];   // the selected experts in increasing id (row order)
+  __shared__ int s_row[kMaxTopK];   // slot -> row
+  __shared__ int s_flag;
+  __shared__ float red[3 * 4 * 2 * 64];
+  __shared__ __attribute__((aligned(16))) char xs[kStreamXlMaxK * 2];
+  const int tid = threadIdx.x, k = a.k;
+  const int per_exp = a.f / tn, ntiles = k * per_exp;
+  const int dt = a.d / dtn, ndown = k * dt;
+  const bool lead = blockIdx.x == 0;
+  int32_t* sync = a.sync;
+  if (tid < 64) {
+    route_token<VPL>(a.logits, 0, a.E, k, nullptr, s_w, s_ids);
+  } else {  // meanwhile the other wavefronts stage the token's activations
+    const uint4* xg = static_cast<const uint4*>(a.x);
+    uint4* xw = reinterpret_cast<uint4*>(xs);
+    for (int i = tid - 64; i < a.d / 8; i += 192) xw[i] = xg[i];
+  }
+  __syncthreads();
+  if (tid < k) {  // the k ids are distinct: row = number of selected ids below this one
+    const int e = s_ids[tid];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += s_ids[j] < e ? 1 : 0;
+    s_exp[r] = e;
+    s_row[tid] = r;
+    if (lead) {
+      a.ids[tid] = e;
+      a.w[tid] = s_w[tid];
+      a.perm_src[r] = tid;
+      a.slot_dst[tid] = r;
+      a.tok[r] = 0;
+    }
+  }
+  if (lead) {
+    for (int e = tid; e <= a.E; e += 256) {
+      int below = 0, hit = 0;
+      for (int j = 0; j < k; ++j) {
+        below += s_ids[j] < e ? 1 : 0;
+        hit |= s_ids[j] == e ? 1 : 0;
+      }
+      if (e < a.E) a.counts[e] = hit;
+      a.offsets[e] = below;
+    }
+  }
+  __syncthreads();
+  // gate/up tiles
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // gate/up tile: h through coherent stores, then the row's counter
+    const int r = t / per_exp, e = s_exp[r];
+    Seg sg;
+    sg.a = a.x;
+    sg.tok = nullptr;
+    sg.as = nullptr;
+    sg.w0 = static_cast<const uint8_t*>(a.w_gate) + (size_t)e * a.f * a.d * 2;
+    sg.w1 = static_cast<const uint8_t*>(a.w_up) + (size_t)e * a.f * a.d * 2;
+    sg.s0 = sg.s1 = nullptr;
+    sg.e0 = sg.e1 = nullptr;
+    sg.ae = nullptr;
+    sg.oute = nullptr;
+    sg.out = a.h;
+    sg.outs = nullptr;
+    sg.row0 = r;
+    sg.rows = 1;
+    sg.N = a.f;
+    sg.K = a.d;
+    sg.tile_base = r * per_exp;
+    sg.mtiles = 1;
+    sg.ntiles = per_exp;
+    sg.expert = e;
+    sg.tn = tn;
+    stream_tile_bf16<1, true, WKG, 2, true>(sg, 0, 1, (t - r * per_exp) * tn, red, xs);
+    MOE_WAITCNT(0, 0);  // this wavefront's h stores are acknowledged
+    __syncthreads();
+    if (tid == 0) counter_add(&sync[kFusedSyncRow * r], 1);
+  }
+  __syncthreads();  // (every wavefront is done reading x from xs)
+  // down tiles
+  for (int t = blockIdx.x; t < ndown; t += gridDim.x) {
+    // down tile: wait for the row's gate/up tiles, stage its h row, stream, count, maybe combine
+    const int r = t / dt, cb = t - r * dt, e = s_exp[r];
+    if (tid == 0) {
+      int spins = 0;
+      while (counter_load(&sync[kFusedSyncRow * r]) < per_exp) {
+        if (++spins > kFusedMaxSpins) {
+          counter_store(&sync[kFusedSyncErr], 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(32);  // (about 1 us between polls)
+      }
+      if (counter_add(&sync[kFusedSyncRow * r + 32], 1) == dt - 1) {  // the last waiter clears both
+        counter_store(&sync[kFusedSyncRow * r], 0);
+        counter_store(&sync[kFusedSyncRow * r + 32], 0);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < a.f / 4; i += 256)
+      reinterpret_cast<uint2*>(xs)[i] = gload8_coh(a.h, ((size_t)r * a.f + 4 * i) * 2);
+    __syncthreads();
+    Seg sg;
+    sg.a = a.h;
+    sg.tok = nullptr;
+    sg.as = nullptr;
+    sg.w0 = static_cast<const uint8_t*>(a.w_down) + (size_t)e * a.d * a.f * 2;
+    sg.w1 = nullptr;
+    sg.s0 = sg.s1 = nullptr;
+    sg.e0 = sg.e1 = nullptr;
+    sg.ae = nullptr;
+    sg.oute = nullptr;
+    sg.out = a.y;
+    sg.outs = nullptr;
+    sg.row0 = r;
+    sg.rows = 1;
+    sg.N = a.d;
+    sg.K = a.f;
+    sg.tile_base = r * dt;
+    sg.mtiles = 1;
+    sg.ntiles = dt;
+    sg.expert = e;
+    sg.tn = dtn;
+    stream_tile_bf16<1, false, WKD, 2, true>(sg, 0, 1, cb * dtn, red, xs);
+    MOE_WAITCNT(0, 0);  // this wavefront's y stores are acknowledged
+    __syncthreads();
+    if (tid == 0) s_flag = counter_add(&sync[kFusedSyncDn + cb], 1) == k - 1;
+    __syncthreads();
+    if (s_flag) {
+      // the combine of columns [cb * dtn, +dtn), as combine_kernel: fp32 in slot order, one RNE
+      if (tid < dtn / 4) {
+        const int c = cb * dtn + 4 * tid;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+          const uint2 v = gload8_coh(a.y, ((size_t)s_row[j] * a.d + c) * 2);
+          const float wj = s_w[j];
+          acc[0] += wj * bf16_to_f32(uint16_t(v.x & 0xFFFF));
+          acc[1] += wj * bf16_to_f32(uint16_t(v.x >> 16));
+          acc[2] += wj * bf16_to_f32(uint16_t(v.y & 0xFFFF));
+          acc[3] += wj * bf16_to_f32(uint16_t(v.y >> 16));
+        }
+        uint2 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        gstore8(a.out, (size_t)c * 2, o);
+      }
+      if (tid == 0) counter_store(&sync[kFusedSyncDn + cb], 0);
+    }
+    __syncthreads();  // (s_flag and xs are reused by the next tile)
+  }
+}
+
+template <int VPL, int WKG, int WKD>
+static hipError_t launch_fused_t(const Decode1Args& a, int num_cus, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&decode1_fused_bf16<VPL, WKG, WKD>);
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
+  if (e != hipSuccess) return e;
+  const int g = std::max(1, std::min(4, per_cu)) * num_cus;
+  Decode1Args arg = a;
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(fn, dim3(g), dim3(256), args, 0, s);
+}
+
+template <int VPL>
+static hipError_t launch_fused_vpl(const Decode1Args& a, int num_cus, hipStream_t s) {
+  const bool g4 = a.d >= kStreamSplitK, d4 = a.f >= kStreamSplitK;
+  if (g4 && d4) return launch_fused_t<VPL, 4, 4>(a, num_cus, s);
+  if (g4) return launch_fused_t<VPL, 4, 2>(a, num_cus, s);
+  if (d4) return launch_fused_t<VPL, 2, 4>(a, num_cus, s);
+  return launch_fused_t<VPL, 2, 2>(a, num_cus, s);
+}
+
+hipError_t launch_decode1_fused(const Decode1Args& a, int num_cus, hipStream_t s) {
+  if (a.E <= 64) return launch_fused_vpl<1>(a, num_cus, s);
+  if (a.E <= 128) return launch_fused_vpl<2>(a, num_cus, s);
+  if (a.E <= 256) return launch_fused_vpl<4>(a, num_cus, s);
+  return launch_fused_vpl<8>(a, num_cus, s);
 }
 
 template <int VPL>

@@ -191,9 +191,15 @@ struct Decode1Args {
   int32_t* counts; int32_t* offsets;      // [E], [E + 1]
   int32_t* perm_src; int32_t* slot_dst;   // [k]
   int32_t* tok;                           // [k]
+  int32_t* sync;                          // fused launch: kFusedSyncInts counters (zero on entry)
+  void* out;                              // fused launch: [d] bf16
 };
+constexpr int kFusedSyncInts = 9216;  // the fused single-token launch's counters (36 KB)
 hipError_t launch_decode1_bf16(const Decode1Args& a, const SelectOut& o, int num_cus,
                                hipStream_t s);
+// The whole single-token layer (routing, gate/up, down, combine) in one launch (MOE_CONFIG_FUSED;
+// bf16, no shared expert, d and f <= kStreamXlMaxK).
+hipError_t launch_decode1_fused(const Decode1Args& a, int num_cus, hipStream_t s);
 hipError_t launch_combine(const void* y, const int32_t* slot_dst, const float* w, int T, int k,
                           int d, const void* shared_y, void* out, hipStream_t s);
 hipError_t launch_quant_act(const void* x, int T, int d, uint8_t* xq, float* xs, hipStream_t s);

@@ -29,7 +29,7 @@ __device__ __forceinline__ int pop_tile(int32_t* queue, int* slot) {
 // kw = 1..WK-1 park their partials in LDS and wavefront kw = 0 adds them in order (slots
 // grp * (WK - 1) + kw - 1, at most 3), then applies SwiGLU (gate/up) and stores bf16.  n0 is the
 // first column of the calling wavefront's group of 16.
-template <int MQ, bool GU, int WK>
+template <int MQ, bool GU, int WK, bool COH = false>
 __device__ __forceinline__ void stream_tile_finish(const Seg& sg, int m0, int rows, int n0,
                                                    float* red, f32x4 (&acc0)[MQ], f32x4 (&acc1)[MQ]) {
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -74,7 +74,9 @@ __device__ __forceinline__ void stream_tile_finish(const Seg& sg, int m0, int ro
       uint2 pk;
       pk.x = pack_bf16x2(v[0], v[1]);
       pk.y = pack_bf16x2(v[2], v[3]);
-      gstore8(sg.out, ((size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) * 2, pk);
+      const size_t off = ((size_t)(sg.row0 + m0 + r) * N + n0 + kg * 4) * 2;
+      if (COH) gstore8_coh(sg.out, off, pk);  // (read by other XCDs in the same launch)
+      else gstore8(sg.out, off, pk);
     }
   }
 }

@@ -18,7 +18,8 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(_PKG, "libmoe_mi355x.so
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 DTYPE_BF16, DTYPE_FP8, DTYPE_MXFP4, DTYPE_MXFP4_A8 = 0, 1, 2, 3
-CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA = -1, 0, 1
+CONFIG_AUTO, CONFIG_STREAM, CONFIG_MFMA, CONFIG_FUSED = -1, 0, 1, 2
+FUSED_SYNC_BYTES = 36864    # the fused single-token launch's counters at the workspace's start
 CONFIG_POLICY0, NUM_POLICIES = 16, 8  # config = 16 + i forces selection policy i (bf16)
 LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
 
@@ -300,7 +301,9 @@ class Layer:
         self.p = problem(T, d, f, E, k, shared_f=shf, config=config, wdtype=weights.wdtype)
         self.w = weights.struct()
         dev = device if device is not None else weights.gate.device
-        self.ws = torch.empty(max(1, lib().moe_layer_workspace_bytes(ctypes.byref(self.p))),
+        # (zeroed once: the fused single-token launch keeps its counters, which every call
+        # leaves zero, in the first FUSED_SYNC_BYTES)
+        self.ws = torch.zeros(max(1, lib().moe_layer_workspace_bytes(ctypes.byref(self.p))),
                               dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, d), dtype=torch.int16, device=dev)
 

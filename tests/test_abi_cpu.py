@@ -214,9 +214,40 @@ def test_policy_configs():
     ws = L.moe_layer_workspace_bytes
     for i in range(moe.NUM_POLICIES):
         assert ws(ctypes.byref(moe.problem(64, 256, 512, 8, 2, config=moe.CONFIG_POLICY0 + i))) > 0
-    for bad in (2, 15, moe.CONFIG_POLICY0 + moe.NUM_POLICIES, -2):
+    for bad in (3, 15, moe.CONFIG_POLICY0 + moe.NUM_POLICIES, -2):
         assert ws(ctypes.byref(moe.problem(64, 256, 512, 8, 2, config=bad))) == 0
     fp8 = moe.problem(64, 256, 512, 8, 2, fp8=True, config=moe.CONFIG_POLICY0)
     w = moe.Weights(w_gate=256, w_up=512, w_down=768)
     assert L.moe_layer(ctypes.byref(fp8), 1024, 2048, ctypes.byref(w), 4096, None, 8192, 16,
                        None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_fused_config_limits():
+    """MOE_CONFIG_FUSED runs the whole layer of one bf16 token in one launch: more tokens, other
+    weight formats, a shared expert, d_model or d_ff above 8192, and the grouped FFN entry point are
+    rejected before any device work; the layer workspace starts with the launch's 36 KB of counters."""
+    L = moe.lib()
+    ws = L.moe_layer_workspace_bytes
+    F = moe.CONFIG_FUSED
+    ok = moe.problem(1, 7168, 2048, 256, 8, config=F)
+    assert ws(ctypes.byref(ok)) > moe.FUSED_SYNC_BYTES
+    assert ws(ctypes.byref(moe.problem(0, 256, 512, 8, 2, config=F))) > 0  # T = 0: a no-op call
+    assert ws(ctypes.byref(moe.problem(1, 8192, 8192, 8, 2, config=F))) > 0
+    for bad in (moe.problem(2, 256, 512, 8, 2, config=F),
+                moe.problem(1, 256, 512, 8, 2, fp8=True, config=F),
+                moe.problem(1, 256, 512, 8, 2, shared_f=256, config=F),
+                moe.problem(1, 8320, 512, 8, 2, config=F),
+                moe.problem(1, 256, 8320, 8, 2, config=F),
+                moe.problem(1, 256, 512, 8, 2, wdtype=moe.DTYPE_MXFP4, config=F)):
+        assert ws(ctypes.byref(bad)) == 0
+        w = moe.Weights(w_gate=256, w_up=512, w_down=768)
+        assert L.moe_layer(ctypes.byref(bad), 1024, 2048, ctypes.byref(w), 4096, None, 8192, 1 << 20,
+                           None) == moe.MOE_ERR_UNSUPPORTED
+    # the grouped FFN has no fused form
+    w = moe.Weights(w_gate=256, w_up=512, w_down=768)
+    assert L.moe_grouped_ffn(ctypes.byref(ok), 1024, None, 2048, 4096, ctypes.byref(w), 8192,
+                             12288, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
+    # every layer workspace holds the counters, so the fused and automatic forms of a problem need
+    # the same bytes
+    auto = moe.problem(1, 7168, 2048, 256, 8)
+    assert ws(ctypes.byref(ok)) == ws(ctypes.byref(auto))

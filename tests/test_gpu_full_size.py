@@ -36,11 +36,11 @@ def moe():
     return m
 
 
-def _run(moe, inp):
+def _run(moe, inp, config=-1):
     """One layer call keeping every routing output, and a second call that must give the same
     bits."""
     p = inp.p
-    L = moe.Layer(inp.expert_weights(), p.T, p.E, p.k)
+    L = moe.Layer(inp.expert_weights(), p.T, p.E, p.k, config=config)
     keep = dict(topk_ids=torch.empty((p.T, p.k), dtype=torch.int32, device="cuda"),
                 topk_w=torch.empty((p.T, p.k), dtype=torch.float32, device="cuda"),
                 counts=torch.empty(p.E, dtype=torch.int32, device="cuda"),
@@ -66,9 +66,9 @@ def _check_routing(p, keep, ids, w, counts, offsets, perm_src, slot_dst):
     assert np.array_equal(keep["slot_dst"], slot_dst)
 
 
-def _check_whole(moe, inp, ref, tol):
+def _check_whole(moe, inp, ref, tol, config=-1):
     """Every routing output and every output value against a whole-layer oracle result."""
-    got, keep = _run(moe, inp)
+    got, keep = _run(moe, inp, config)
     _check_routing(inp.p, keep, ref["ids"], ref["w"], ref["counts"], ref["offsets"],
                    ref["perm_src"], ref["slot_dst"])
     err = rel_err(got, ref["out"])
@@ -112,6 +112,13 @@ def dsv3(moe):
 def test_dsv3_decode_full(moe, dsv3, p):
     inp, ref = dsv3[p.name]
     _check_whole(moe, inp, ref, BF16_TOL)
+
+
+# the single-token points through the one-launch layer (MOE_CONFIG_FUSED)
+@pytest.mark.parametrize("p", [p for p in DSV3_POINTS if p.T == 1], ids=lambda p: p.name)
+def test_dsv3_decode_fused_full(moe, dsv3, p):
+    inp, ref = dsv3[p.name]
+    _check_whole(moe, inp, ref, BF16_TOL, config=moe.CONFIG_FUSED)
 
 
 # ------------------------------------------------------------------------------------------------

@@ -225,6 +225,43 @@ def test_decode1_matches_oracle(moe, p, config):
     _check_layer(moe, Inputs(p), config=config, runs=2)
 
 
+# The whole single-token layer in one launch (config FUSED): every single-token shape whose d and f
+# stay within 8192 (so both tile widths of each GEMM, every routing width, more tiles than
+# workgroups), against the oracle; then three calls on one Layer: the device counters that order
+# the launch's phases must return to zero after each call (the same bits every time, the counter
+# block zero afterwards, the error flag clear), and the result must equal the multi-launch path's
+# bits (the same tiles in the same order, read through LDS and coherent loads).
+FUSED = [p for p in DECODE1 if p.d <= 8192 and p.f <= 8192]
+
+
+@pytest.mark.parametrize("p", FUSED, ids=lambda p: p.name)
+def test_fused_decode_matches_oracle(moe, p):
+    inp = Inputs(p)
+    _check_layer(moe, inp, config=moe.CONFIG_FUSED)
+    L = moe.Layer(inp.expert_weights(), 1, p.E, p.k, config=moe.CONFIG_FUSED)
+    outs = []
+    for _ in range(3):
+        outs.append(L(inp.d_logits, inp.d_x).clone())
+        torch.cuda.synchronize()
+        sync = L.ws[:moe.FUSED_SYNC_BYTES].view(torch.int32).cpu().numpy()
+        assert not sync.any(), np.flatnonzero(sync)[:8]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    multi = moe.layer(inp.d_logits, inp.d_x, inp.expert_weights(), p.k, config=-1)
+    assert torch.equal(multi, outs[0])
+
+
+def test_fused_ties(moe):
+    inp = Inputs(_small("fused_ties", T=1, d=256, f=256, E=256, k=8, cfg_index=168))
+    rng = np.random.default_rng(7)
+    L = rng.integers(-1, 2, size=(1, 256)).astype(np.float32)
+    L[0, ::5] = -0.0
+    L[0, 1::5] = 0.0
+    inp.logits = L
+    inp.d_logits = torch.from_numpy(L).cuda()
+    _check_layer(moe, inp, config=moe.CONFIG_FUSED)
+
+
 # Ties inside the single-token routing: equal logits (and +0.0 / -0.0) go to the lower expert id.
 @pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (512, 3)])
 def test_decode1_ties(moe, E, k):
