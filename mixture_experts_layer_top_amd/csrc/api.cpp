@@ -197,7 +197,7 @@ PolicyBounds policy_bounds(const moe_problem* p) {
 hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int64_t max_rows,
                         int64_t total_rows, int cus, hipStream_t s) {
   if (p->wdtype == MOE_DTYPE_FP8_E4M3)
-    return moe::launch_gemms_fp8(o, gemm, cus, p->config != MOE_CONFIG_MFMA,
+    return moe::launch_gemms_fp8(o, gemm, cus, max_rows, p->config != MOE_CONFIG_MFMA,
                                  p->config == MOE_CONFIG_MFMA ||
                                      (p->config == MOE_CONFIG_AUTO && max_rows > kFp8MfmaRows),
                                  s);

@@ -164,8 +164,8 @@ hipError_t launch_gemms_bf16(const SelectOut& o, int gemm, int num_cus, int64_t 
                              bool w4);
 // fp8: the streaming kernel and/or the LDS-staged MFMA kernel of one GEMM (each launched only when
 // its list may hold tiles).
-hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, bool stream, bool mfma,
-                            hipStream_t s);
+hipError_t launch_gemms_fp8(const SelectOut& o, int gemm, int num_cus, int64_t max_rows,
+                            bool stream, bool mfma, hipStream_t s);
 void launch_mfma_fp8(const Seg* segs, int32_t* meta, int gemm, int num_cus, hipStream_t s);
 // MXFP4 weights with MXFP8 activations (streaming tiles on the scaled f8f6f4 MFMA); max_rows
 // bounds any expert's rows, K is the GEMM's (d for gate/up, f for down).
