@@ -682,7 +682,9 @@ def main() -> int:
         timing = "median of per-step HIP events around the layer, no cache flush"
     value = p.T / (ms_per_step * 1e-3)
 
-    peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" else PEAK_BF16_TFLOPS
+    # (mxfp4 x mxfp8 products run at the fp8 rate: the doubled fp4/fp6 rate needs both operands
+    # narrow; mxfp4 weights with bf16 activations are expanded to bf16 products)
+    peak_flops = PEAK_FP8_TFLOPS if p.wdtype == "fp8" or p.act_mx8 else PEAK_BF16_TFLOPS
     # the dominant kernel's bound: whichever of its algorithmic flops and bytes takes longer at peak
     prefill = alg["flop_gu"] / (peak_flops * 1e12) > alg["bytes_gu"] / (PEAK_HBM_GBS * 1e9)
     gu_ms = statistics.mean(gu_launch_ms)

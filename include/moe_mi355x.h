@@ -73,11 +73,13 @@ enum moe_dtype {
   MOE_DTYPE_BF16 = 0,
   MOE_DTYPE_FP8_E4M3 = 1,
   MOE_DTYPE_MXFP4 = 2, /* expert weights only: bf16 activations, no shared expert, streaming tiles
-                          only (config MOE_CONFIG_MFMA and has_shared give MOE_ERR_UNSUPPORTED) */
+                          only (config MOE_CONFIG_MFMA and has_shared give MOE_ERR_UNSUPPORTED).
+                          e_gate, e_up and e_down must be 4-byte aligned */
   MOE_DTYPE_MXFP4_A8 = 3 /* MXFP4 expert weights with MXFP8 activations: the layer quantises x (and
                             the SwiGLU output h) per token and 32 channels to E4M3 with one E8M0
                             scale each (the smallest scale 2^E with amax <= 448 * 2^E), and both
-                            GEMMs run on the scaled f8f6f4 MFMA.  Same limits as MOE_DTYPE_MXFP4 */
+                            GEMMs run on the scaled f8f6f4 MFMA.  No shared expert; e_* 4-byte
+                            aligned; MOE_CONFIG_MFMA is supported (256 x 256 LDS-staged tiles) */
 };
 
 /* Tile configuration for the expert GEMMs.  MOE_CONFIG_AUTO lets the device pick per expert and per
@@ -86,13 +88,15 @@ enum moe_dtype {
  * the Skew", Abstract: the live distribution matched to offline-tuned configurations).  The others
  * force one family for every expert, or (MOE_CONFIG_POLICY0 + i, bf16 only) force policy i; tests
  * use them to cover each.  Block-scaled fp8 weights in automatic mode put experts of more than 128
- * rows on the MFMA tiles when a GEMM's MFMA tiles fill at least one round of compute units, the
- * others on the streaming tiles (no policy table); mxfp4 weights always stream. */
+ * rows (mxfp4 weights with mxfp8 activations: more than 64) on the MFMA tiles when a GEMM's MFMA
+ * tiles fill at least one round of compute units, the others on the streaming tiles (no policy
+ * table); mxfp4 weights with bf16 activations always stream. */
 enum moe_config {
   MOE_CONFIG_AUTO = -1,
   MOE_CONFIG_STREAM = 0, /* weight-streaming tiles: up to 64 of an expert's rows per pass */
   MOE_CONFIG_MFMA = 1,   /* LDS-tiled MFMA tiles: bf16 64, 128 or 256 rows (from the rows a tile
-                            holds) x 256 weight rows; fp8 256 x 256 (mxfp4: MOE_ERR_UNSUPPORTED) */
+                            holds) x 256 weight rows; fp8 and mxfp4 with mxfp8 activations
+                            256 x 256 (mxfp4 with bf16 activations: MOE_ERR_UNSUPPORTED) */
   MOE_CONFIG_FUSED = 2,  /* moe_layer of one bf16 token without a shared expert, d_model and d_ff
                             <= 8192: the whole layer in one launch ("Weave", Abstract:
                             an MoE layer as one persistent megakernel; GC-MoE, summary: a decode

@@ -70,7 +70,9 @@ int check_problem(const moe_problem* p) {
   if (p->wdtype != MOE_DTYPE_BF16 && p->wdtype != MOE_DTYPE_FP8_E4M3 &&
       p->wdtype != MOE_DTYPE_MXFP4 && p->wdtype != MOE_DTYPE_MXFP4_A8)
     return MOE_ERR_UNSUPPORTED;
-  if (is_mxfp4(p) && (p->has_shared || p->config == MOE_CONFIG_MFMA)) return MOE_ERR_UNSUPPORTED;
+  if (is_mxfp4(p) && p->has_shared) return MOE_ERR_UNSUPPORTED;
+  // (MFMA tiles exist for mxfp4 weights with mxfp8 activations only)
+  if (p->wdtype == MOE_DTYPE_MXFP4 && p->config == MOE_CONFIG_MFMA) return MOE_ERR_UNSUPPORTED;
   if (p->has_shared != 0 && p->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (p->has_shared && (p->d_ff_shared <= 0 || p->d_ff_shared % 128)) return MOE_ERR_UNSUPPORTED;
   const bool policy = p->config >= kConfigPolicy0 && p->config < kConfigPolicy0 + kNumPolicies;
@@ -105,7 +107,10 @@ int check_weights(const moe_problem* p, const moe_weights* w, bool with_shared) 
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_INVALID_ARG;
   }
   if (is_mxfp4(p)) {
-    if (!w->e_gate || !w->e_up || !w->e_down) return MOE_ERR_INVALID_ARG;
+    // (the tiles stage the scale rows with 4-byte loads)
+    const void* e[] = {w->e_gate, w->e_up, w->e_down};
+    for (const void* q : e)
+      if (!q || reinterpret_cast<uintptr_t>(q) % 4) return MOE_ERR_INVALID_ARG;
   }
   if (with_shared && p->has_shared) {
     const void* sh[] = {w->sh_gate, w->sh_up, w->sh_down};
@@ -203,7 +208,11 @@ hipError_t launch_gemms(const SelectOut& o, const moe_problem* p, int gemm, int6
                                  s);
   if (p->wdtype == MOE_DTYPE_MXFP4_A8)
     return moe::launch_gemms_mx(o, gemm, cus, max_rows,
-                                gemm == kGemmGateUp ? p->d_model : p->d_ff, s);
+                                gemm == kGemmGateUp ? p->d_model : p->d_ff,
+                                p->config != MOE_CONFIG_MFMA,
+                                p->config == MOE_CONFIG_MFMA ||
+                                    (p->config == MOE_CONFIG_AUTO && max_rows > kMxMfmaRows),
+                                s);
   const int max_k_w4 = gemm == kGemmGateUp ? p->d_model : p->d_ff;
   if (p->wdtype == MOE_DTYPE_MXFP4)  // streaming tiles only
     return moe::launch_gemms_bf16(o, gemm, cus, max_rows, max_k_w4, true, false, false, s, true);

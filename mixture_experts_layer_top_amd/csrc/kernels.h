@@ -37,6 +37,8 @@ constexpr int kSegCap = 1040;       // segment slots per (gemm, family); >= 2 * 
 // fp8 experts of more than kFp8MfmaRows rows take the LDS-staged MFMA tiles in automatic mode (when
 // the GEMM's MFMA tiles fill at least one round of CUs), the others the streaming tiles.
 constexpr int kFp8MfmaRows = 128;
+// The same for mxfp4 experts with mxfp8 activations (whose streaming passes hold 32 rows).
+constexpr int kMxMfmaRows = 64;
 // fp8 weight-streaming tiles: rows per pass (more rows take more passes, which re-read
 // the weights from L2; with 32 the down kernel fits three wavefronts per SIMD, while the gate/up
 // kernel, which holds two K blocks of gate and up weights in flight, needs 256 VGPRs and runs one
@@ -170,7 +172,8 @@ void launch_mfma_fp8(const Seg* segs, int32_t* meta, int gemm, int num_cus, hipS
 // MXFP4 weights with MXFP8 activations (streaming tiles on the scaled f8f6f4 MFMA); max_rows
 // bounds any expert's rows, K is the GEMM's (d for gate/up, f for down).
 hipError_t launch_gemms_mx(const SelectOut& o, int gemm, int num_cus, int64_t max_rows, int K,
-                           hipStream_t s);
+                           bool stream, bool mfma, hipStream_t s);
+void launch_mfma_mx(const Seg* segs, int32_t* meta, int gemm, int num_cus, hipStream_t s);
 // x [T][d] bf16 -> MXFP8: xq [T][d] e4m3, xe [T][d/32] E8M0 (smallest scale with no saturation).
 hipError_t launch_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t* xe,
                                hipStream_t s);

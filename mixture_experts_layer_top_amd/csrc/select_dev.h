@@ -13,15 +13,17 @@ constexpr int kSelThreads = 1024;  // one thread per expert (E + 1 <= kSelThread
 static_assert(kSegCap >= 2 * (kSelThreads / 2 + 1), "two segments per expert (E <= 512)");
 
 // config: -1 or a forced policy (>= kConfigPolicy0): the policy's thresholds; 0 / 1: that family.
-// mxfp4 experts stream; fp8 experts in automatic mode take the MFMA tiles above kFp8MfmaRows rows
-// (subject to the one-round check in select_block).
-__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8, int w4,
+// mxfp4 experts with bf16 activations stream; fp8 experts, and mxfp4 experts with mxfp8
+// activations, take the MFMA tiles in automatic mode above kFp8MfmaRows / kMxMfmaRows rows (subject
+// to the one-round check in select_block).
+__device__ __forceinline__ int pick_family(int c, int g, int config, int fp8, int w4, int mx8,
                                            const SelectPolicy& P) {
   if (c <= 0) return -1;
-  if (w4) return kFamStream;
+  if (w4 && !mx8) return kFamStream;
   if (config == 0) return kFamStream;
   if (config == 1) return kFamMfma;
   if (fp8) return c > kFp8MfmaRows ? kFamMfma : kFamStream;
+  if (mx8) return c > kMxMfmaRows ? kFamMfma : kFamStream;
   return c <= (g == kGemmGateUp ? P.thr_gu : P.thr_dn) ? kFamStream : kFamMfma;
 }
 
@@ -92,7 +94,8 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   }
   int fm[2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8, a.w4, P) : -1;
+  for (int g = 0; g < 2; ++g)
+    fm[g] = e < nexp ? pick_family(c, g, a.config, a.fp8, a.w4, a.mx8, P) : -1;
   // The down GEMM's light experts (<= kStreamRowsDown rows) take the streaming tiles only while its
   // heavier experts' MFMA tiles fill less than one round of CUs; with a round or more they join the
   // MFMA list, where their short tiles fill the rounds' gaps instead of running as a second launch
@@ -108,10 +111,11 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   // same (block-wide) totals give the list's ordering mode: one to kSplitMaxRounds rounds ->
   // longest first (below one round every tile starts at once and order does not matter); else XCD
   // chunks when K >= kLongK and some expert spans several m-tiles.
-  // fp8 (automatic mode): a GEMM whose MFMA tiles would fill less than one round of CUs runs wholly
-  // on the streaming tiles (one CU per weight tile draws too little of the chip's bandwidth).
+  // fp8 and mxfp8-activation experts (automatic mode): a GEMM whose MFMA tiles would fill less than
+  // one round of CUs runs wholly on the streaming tiles (one CU per weight tile draws too little of
+  // the chip's bandwidth).
   bool lpt[2] = {false, false}, chunks[2] = {false, false};
-  if (a.fp8 && a.config < 0) {
+  if ((a.fp8 || a.mx8) && a.config < 0) {
     const int nt_dn = (a.d + kMfmaBNDown - 1) / kMfmaBNDown;
     int w[2], wex[2], wtot[2];
 #pragma unroll
@@ -314,7 +318,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     const int K = g == kGemmGateUp ? a.d : a.f;
     const bool uniform_k = g == kGemmGateUp || !a.has_shared || a.f_sh == a.f;
     const int C = min(a.num_cus, kSplitMaxPieces);
-    const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8;
+    const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8 && !a.w4;
     // (lpt[] is the same for every thread)
     m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : chunks[g] ? kOrderChunks
                                                                                       : kOrderMix;

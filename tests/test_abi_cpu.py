@@ -160,6 +160,20 @@ def test_narrow_weight_formats_need_the_tiled_layout():
                            None) == moe.MOE_ERR_WORKSPACE
         assert L.moe_grouped_ffn(ctypes.byref(p), 4096, 4352, 8192, 12288, ctypes.byref(row),
                                  16384, 32768, 16, None) == moe.MOE_ERR_INVALID_ARG
+    # the E8M0 scale arrays are staged with 4-byte loads: each must be 4-byte aligned
+    for name in ("e_gate", "e_up", "e_down"):
+        for wd in (moe.DTYPE_MXFP4, moe.DTYPE_MXFP4_A8):
+            p = moe.problem(8, 256, 512, 8, 2, wdtype=wd)
+            off = moe.Weights(**dict(ptrs, **{name: ptrs[name] + 2}), layout=moe.LAYOUT_TILED)
+            assert L.moe_layer(ctypes.byref(p), 4096, 8192, ctypes.byref(off), 16384, None, 32768,
+                               16, None) == moe.MOE_ERR_INVALID_ARG
+    # MFMA tiles exist for mxfp4 weights with mxfp8 activations, not with bf16 activations
+    tiled = moe.Weights(**ptrs, layout=moe.LAYOUT_TILED)
+    for wd, want in ((moe.DTYPE_MXFP4, moe.MOE_ERR_UNSUPPORTED),
+                     (moe.DTYPE_MXFP4_A8, moe.MOE_ERR_WORKSPACE)):
+        p = moe.problem(8, 256, 512, 8, 2, wdtype=wd, config=moe.CONFIG_MFMA)
+        assert L.moe_layer(ctypes.byref(p), 4096, 8192, ctypes.byref(tiled), 16384, None, 32768,
+                           16, None) == want
     bf = moe.problem(8, 256, 512, 8, 2)
     assert L.moe_layer(ctypes.byref(bf), 4096, 8192,
                        ctypes.byref(moe.Weights(w_gate=256, w_up=512, w_down=768,

@@ -579,10 +579,24 @@ def test_quant_act_mx_random(moe, scale):
 MXA8_SMALL = [replace(p, name=p.name + "_a8", act_mx8=True) for p in MXFP4_SMALL]
 
 
-@pytest.mark.parametrize("config", [-1, 0])
+# config 1: the LDS-staged MFMA tiles (256 x 256, one 128-value chunk per stage, both operands'
+# E8M0 scales applied by the scaled MFMA) on every shape: several m-tiles with ragged tails
+# (T = 300, k = 2, E = 6), an odd number of K chunks and a down tile half past d (d = 384), long K
+# (d = 4096), one token (a tile of one row).  Automatic selection puts experts of more than 64 rows
+# on them when a GEMM's MFMA tiles fill a round of CUs: the prefill-shaped case's gate/up GEMM
+# (512 tiles) does, its down GEMM (128) streams.
+@pytest.mark.parametrize("config", [-1, 0, 1])
 @pytest.mark.parametrize("p", MXA8_SMALL, ids=lambda p: p.name)
 def test_mxfp4_a8_layer_matches_oracle(moe, p, config):
     _check_layer(moe, Inputs(p), config=config, tol=FP8_TOL, runs=2)
+
+
+MXA8_PREFILL = I.Problem("mx_a8_prefill", 125, T=4096, d=1024, f=2048, E=8, k=2,
+                         wdtype=I.WDT_MXFP4, act_mx8=True)
+
+
+def test_mxfp4_a8_prefill_auto_matches_oracle(moe):
+    _check_layer(moe, Inputs(MXA8_PREFILL), config=-1, tol=FP8_TOL, runs=2)
 
 
 def test_mxfp4_a8_grouped_ffn_matches_oracle(moe):
@@ -599,7 +613,15 @@ def test_mxfp4_a8_grouped_ffn_matches_oracle(moe):
     assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
 
 
-def test_mxfp4_a8_rejects_mfma_config(moe):
-    inp = Inputs(MXA8_SMALL[0])
-    with pytest.raises(moe.MoEError, match="UNSUPPORTED"):
-        moe.Layer(inp.expert_weights(), inp.p.T, inp.p.E, inp.p.k, config=1)(inp.d_logits, inp.d_x)
+def test_mxfp4_a8_mfma_grouped_ffn_matches_oracle(moe):
+    p = MXA8_SMALL[1]
+    inp = Inputs(p)
+    rids, _ = O.route(inp.logits, p.k)
+    counts, offsets = O.histogram(rids, p.E)
+    perm_src, _ = O.permute(rids, p.E)
+    x_perm = torch.from_numpy(np.ascontiguousarray(inp.x[perm_src // p.k]).view(np.int16)).cuda()
+    y = moe.grouped_ffn(x_perm, None, torch.from_numpy(counts.astype(np.int32)).cuda(),
+                        torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        inp.expert_weights(), p.T, p.k, config=1)
+    ref = O.moe_layer(inp.logits, inp.x, p.k, inp.get, act="mxfp8")["y_perm"]
+    assert rel_err(bits_to_f64(y), ref) <= FP8_TOL
