@@ -393,16 +393,17 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // LDS-tiled MFMA family
 //
 // A tile is 256 weight rows (gate/up: 128 gate + 128 up rows -> 128 h columns; down: 256 y columns)
-// by a tile height of token rows chosen from the rows the tile holds: 256 (full), 128 or 64.  The
+// by a tile height of token rows chosen from the rows the tile holds: 256 (full), 128, 64 or 32.  The
 // last m-tile of an expert and every expert with at most 128 rows take the shortest height that
 // holds their rows, so a 40-row expert runs a quarter of the MFMAs of a full tile and its weights
 // stream at the rate of the loads instead of the MFMAs.
 //  * full: 4 wavefronts as 2 (tokens) x 2 (weights), each 128 x 128 with MFMA 32x32x16: 16
 //    accumulator blocks, 4 A and 4 B fragments per k-substep, every fragment reused 4 times; two
 //    LDS stages of 64 KB.
-//  * short (128 or 64 rows): the 4 wavefronts split the weight rows (gate/up: 32 gate + 32 up rows
-//    each, down: 64 rows each) and each covers every token row; three LDS stages of 48 or 40 KB,
-//    since these tiles wait on the weight stream rather than on the MFMAs.
+//  * short (128, 64 or 32 rows): the 4 wavefronts split the weight rows (gate/up: 32 gate + 32 up
+//    rows each, down: 64 rows each) and each covers every token row; three LDS stages of 48 or
+//    40 KB, four of 36 KB for 32 rows, since these tiles wait on the weight stream rather than on
+//    the MFMAs.
 // Within a tile every MFMA runs whatever its rows (skipping empty 32-row token blocks inside a full
 // tile was measured: ~3% on many-expert prefill, -2% on 8-expert prefill and ~40% more gate/up L2
 // miss traffic).
@@ -523,10 +524,10 @@ __device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], vo
 // done and every load it issued has landed; barrier (stage S^1 complete, stage S free); loads for
 // step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
 //
-// Short tiles: three stages at a run-time stage index, so that two steps of loads stay in flight
-// while one stage is read.  Step kt reads stage kt % 3; before the
-// barrier it waits until the loads of step kt+1 have landed (those of kt+2 may still fly), then
-// loads step kt+3 into the stage it just finished.
+// Short tiles: NS stages (three; four for 32-row tiles) at a run-time stage index, so that NS - 1
+// steps of loads stay in flight while one stage is read.  Step kt reads stage kt % NS; before the
+// barrier it waits until the loads of step kt+1 have landed (later ones may still fly), then loads
+// step kt+NS into the stage it just finished.
 // ------------------------------------------------------------------------------------------------
 constexpr int BK64 = 64;
 constexpr int ROWB64 = 128;
@@ -534,6 +535,14 @@ constexpr int STAGE64 = LROWS * ROWB64;            // 64 KB
 constexpr int DMA64 = STAGE64 / (256 * 16);        // 16 loads per thread per stage
 constexpr int kShortStages = 3;
 constexpr int kRingBytes = kShortStages * (128 + BNW) * ROWB64;  // 144 KB (>= 2 full stages)
+// LDS stages of a short tile of TB token blocks: as many as the ring holds (32-row tiles: four
+// 36 KB stages, three K-steps of loads in flight; 64- and 128-row tiles: three).
+template <int TB> constexpr int kStagesFor = kRingBytes / ((TB * 32 + BNW) * ROWB64) >= 4 ? 4 : 3;
+static_assert(kStagesFor<1> * (32 + BNW) * ROWB64 <= kRingBytes, "32-row stages fit the ring");
+// Tile height for a tile holding `rows` token rows (the shortest that fits).
+__device__ __forceinline__ int tile_height(int rows) {
+  return rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : kMfmaBM;
+}
 static_assert(kRingBytes >= 2 * STAGE64, "ring holds two full-tile stages");
 __shared__ __attribute__((aligned(1024))) uint8_t g_ring[kRingBytes];
 template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return g_ring + S * STAGE64; }
@@ -565,7 +574,7 @@ struct MfmaTile {
   const char* wbase1;
   uint32_t off[DMA64];
   int wvu;
-  int bm;  // tile height: 256, 128 or 64 token rows
+  int bm;  // tile height: 256, 128, 64 or 32 token rows
   int arow0, brow0;  // LDS byte offsets of the wavefront's first weight and token rows
   f32x16 acc[4][4];
 
@@ -578,7 +587,7 @@ struct MfmaTile {
   __device__ __forceinline__ void setup(const Seg& sg, int m0, int rows, int n0, int kt0) {
     const int lane = tid_here() & 63;  // (lane constants stay in the claim, not held across tiles)
     wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    bm = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
+    bm = tile_height(rows);
     const int nts = bm >> 5;
     const uint32_t rowbytes = (uint32_t)sg.K * 2;
     abase = static_cast<const char*>(sg.a);
@@ -768,32 +777,35 @@ struct MfmaTile {
     __builtin_amdgcn_sched_barrier(0);
     read_frags_short<TB>(st, kk, nxt);
     mfmas_short<TB>(cur);
+    constexpr int kPairs = 2 * TB < 2 + TB ? 2 * TB : 2 + TB;
 #pragma unroll
-    for (int i = 0; i < 2 + TB; ++i) {
+    for (int i = 0; i < kPairs; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if constexpr (TB > 2) __builtin_amdgcn_sched_group_barrier(0x008, TB - 2, 0);
+    if constexpr (2 * TB > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, 2 * TB - kPairs, 0);
+    if constexpr (2 + TB > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, 2 + TB - kPairs, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
   template <int TB>
   __device__ __forceinline__ void prologue_short(int nk) {
 #pragma unroll
-    for (int s = 0; s < kShortStages; ++s) issue_short<TB>(s, min(s, nk - 1));
+    for (int s = 0; s < kStagesFor<TB>; ++s) issue_short<TB>(s, min(s, nk - 1));
   }
 
   template <int TB>
   __device__ __forceinline__ void run_short(int nk) {
     constexpr int kStage = (TB * 32 + BNW) * ROWB64;
     constexpr int D = TB + 8;  // loads per thread per stage
+    constexpr int NS = kStagesFor<TB>;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    MOE_WAITCNT((kShortStages - 1) * D, 15);  // stage 0 (the oldest loads) has landed
+    MOE_WAITCNT((NS - 1) * D, 15);  // stage 0 (the oldest loads) has landed
     __builtin_amdgcn_s_barrier();
     bf16x8 f0[2 + TB], f1[2 + TB];
     read_frags_short<TB>(g_ring, 0, f0);
@@ -804,12 +816,12 @@ struct MfmaTile {
       sub_short<TB>(st, 2, f1, f0);
       sub_short<TB>(st, 3, f0, f1);
       // this wavefront's reads of stage s are done and its loads for step kt+1 have landed
-      MOE_WAITCNT((kShortStages - 2) * D, 0);
+      MOE_WAITCNT((NS - 2) * D, 0);
       __builtin_amdgcn_s_barrier();
-      // the loads for step kt+3 into stage s, interleaved with the MFMAs of substep 3 and the
+      // the loads for step kt+NS into stage s, interleaved with the MFMAs of substep 3 and the
       // reads of substep 0 of the next stage
-      const uint32_t ko = (uint32_t)min(kt + kShortStages, nk - 1) * ROWB64;
-      const int sn = s == kShortStages - 1 ? 0 : s + 1;
+      const uint32_t ko = (uint32_t)min(kt + NS, nk - 1) * ROWB64;
+      const int sn = s == NS - 1 ? 0 : s + 1;
       const uint8_t* rd = g_ring + sn * kStage;
       const int lo = frag_lane_off(0), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
@@ -829,7 +841,8 @@ struct MfmaTile {
   __device__ __forceinline__ void prologue(int nk) {
     if (bm == BM) prologue_full();
     else if (bm == 128) prologue_short<4>(nk);
-    else prologue_short<2>(nk);
+    else if (bm == 64) prologue_short<2>(nk);
+    else prologue_short<1>(nk);
   }
 };
 
@@ -935,12 +948,18 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split
         MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<2, 4>(tile.acc, part(cur), cur.piece);
-    } else {
+    } else if (cur.h == 64) {
       tile.template run_short<2>(cur.nk);
       if (!kSplit || cur.piece < 0)
         MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<2, 2>(tile.acc, part(cur), cur.piece);
+    } else {
+      tile.template run_short<1>(cur.nk);
+      if (!kSplit || cur.piece < 0)
+        MfmaTileStoreShort<GU, 1>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+      else
+        split_store<2, 1>(tile.acc, part(cur), cur.piece);
     }
     if (!claim(cur)) break;
   }
@@ -1000,7 +1019,7 @@ __global__ __launch_bounds__(256, 1) void mfma_split_epilogue(const Seg* __restr
   const int mt = local % sg.mtiles, nt = local / sg.mtiles;
   const int m0 = mt * BM, rows = min(BM, sg.rows - m0);
   const int n0 = nt * (GU ? kMfmaBNGateUp : kMfmaBNDown);
-  const int h = rows <= 64 ? 64 : rows <= 128 ? 128 : BM;
+  const int h = tile_height(rows);
   const int NA = h == BM ? 4 : 2, NB = h == BM ? 4 : h / 32;
   const float* part = split_part + (size_t)u * S * kSplitSlotFloats;
   const uint32_t lane_off = threadIdx.x * 16;
@@ -1028,7 +1047,8 @@ __global__ __launch_bounds__(256, 1) void mfma_split_epilogue(const Seg* __restr
     }
   if (h == BM) MfmaTileStore<GU>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
   else if (h == 128) MfmaTileStoreShort<GU, 4>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
-  else MfmaTileStoreShort<GU, 2>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
+  else if (h == 64) MfmaTileStoreShort<GU, 2>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
+  else MfmaTileStoreShort<GU, 1>(acc, sg.out, sg.N, sg.row0, m0, rows, n0);
 }
 
 // ------------------------------------------------------------------------------------------------

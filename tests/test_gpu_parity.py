@@ -300,12 +300,14 @@ def test_mfma_mixed_heights_persistent(moe):
 
 
 # Last-round split in K: tiles past the last whole round of CUs run as 2 or 4 K-pieces whose fp32
-# partial sums the last piece to finish adds in piece order.  1100 rows = 4 full m-tiles + a 128-row
-# short one.  f = 1024: 40 gate/up and 10 down tiles, all split 4 ways; f = 8192: 320 gate/up tiles,
-# one whole round + 64 tiles split 4 ways (256 pieces).  Two runs must agree bit for bit.
-@pytest.mark.parametrize("f", [1024, 8192])
-def test_mfma_last_round_split(moe, f):
-    p = _small(f"split_f{f}", T=1100, d=512, f=f, E=1, k=1, cfg_index=141 + (f > 1024))
+# partial sums an epilogue kernel adds in piece order.  1100 rows = 4 full m-tiles + a 128-row
+# short one; 1050 rows = 4 full m-tiles + a 32-row one.  f = 1024: 40 gate/up and 10 down tiles,
+# all split 4 ways; f = 8192: 320 gate/up tiles, one whole round + 64 tiles split 4 ways (256
+# pieces).  Runs must agree bit for bit.
+@pytest.mark.parametrize("T,f", [(1100, 1024), (1100, 8192), (1050, 1024), (1050, 8192)])
+def test_mfma_last_round_split(moe, T, f):
+    cfg = 141 + (f > 1024) if T == 1100 else 143 + (f > 1024)
+    p = _small(f"split_T{T}_f{f}", T=T, d=512, f=f, E=1, k=1, cfg_index=cfg)
     for config in (1, -1):
         _check_layer(moe, Inputs(p), config=config, runs=3)
 
