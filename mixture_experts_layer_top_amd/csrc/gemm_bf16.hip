@@ -521,8 +521,9 @@ __device__ __forceinline__ void MfmaTileStoreShort(const f32x16 (&acc)[4][4], vo
 // Full tiles: two stages of 64 KB.  Waits are explicit (vmcnt) around a plain barrier so prefetches
 // stay in flight.  Step kt
 // on stage S: substeps 0..2 run while substeps 1..3 are read; wait until this wavefront's reads are
-// done and every load it issued has landed; barrier (stage S^1 complete, stage S free); loads for
-// step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read.
+// done and every load it issued has landed; barrier (stage S^1 complete, stage S free); half the
+// loads for step kt+2 into stage S while substep 3 runs and substep 0 of stage S^1 is read, the
+// other half during substep 1 of step kt+1.
 //
 // Short tiles: NS stages (three; four for 32-row tiles) at a run-time stage index, so that NS - 1
 // steps of loads stay in flight while one stage is read.  Step kt reads stage kt % NS; before the
@@ -686,22 +687,51 @@ struct MfmaTile {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // The same with loads J0 .. J0 + N - 1 of the K-step at offset ko (into stage T), one per MFMA:
+  // gate/up places them on the first N MFMAs, beside the fragment reads, down on the last N, the
+  // faster placement for each (the scheduler cannot see the asm loads, so the interleave is fixed
+  // by hand).
+  template <int S, int T, int J0, int N>
+  __device__ __forceinline__ void sub_dma(int kk, const bf16x8 (&cur)[8], bf16x8 (&nxt)[8], uint32_t ko) {
+    const uint8_t* st = stage64_ptr<S>();
+    const int lo = frag_lane_off(kk), va = arow0 + lo, vb = brow0 + lo;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int L0 = GU ? 0 : 16 - N;  // first MFMA with a load
+      if (i >= L0 && i < L0 + N) issue_one<T>(J0 + i - L0, ko);
+      if (i < 8) nxt[i] = frag_full(st, va, vb, i);
+      acc[i >> 2][i & 3] = mfma32(cur[i >> 2], cur[4 + (i & 3)], acc[i >> 2][i & 3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // The 16 loads of a K-step go out in two halves: kDma0 behind the MFMAs of the previous step's
+  // substep 3 (right after its barrier), the rest behind substep 1 of the step before the one
+  // that reads them.  Issued all at once after the barrier, the four wavefronts' 64 loads queued
+  // behind each other and held up the MFMAs interleaved with them (Mixtral-shaped layer 2.68 ->
+  // 2.58 ms); issuing any of them later than substep 1 left too little time for them to land.
+  // (At a tile's first step the second half repeats loads of the prologue.)
+  static constexpr int kDma0 = 8;
+
   template <int S>
   __device__ __forceinline__ void step(int kt, int nk, bf16x8 (&f0)[8], bf16x8 (&f1)[8]) {
-    sub<S>(1, f0, f1);
+    // the rest of step kt+1's loads (into stage S^1)
+    const uint32_t k1 = (uint32_t)min(kt + 1, nk - 1) * ROWB64;
+    sub_dma<S, S ^ 1, kDma0, DMA64 - kDma0>(1, f0, f1, k1);
     sub<S>(2, f1, f0);
     sub<S>(3, f0, f1);
     MOE_WAITCNT(0, 0);
     __builtin_amdgcn_s_barrier();
-    // one load for step kt+2 per MFMA of substep 3 (the scheduler cannot see the asm loads, so the
-    // interleave is fixed by hand), with substep 0 of stage S^1 read behind the first eight
+    // the first kDma0 loads for step kt+2, with substep 0 of stage S^1 read behind the first eight
+    // MFMAs of substep 3
     const uint32_t ko = (uint32_t)min(kt + 2, nk - 1) * ROWB64;
     const uint8_t* rd = stage64_ptr<S ^ 1>();
     const int lo = frag_lane_off(0), va = arow0 + lo, vb = brow0 + lo;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      issue_one<S>(i, ko);
+      if (i < kDma0) issue_one<S>(i, ko);
       acc[i >> 2][i & 3] = mfma32(f1[i >> 2], f1[4 + (i & 3)], acc[i >> 2][i & 3]);
       if (i < 8) f0[i] = frag_full(rd, va, vb, i);
     }
