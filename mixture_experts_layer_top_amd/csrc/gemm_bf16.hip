@@ -421,6 +421,8 @@ constexpr int BM = kMfmaBM;
 constexpr int BNW = 256;                  // weight rows per tile
 constexpr int LROWS = BM + BNW;           // LDS rows per stage of a full tile
 
+// Direct stores from the accumulators (the split-K epilogue kernel, which has no staging ring; the
+// persistent MFMA kernel stages its tiles through LDS, MfmaTileStoreLds).
 template <bool GU>
 __device__ __forceinline__ void MfmaTileStore(const f32x16 (&acc)[4][4], void* out, int N, int row0,
                                               int m0, int rows, int n0) {
@@ -547,6 +549,90 @@ __device__ __forceinline__ int tile_height(int rows) {
 static_assert(kRingBytes >= 2 * STAGE64, "ring holds two full-tile stages");
 __shared__ __attribute__((aligned(1024))) uint8_t g_ring[kRingBytes];
 template <int S> __device__ __forceinline__ uint8_t* stage64_ptr() { return g_ring + S * STAGE64; }
+
+// Epilogue through LDS.  Stored straight from the accumulators, a lane writes 8 bytes (4 columns)
+// of each of 32 token rows per instruction: a full tile took 64 such stores per lane, and since
+// stores and loads share one counter, the next tile's first wait waited for them all.  Instead the
+// tile (bf16, after SwiGLU for gate/up) goes into the idle ring as [token row][column] with 16 bytes
+// of padding per row (conflict-free 8-byte writes), and then every thread stores 16-byte chunks of
+// whole rows: a wavefront writes two or four contiguous row segments of 256 or 512 bytes.  TB: token
+// blocks of a short tile (8: a full tile).  The ring is idle: the K loop ended with a wait and a
+// barrier, and the next tile's loads go out after the claim's barrier.
+
+template <bool GU, int TB>
+__device__ __forceinline__ void MfmaTileStoreLds(const f32x16 (&acc)[4][4], void* out, int N, int row0,
+                                                 int m0, int rows, int n0) {
+  constexpr bool kFull = TB == 8;
+  constexpr int W = GU ? 128 : 256;  // the tile's output columns
+  constexpr int RS = W * 2 + 16;     // LDS row stride in bytes
+  static_assert(256 * RS <= kRingBytes, "an output tile fits the ring");
+  const uint32_t tid = tid_here();
+  const int lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  auto put = [&](int t, int col, float v0, float v1, float v2, float v3) {
+    uint2 pk;
+    pk.x = pack_bf16x2(v0, v1);
+    pk.y = pack_bf16x2(v2, v3);
+    *reinterpret_cast<uint2*>(g_ring + t * RS + col * 2) = pk;
+  };
+  // lane holds C[8*(r/4) + 4*khalf + r%4][l32] of each 32x32 block (rows = weights)
+  if (kFull) {
+    const int wm = wv & 1, wn = wv >> 1;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int t = wm * 128 + b * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (GU) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            float v[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[a][b][q * 4 + s], acc[a + 2][b][q * 4 + s]);
+            put(t, wn * 64 + a * 32 + 8 * q + 4 * khalf, v[0], v[1], v[2], v[3]);
+          }
+        } else {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            put(t, wn * 128 + a * 32 + 8 * q + 4 * khalf, acc[a][b][q * 4], acc[a][b][q * 4 + 1],
+                acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
+        }
+      }
+    }
+  } else {
+    const int wn = wv;
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const int t = b * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (GU) {
+          float v[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) v[s] = swiglu(acc[0][b][q * 4 + s], acc[1][b][q * 4 + s]);
+          put(t, wn * 32 + 8 * q + 4 * khalf, v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+            put(t, wn * 64 + a * 32 + 8 * q + 4 * khalf, acc[a][b][q * 4], acc[a][b][q * 4 + 1],
+                acc[a][b][q * 4 + 2], acc[a][b][q * 4 + 3]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = W / 8;      // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;  // rows per pass of the workgroup
+  constexpr int H = kFull ? 256 : TB * 32;
+  const int c = tid % CPR;
+  const int col = n0 + c * 8;
+  const int nr = rows < H ? rows : H;
+  if (col < N) {  // (down: the last tile of a row may be half full)
+    for (int t = tid / CPR; t < nr; t += RPP)
+      gstore16(out, ((size_t)(row0 + m0 + t) * N + col) * 2,
+               *reinterpret_cast<const uint4*>(g_ring + t * RS + c * 16));
+  }
+}
 
 __device__ __forceinline__ int lds_off64(int r, int c) { return r * ROWB64 + ((c ^ ((r >> 1) & 7)) << 4); }
 
@@ -969,25 +1055,25 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split
     if (cur.h == BM) {
       tile.run_full(cur.nk);
       if (!kSplit || cur.piece < 0)
-        MfmaTileStore<GU>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+        MfmaTileStoreLds<GU, 8>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<4, 4>(tile.acc, part(cur), cur.piece);
     } else if (cur.h == 128) {
       tile.template run_short<4>(cur.nk);
       if (!kSplit || cur.piece < 0)
-        MfmaTileStoreShort<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+        MfmaTileStoreLds<GU, 4>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<2, 4>(tile.acc, part(cur), cur.piece);
     } else if (cur.h == 64) {
       tile.template run_short<2>(cur.nk);
       if (!kSplit || cur.piece < 0)
-        MfmaTileStoreShort<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+        MfmaTileStoreLds<GU, 2>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<2, 2>(tile.acc, part(cur), cur.piece);
     } else {
       tile.template run_short<1>(cur.nk);
       if (!kSplit || cur.piece < 0)
-        MfmaTileStoreShort<GU, 1>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
+        MfmaTileStoreLds<GU, 1>(tile.acc, cur.out, cur.N, cur.row0, cur.m0, cur.rows, cur.n0);
       else
         split_store<2, 1>(tile.acc, part(cur), cur.piece);
     }
