@@ -409,13 +409,13 @@ __global__ __launch_bounds__(256) void gemm_stream_bf16(const Seg* __restrict__ 
 // miss traffic).
 //
 // Scheduling: one persistent workgroup per CU.  Tiles are handed out in one of three orders chosen
-// by the selection kernel (select_dev.h): light tiles spread between heavy ones; XCD chunks of
-// short tiles spread between chunks of full-height ones (long K); or, for GEMMs of few rounds,
-// longest first.  Within a segment the m-tiles of one weight tile are next
-// to each other; consecutive runs of (CUs per XCD) tiles go to
-// one XCD, so tiles that share weight and activation tiles run side by side on the same L2.  Each
-// XCD has its own queue; a workgroup whose queue is empty takes work from the other XCDs' queues.
-// Tiles past the last whole round of CUs may be split in K (see kernels.h).
+// by the selection kernel (select_dev.h): light tiles spread between heavy ones; two classes with a
+// queue each on every XCD, part of each XCD's CUs on full-height tiles and the rest on short ones
+// (long K); or, for GEMMs of few rounds, longest first.  Within a segment the m-tiles of one weight
+// tile are next to each other; consecutive runs of tiles go to one XCD, so tiles that share weight
+// and activation tiles run side by side on the same L2.  A workgroup whose XCD's queues are empty
+// takes work from the other XCDs' queues.  Tiles past the last whole round of CUs may be split in
+// K (see kernels.h).
 // ------------------------------------------------------------------------------------------------
 constexpr int BM = kMfmaBM;
 constexpr int BNW = 256;                  // weight rows per tile
@@ -998,9 +998,11 @@ struct MfmaCur { int m0, rows, n0, h, nk, N, row0, piece, u; void* out; };
 struct MfmaQueue {
   const Seg* segs;
   int32_t* queues;
+  int32_t* queues1;     // class-1 queues of the two-class order
   const int* seg_base;  // LDS: first tile of each segment
   int nseg, ntiles, ntiles0, sbase, S, nq, chunk;
   int order;  // TileOrder
+  int pref, b0, b1;  // two-class order: this workgroup's first class, the classes' XCD chunks
 };
 
 // The persistent tile loop.  Instantiated with and without the split-K epilogue, so that lists that
@@ -1013,20 +1015,26 @@ __device__ __forceinline__ void mfma_persistent(const MfmaQueue& Q, float* split
     // (the queue's counts go through opaque moves: the reciprocals of its integer divisions are
     // then computed here per claim instead of being hoisted and held across the K loops)
     const int ntiles = opaque_s(Q.ntiles), ntiles0 = opaque_s(Q.ntiles0), chunk = opaque_s(Q.chunk);
-    const int pos = pop_tile_xcd(Q.queues, kSplit ? opaque_s(Q.nq) : ntiles, chunk, slot, q);
-    if (pos < 0) return false;
-    int tp = pos;
     c.piece = -1;
     c.u = 0;
-    if (kSplit && pos >= Q.sbase) {
-      const int S = opaque_s(Q.S);
-      c.u = (pos - Q.sbase) / S;
-      c.piece = pos - Q.sbase - c.u * S;
-      tp = Q.sbase + c.u;
+    int t;
+    if (!kSplit && Q.order == kOrderTwoClass) {  // (lists of that order split nothing)
+      t = pop_tile_two_class(Q.queues, Q.queues1, ntiles0, ntiles - ntiles0, opaque_s(Q.b0),
+                             opaque_s(Q.b1), Q.pref, slot, q);
+      if (t < 0) return false;
+    } else {
+      const int pos = pop_tile_xcd(Q.queues, kSplit ? opaque_s(Q.nq) : ntiles, chunk, slot, q);
+      if (pos < 0) return false;
+      int tp = pos;
+      if (kSplit && pos >= Q.sbase) {
+        const int S = opaque_s(Q.S);
+        c.u = (pos - Q.sbase) / S;
+        c.piece = pos - Q.sbase - c.u * S;
+        tp = Q.sbase + c.u;
+      }
+      // (a split list of the two-class order, which has less than one round, takes the mixed one)
+      t = Q.order == kOrderLongestFirst ? tp : interleave_tile(tp, ntiles0, ntiles);
     }
-    const int t = Q.order == kOrderLongestFirst ? tp
-                  : Q.order == kOrderChunks      ? chunked_interleave(tp, ntiles0, ntiles, chunk)
-                                                 : interleave_tile(tp, ntiles0, ntiles);
     const int si = __builtin_amdgcn_readfirstlane(find_seg_lds(Q.seg_base, Q.nseg, t));
     const Seg& sg = Q.segs[si];
     const int local = t - sg.tile_base;
@@ -1092,10 +1100,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   if (Q.ntiles == 0) return;
   Q.segs = segs;
   Q.queues = meta + kMetaQueue;
+  Q.queues1 = meta + kMetaQueue1;
   Q.seg_base = seg_base;
   Q.nseg = meta[0];
   Q.ntiles0 = meta[kMetaClass0];
   Q.order = meta[kMetaOrder];
+  {
+    // two-class order: the first r0 workgroups of each XCD start on class 0, in proportion to the
+    // classes' estimated CU time; each class's XCD chunk is the number of CUs that start on it
+    const int g = max(1, (int)gridDim.x / kXcds), n0 = Q.ntiles0, n1 = Q.ntiles - Q.ntiles0;
+    const long long w0 = (long long)kTwoClassW0 * n0, w1 = (long long)kTwoClassW1 * n1;
+    int r0 = n1 == 0 ? g : n0 == 0 ? 0 : (int)((g * w0 + (w0 + w1) / 2) / (w0 + w1));
+    if (n0 > 0 && n1 > 0) r0 = min(max(r0, 1), g - 1);
+    Q.pref = (int)(blockIdx.x / kXcds) < r0 ? 0 : 1;
+    Q.b0 = max(r0, 1);
+    Q.b1 = max(g - r0, 1);
+  }
   Q.sbase = meta[kMetaSplitBase];
   Q.S = meta[kMetaSplitS];
   Q.nq = Q.sbase + (Q.ntiles - Q.sbase) * Q.S;
@@ -1109,21 +1129,16 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
 // Epilogue of the tiles split in K: workgroup u adds the S partial-sum slots of split tile u (queue
 // position sbase + u) in piece order -- so the result does not depend on which piece finished
 // first -- and stores the tile as the MFMA kernel would have.  It runs after the GEMM's MFMA kernel
-// on the same stream; with no split tiles every workgroup returns at once.  num_cus: the MFMA
-// kernel's grid (its XCD chunk size enters the chunked tile order).
+// on the same stream; with no split tiles every workgroup returns at once.
 template <bool GU>
 __global__ __launch_bounds__(256, 1) void mfma_split_epilogue(const Seg* __restrict__ segs,
                                                                const int32_t* __restrict__ meta,
-                                                               const float* __restrict__ split_part,
-                                                               int num_cus) {
+                                                               const float* __restrict__ split_part) {
   const int ntiles = meta[1], sbase = meta[kMetaSplitBase], S = meta[kMetaSplitS];
   const int u = blockIdx.x;
   if (S <= 1 || sbase + u >= ntiles) return;
   const int tp = sbase + u, order = meta[kMetaOrder], ntiles0 = meta[kMetaClass0];
-  const int chunk = max(1, num_cus / kXcds);
-  const int t = order == kOrderLongestFirst ? tp
-                : order == kOrderChunks      ? chunked_interleave(tp, ntiles0, ntiles, chunk)
-                                             : interleave_tile(tp, ntiles0, ntiles);
+  const int t = order == kOrderLongestFirst ? tp : interleave_tile(tp, ntiles0, ntiles);
   int lo = 0, hi = meta[0] - 1;  // the last segment whose first tile is <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -1574,11 +1589,11 @@ hipError_t launch_gemms_bf16(const SelectOut& o, int g, int num_cus, int64_t max
   if (g == kGemmGateUp) {
     if (stream) launch_stream_bf16<true>(ss, ms, num_cus, max_rows, max_k, s, w4);
     if (mfma) gemm_mfma_bf16<true><<<num_cus, 256, 0, s>>>(sm, mm, o.split_part);
-    if (split) mfma_split_epilogue<true><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part, num_cus);
+    if (split) mfma_split_epilogue<true><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part);
   } else {
     if (stream) launch_stream_bf16<false>(ss, ms, num_cus, max_rows, max_k, s, w4);
     if (mfma) gemm_mfma_bf16<false><<<num_cus, 256, 0, s>>>(sm, mm, o.split_part);
-    if (split) mfma_split_epilogue<false><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part, num_cus);
+    if (split) mfma_split_epilogue<false><<<kSplitGrid, 256, 0, s>>>(sm, mm, o.split_part);
   }
   return hipGetLastError();
 }

@@ -126,16 +126,21 @@ struct SelectArgs {
 // first), zeroed by the selection kernel before each GEMM, then the number of class-0 tiles (which
 // come first in tile order; see select_dev.h), then (MFMA family) the first queue position whose
 // tile is split in K and the pieces per split tile (positions [0, base) are whole tiles, and each
-// tile of [base, ntiles) takes S consecutive positions), then the ordering mode.
-constexpr int kMetaStride = 16;
+// tile of [base, ntiles) takes S consecutive positions), then the ordering mode, then kXcds more
+// queue counters (the class-1 queues of the two-class order), also zeroed before each GEMM.
+constexpr int kMetaStride = 32;
 constexpr int kMetaQueue = 2;
 constexpr int kMetaClass0 = kMetaQueue + kXcds;
 constexpr int kMetaSplitBase = kMetaClass0 + 1;
 constexpr int kMetaSplitS = kMetaClass0 + 2;
 constexpr int kMetaOrder = kMetaClass0 + 3;  // tile order of an MFMA list (select_dev.h)
-enum TileOrder { kOrderMix = 0, kOrderChunks = 1, kOrderLongestFirst = 2 };
-constexpr int kLongK = 4096;  // K from which an MFMA list keeps XCD chunks of equal-length tiles
-static_assert(kMetaOrder < kMetaStride, "meta layout");
+constexpr int kMetaQueue1 = kMetaOrder + 1;
+enum TileOrder { kOrderMix = 0, kOrderTwoClass = 1, kOrderLongestFirst = 2 };
+constexpr int kLongK = 4096;  // K from which an MFMA list takes the two-class order
+static_assert(kMetaQueue1 + kXcds <= kMetaStride, "meta layout");
+// Two-class order: relative CU time of a class-1 (short) tile against a class-0 (full-height) one,
+// in twentieths, which sets how many of an XCD's CUs start on each class.
+constexpr int kTwoClassW0 = 20, kTwoClassW1 = 11;
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t s);

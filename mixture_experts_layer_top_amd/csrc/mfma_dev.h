@@ -66,8 +66,12 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t off, lds_void* d
                : "memory", "m0");
 }
 
-// Next tile for this workgroup from the per-XCD queues (see the scheduling note above), or -1.
-// `q` is the workgroup's current queue offset (0 = its own XCD), kept across calls.
+// Next queue position for this workgroup from the per-XCD queues, or -1.  Workgroup b runs on XCD
+// b % kXcds (the dispatcher deals workgroups to the XCDs in turn); queue x hands out the positions
+// of XCD chunks x, x + kXcds, x + 2 kXcds, ... of `chunk` consecutive positions each, so the CUs of
+// one XCD work on neighbouring tiles, which share weight and token tiles in its L2.  A workgroup
+// drains its own XCD's queue, then takes from the others in turn.  `q` is the workgroup's current
+// queue offset (0 = its own XCD), kept across calls.
 __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chunk, int* slot,
                                             int& q) {
   const int xcd = blockIdx.x % kXcds;
@@ -86,19 +90,34 @@ __device__ __forceinline__ int pop_tile_xcd(int32_t* queues, int ntiles, int chu
   return -1;
 }
 
-// Queue position -> tile index in the chunked order: class-0 tiles are [0, H) in tile order,
-// class-1 ones [H, N).  Positions come in units of B (one XCD chunk); each class's whole units are
-// spread evenly over the first U0 + U1 units (among the first u units, floor(u * U1 / U) are
-// class 1), and the two classes' partial units (fewer than B tiles each) come last.
-__device__ __forceinline__ int chunked_interleave(int p, int H, int N, int B) {
-  const int L = N - H, U0 = H / B, U1 = L / B, U = U0 + U1;
-  const int u = p / B, o = p - u * B;
-  if (u < U) {
-    const int c1 = (int)((long long)u * U1 / U), c1n = (int)((long long)(u + 1) * U1 / U);
-    return c1n > c1 ? H + c1 * B + o : (u - c1) * B + o;
+// The two-class order: each XCD keeps one queue per class (class-0 tiles [0, n0) in tile order,
+// class-1 tiles [n0, n0 + n1)), with XCD chunks of b0 class-0 and b1 class-1 positions.  Workgroups
+// whose rank on their XCD (blockIdx.x / kXcds) is below r0 start on class 0, the others on class 1,
+// so every XCD runs both classes at once: its full-height tiles, which all take the same K loop,
+// stay in step in chunks that share operands in L2, while the short tiles stream beside them on
+// the same XCD.  A workgroup drains its own class's queue on its XCD, then the other class's, then
+// both queues of the other XCDs in turn.  Every position below a class's count is handed out
+// exactly once: the positions of one queue grow with its counter, so a queue that returned one past
+// its end is empty for good, and every workgroup visits every queue before it stops.  `q` counts
+// the (XCD, class) queues this workgroup has finished; returns the tile index, or -1.
+__device__ __forceinline__ int pop_tile_two_class(int32_t* queues0, int32_t* queues1, int n0, int n1,
+                                                  int b0, int b1, int pref, int* slot, int& q) {
+  const int xcd = blockIdx.x % kXcds;
+  while (q < 2 * kXcds) {
+    const int x = (xcd + (q >> 1)) % kXcds;
+    const int c = (q & 1) ^ pref;
+    const int b = c ? b1 : b0;
+    if (threadIdx.x == 0) {
+      const int i = atomicAdd(c ? &queues1[x] : &queues0[x], 1);
+      *slot = (i / b) * (b * kXcds) + x * b + (i % b);
+    }
+    __syncthreads();
+    const int p = __builtin_amdgcn_readfirstlane(*slot);
+    __syncthreads();
+    if (p < (c ? n1 : n0)) return c ? n0 + p : p;
+    ++q;
   }
-  const int q = p - U * B, r0 = H - U0 * B;
-  return q < r0 ? U0 * B + q : H + U1 * B + (q - r0);
+  return -1;
 }
 
 // Queue position -> tile index in the mixed order: the L class-1 tiles spread evenly between the

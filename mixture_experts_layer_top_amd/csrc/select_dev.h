@@ -52,16 +52,20 @@ __device__ __forceinline__ float block_eeff(int c, int N) {
 //    or more m-tiles ("heavy"), class 1 = the rest; the light tiles are spread evenly between the
 //    heavy ones, and an expert's last m-tile stays next to its siblings, which share its weight
 //    tile in L2.  (Streaming lists use the same classes.)
-//  * kOrderChunks (K >= kLongK, several rounds, some expert of more than one m-tile -- without one
+//  * kOrderTwoClass (K >= kLongK, several rounds, some expert of more than one m-tile -- without one
 //    no weight tile is shared by several m-tiles and the mixed order is faster, 3.5% on a
-//    DeepSeek-V3-shaped layer at T = 256): an expert whose last 256-row m-tile would hold at
-//    most 128 rows gets that tail as a segment of its own; class 0 = segments of full-height tiles,
-//    class 1 = shorter ones; whole XCD chunks of one class, the class-1 chunks spread evenly between
-//    the class-0 ones.  Short tiles still run beside MFMA-bound full ones across the chip, while the
-//    CUs of one XCD work on tiles of equal length and stay in step with the neighbours they share
-//    weight tiles with in L2 (with long K, a short tile inside a chunk drifts its neighbours apart:
-//    twice the gate/up L2 miss traffic was measured).
-//  * kOrderLongestFirst (one to kSplitMaxRounds rounds): classes as for kOrderChunks, tiles in
+//    DeepSeek-V3-shaped layer at T = 256): an expert whose last 256-row m-tile would hold at most
+//    128 rows gets that tail as a segment of its own; class 0 = segments of full-height tiles,
+//    class 1 = shorter ones.  Every XCD keeps one queue per class (pop_tile_two_class): part of its
+//    CUs runs the full-height tiles, which all take the same K loop, in chunks whose tiles stay in
+//    step and share weight and token tiles in L2 (with long K, a short tile among them drifts its
+//    neighbours apart: twice the gate/up L2 miss traffic was measured), while the rest streams the
+//    short tiles beside them on the same XCD.  It replaced an order of whole XCD chunks of one
+//    class each, which left an XCD on short tiles alone at times, their weight stream then limited
+//    by that XCD's share of the fabric: gate/up 1.2% faster on a Mixtral-shaped layer and 1.5% on
+//    a Kimi-K2-shaped one.  (Short K keeps the mixed order: the two-class order measured 5% slower
+//    on the Kimi-K2-shaped down GEMM, K = 2048.)
+//  * kOrderLongestFirst (one to kSplitMaxRounds rounds): classes as for kOrderTwoClass, tiles in
 //    order -- round quantization dominates, so the short ones fill the last round, whose tiles may
 //    be split in K.
 // The ranks and tile bases come from one block-wide scan of 16 per-expert counts.  Every thread of
@@ -109,12 +113,12 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
   // a split GEMM runs its two launches back to back with the MFMA one under-filled (1.3-1.5x the
   // all-MFMA time on a DeepSeek-V3-shaped layer at T = 64 and 256 with 8 effective experts).  The
   // same (block-wide) totals give the list's ordering mode: one to kSplitMaxRounds rounds ->
-  // longest first (below one round every tile starts at once and order does not matter); else XCD
-  // chunks when K >= kLongK and some expert spans several m-tiles.
+  // longest first (below one round every tile starts at once and order does not matter); else the
+  // two-class order when K >= kLongK and some expert spans several m-tiles.
   // fp8 and mxfp8-activation experts (automatic mode): a GEMM whose MFMA tiles would fill less than
   // one round of CUs runs wholly on the streaming tiles (one CU per weight tile draws too little of
   // the chip's bandwidth).
-  bool lpt[2] = {false, false}, chunks[2] = {false, false};
+  bool lpt[2] = {false, false}, two[2] = {false, false};
   if ((a.fp8 || a.mx8) && a.config < 0) {
     const int nt_dn = (a.d + kMfmaBNDown - 1) / kMfmaBNDown;
     int w[2], wex[2], wtot[2];
@@ -157,7 +161,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
         fm[g] = kFamStream;
       const int C = min(a.num_cus, kSplitMaxPieces);
       lpt[g] = wtot[g] >= C && wtot[g] < kSplitMaxRounds * C;
-      chunks[g] = !lpt[g] && (g == kGemmGateUp ? a.d : ffe) >= kLongK && wtot[2 + g] > 0;
+      two[g] = !lpt[g] && (g == kGemmGateUp ? a.d : ffe) >= kLongK && wtot[2 + g] > 0;
     }
   }
   // Segment j = 2 * gemm + part (part 0: main, 1: MFMA tail), rows [r0[j], r0[j] + nr[j]) of the
@@ -177,7 +181,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     for (int j = 0; j < NS; ++j) {
       const int g = j >> 1, part = j & 1;
       const bool mf = fm[g] == kFamMfma;
-      const bool split = mf && tail > 0 && (lpt[g] || chunks[g]);
+      const bool split = mf && tail > 0 && (lpt[g] || two[g]);
       fam[j] = part == 0 ? fm[g] : (split ? kFamMfma : -1);
       r0[j] = part == 0 ? 0 : c - tail;
       nr[j] = part == 0 ? (split ? c - tail : c) : tail;
@@ -192,7 +196,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
         nt[j] = (a.d + tn[j] - 1) / tn[j];
       }
       mt[j] = (nr[j] + tm - 1) / tm;
-      const bool by_height = mf && (lpt[g] || chunks[g]);
+      const bool by_height = mf && (lpt[g] || two[g]);
       cls[j] = by_height ? (nr[j] <= kMfmaBM / 2 ? 1 : 0) : (mt[j] >= 2 ? 0 : 1);
       // (all indexing below is static after unrolling, so nothing lands in scratch memory)
 #pragma unroll
@@ -308,6 +312,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     m[0] = nseg;
     m[1] = ntl;
     for (int q = kMetaQueue; q < kMetaQueue + kXcds; ++q) m[q] = 0;
+    for (int q = kMetaQueue1; q < kMetaQueue1 + kXcds; ++q) m[q] = 0;
     m[kMetaClass0] = ntl0;
     // MFMA lists of bf16 GEMMs with fewer than kSplitMaxRounds whole rounds (longest first when
     // there is at least one) split in K the tiles past the last whole round of CUs, S = 4 or 2
@@ -320,8 +325,8 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     const int C = min(a.num_cus, kSplitMaxPieces);
     const bool mfma_bf16 = e % kNumFam == kFamMfma && !a.fp8 && !a.w4;
     // (lpt[] is the same for every thread)
-    m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : chunks[g] ? kOrderChunks
-                                                                                      : kOrderMix;
+    m[kMetaOrder] = !mfma_bf16 ? kOrderMix : lpt[g] ? kOrderLongestFirst : two[g] ? kOrderTwoClass
+                                                                                  : kOrderMix;
     if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_part && uniform_k) {
       const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
       if (rem > 0) {

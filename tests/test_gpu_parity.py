@@ -313,13 +313,45 @@ def test_mfma_last_round_split(moe, T, f):
 
 
 # Tile orders at a size the oracle still checks in full: the long-K gate/up GEMM (d = 4096, 848
-# tiles on 256 CUs) takes the chunked order, with two heavy experts whose short last m-tiles become
-# segments of their own, 46 light experts and full-height single tiles; the down GEMM (K = 2048)
-# takes the mixed order.  (Routing draw: Dirichlet(0.3) over 64 experts, seed 150.)
+# tiles on 256 CUs) takes the two-class order, with two heavy experts whose short last m-tiles
+# become segments of their own, 46 light experts and full-height single tiles; the down GEMM
+# (K = 2048) takes the mixed order.  (Routing draw: Dirichlet(0.3) over 64 experts, seed 150.)
 def test_mfma_order_modes(moe):
     p = I.Problem("order_modes", 150, T=1000, d=4096, f=2048, E=64, k=2, routing="dirichlet",
                   alpha=0.3)
     _check_layer(moe, Inputs(p), config=-1, runs=2)
+
+
+def _planted_inputs(p, counts):
+    """Inputs whose routing gives exactly `counts` rows per expert (each count <= T): the T*k
+    slots are dealt in expert order, token t taking the experts at positions t, t + T, ..., which
+    are distinct, with logits far above every other expert's and strictly decreasing in j."""
+    counts = np.asarray(counts)
+    assert counts.sum() == p.T * p.k and counts.max() <= p.T
+    deal = np.repeat(np.arange(p.E), counts).reshape(p.k, p.T)
+    inp = Inputs(p)
+    lg = (inp.logits - 20.0).astype(np.float32)
+    for j in range(p.k):
+        lg[np.arange(p.T), deal[j]] = np.float32(10.0 - 0.5 * j)
+    inp.logits = lg
+    inp.d_logits = torch.from_numpy(lg).to("cuda")
+    return inp
+
+
+# The two-class order at its edges (long-K gate/up lists of at least three rounds of 256 CUs):
+# every tile full-height (16 experts of exactly three m-tiles, 768 tiles, no short class), and a
+# short class that dwarfs the full one (one expert of two m-tiles against 47 of 64 rows: 32 full
+# and 752 short tiles, so only two CUs of an XCD start on full tiles and the rest steal them).
+@pytest.mark.parametrize("case", ["full_only", "few_full"])
+def test_mfma_two_class_edges(moe, case):
+    if case == "full_only":
+        p = I.Problem("two_class_full", 151, T=6144, d=4096, f=2048, E=16, k=2)
+        counts = [768] * 16
+    else:
+        p = I.Problem("two_class_few", 152, T=1760, d=4096, f=2048, E=64, k=2)
+        counts = [512] + [64] * 47 + [0] * 16
+    inp = _planted_inputs(p, counts)
+    _check_layer(moe, inp, config=-1, runs=2)
 
 
 def test_generator_device_independent(moe):
