@@ -1163,11 +1163,17 @@ __global__ __launch_bounds__(256, 1) void mfma_split_epilogue(const Seg* __restr
       for (int q = 0; q < 4; ++q) {
         float t4[4] = {0.f, 0.f, 0.f, 0.f};
         if (a < NA && b < NB) {
+          // all pieces' loads first (S <= kSplitMaxS), then the sum in piece order
           const float* gb = part + ((a * 4 + b) * 4 + q) * 1024;
-          for (int p = 0; p < S; ++p) {
-            const uint4 w = gload16(gb + (size_t)p * kSplitSlotFloats, lane_off);
-            const float v[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
-                                __uint_as_float(w.w)};
+          uint4 w[kSplitMaxS];
+#pragma unroll
+          for (int p = 0; p < kSplitMaxS; ++p)
+            if (p < S) w[p] = gload16(gb + (size_t)p * kSplitSlotFloats, lane_off);
+#pragma unroll
+          for (int p = 0; p < kSplitMaxS; ++p) {
+            if (p >= S) break;
+            const float v[4] = {__uint_as_float(w[p].x), __uint_as_float(w[p].y),
+                                __uint_as_float(w[p].z), __uint_as_float(w[p].w)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) t4[i] = p == 0 ? v[i] : t4[i] + v[i];
           }

@@ -88,6 +88,7 @@ __device__ __forceinline__ int find_seg_lds(const int* base, int nseg, int t) {
 constexpr int kSplitMaxPieces = 256;  // partial-sum slots (one round of CUs)
 constexpr int kSplitSlotFloats = 256 * 256;  // one full tile's accumulators
 constexpr int kSplitMaxRounds = 3;    // longest-first order and split: fewer whole rounds than this
+constexpr int kSplitMaxS = 4;         // pieces per split tile: 2 or 4
 
 // Where the selection kernel writes its results (all inside the caller's workspace).
 struct SelectOut {

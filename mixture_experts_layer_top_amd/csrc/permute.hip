@@ -23,6 +23,7 @@ namespace moe {
 
 constexpr int kChunk = 2048;
 constexpr int kMaxE = 512;
+constexpr int kScanBatch = 8;
 
 __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ ids, int n,
                                                          int E, int32_t* __restrict__ rank,
@@ -76,11 +77,19 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
   __shared__ int tot[1024];
   const int e = threadIdx.x;
   int total = 0;
+  // (chunks in batches of kScanBatch: the batch's loads go out together instead of one round trip
+  // per chunk)
   if (e < E) {
-    for (int c = 0; c < nchunk; ++c) {
-      const int h = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = total;
-      total += h;
+    for (int c0 = 0; c0 < nchunk; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        h[i] = c0 + i < nchunk ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nchunk) chunk_hist[(size_t)(c0 + i) * E + e] = total;
+        total += h[i];
+      }
     }
     counts[e] = total;
   }
@@ -96,7 +105,15 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
   if (e < E) {
     const int excl = tot[e] - total;
     offsets[e] = excl;
-    for (int c = 0; c < nchunk; ++c) chunk_hist[(size_t)c * E + e] += excl;
+    for (int c0 = 0; c0 < nchunk; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (c0 + i < nchunk) h[i] = chunk_hist[(size_t)(c0 + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (c0 + i < nchunk) chunk_hist[(size_t)(c0 + i) * E + e] = h[i] + excl;
+    }
   }
   if (e == 0) offsets[E] = n;
 }

@@ -330,6 +330,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const SelectOu
     if (mfma_bf16 && ntl < kSplitMaxRounds * C && o.split_part && uniform_k) {
       const int rounds = ntl / C, rem = ntl - rounds * C, nk = K / 64;
       if (rem > 0) {
+        static_assert(kSplitMaxS == 4, "pieces per split tile");
         if (rem * 4 <= C && nk % 8 == 0) S = 4;
         else if (rem * 2 <= C && nk % 4 == 0) S = 2;
       }
