@@ -500,3 +500,100 @@ def test_layers_sharing_weights_equal_separate_layers():
             assert np.allclose(r["out"], direct["out"], rtol=1e-12, atol=1e-14)
             ids, _ = O.route(L, k)
             assert np.array_equal(r["ids"], ids)
+
+
+# ------------------------------------------------------------------------------------------------
+# storage decoding helpers: bf16 bits, block-scaled e4m3 weights and activations, the weight and
+# activation dispatch
+# ------------------------------------------------------------------------------------------------
+
+def test_bf16_bits_hand_worked():
+    """bfloat16 is the top half of a float32: sign, 8 exponent bits (bias 127), 7 mantissa bits."""
+    cases = {
+        0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x4049: 3.140625,   # 1.1001001b * 2^1
+        0x3E80: 0.25, 0x0001: 2.0 ** -133,                          # min subnormal
+        0x0080: 2.0 ** -126,                                        # min normal
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,                     # max finite
+        0x7F80: math.inf, 0xFF80: -math.inf, 0x0000: 0.0,
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    want = np.array(list(cases.values()))
+    assert np.array_equal(O.bf16_bits_to_f64(bits), want)
+    assert np.array_equal(O.bf16_bits_to_f32(bits), want.astype(np.float32))
+    neg0 = O.bf16_bits_to_f64(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+    # int16 storage (the binding's dtype) is read as the same bit patterns
+    assert np.array_equal(O.bf16_bits_to_f64(bits.view(np.int16)), want)
+    assert math.isnan(O.bf16_bits_to_f64(np.array([0x7FC0], np.uint16))[0])
+
+
+def _e4m3_spec(code: int) -> float:
+    """E4M3FN by its definition: sign, 4 exponent bits (bias 7), 3 mantissa bits, subnormals at
+    exponent 0, S.1111.111 NaN."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    mag = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def test_dequant_e4m3_blocks_by_element():
+    """Block (i // 128, j // 128) scales element (i, j): a 256 x 384 weight with a 2 x 3 scale grid
+    of distinct powers of two and random non-NaN codes, checked element by element."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(256, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11          # no NaN codes
+    scales = np.array([[0.5, 2.0, 8.0], [0.25, 4.0, 16.0]], np.float32)
+    got = O.dequant_e4m3_blocks(codes, scales)
+    for i in range(0, 256, 17):
+        for j in range(0, 384, 13):
+            assert got[i, j] == _e4m3_spec(int(codes[i, j])) * float(scales[i // 128, j // 128])
+    assert got[127, 255] == _e4m3_spec(int(codes[127, 255])) * 2.0
+    assert got[128, 256] == _e4m3_spec(int(codes[128, 256])) * 16.0
+
+
+def test_dequant_act_e4m3_by_element():
+    """Activation scales are per token and 128 channels: token t's group g scales [128 g, 128 g +
+    128) of row t only."""
+    rng = np.random.default_rng(8)
+    q = rng.integers(0, 256, size=(3, 256)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x22
+    s = np.array([[1.0, 0.5], [4.0, 0.125], [3.0, 6.0]], np.float32)
+    got = O.dequant_act_e4m3(q, s)
+    for t in range(3):
+        for c in range(256):
+            assert got[t, c] == _e4m3_spec(int(q[t, c])) * float(s[t, c // 128])
+
+
+def test_decode_weight_and_layer_input_dispatch():
+    """decode_weight: int16/uint16 bf16 bits, uint8 codes with fp32 block scales (e4m3) or uint8
+    E8M0 scales (mxfp4); layer_input: bf16 values unchanged, fp8 and mxfp8 through their
+    quantise-dequantise pairs."""
+    from oracle import mxfp4, mxfp8
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 1 << 16, size=(128, 128)).astype(np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80     # finite only
+    assert np.array_equal(O.decode_weight(bits.view(np.int16)), O.bf16_bits_to_f64(bits))
+    codes = rng.integers(0, 0x7F, size=(128, 256)).astype(np.uint8)
+    sc = np.array([[2.0, 0.5]], np.float32)
+    assert np.array_equal(O.decode_weight(codes, sc), O.dequant_e4m3_blocks(codes, sc))
+    packed = rng.integers(0, 256, size=(16, 64)).astype(np.uint8)
+    e8 = rng.integers(120, 134, size=(16, 4)).astype(np.uint8)
+    assert np.array_equal(O.decode_weight(packed, e8), mxfp4.dequant(packed, e8))
+    with pytest.raises(ValueError):
+        O.decode_weight(codes)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    xb = I.f32_to_bf16_bits(x)
+    v, q, s = O.layer_input(xb)
+    assert q is None and s is None and np.array_equal(v, O.bf16_bits_to_f64(xb))
+    v, q, s = O.layer_input(xb, act="fp8")
+    q2, s2 = O.quant_act_e4m3(xb)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.array_equal(v, O.dequant_act_e4m3(q2, s2))
+    assert np.array_equal(O.layer_input(xb, act_fp8=True)[0], v)
+    v, q, s = O.layer_input(xb, act="mxfp8")
+    q3, s3 = mxfp8.quant_act(xb)
+    assert np.array_equal(q, q3) and np.array_equal(s, s3)
+    assert np.array_equal(v, mxfp8.dequant_rows(q3, s3))
+    with pytest.raises(ValueError):
+        O.layer_input(xb, act="int4")
