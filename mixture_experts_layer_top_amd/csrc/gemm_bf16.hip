@@ -855,7 +855,13 @@ struct MfmaTile {
     constexpr int kStage = (TB * 32 + BNW) * ROWB64;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint8_t* st = g_ring + stage * kStage + wv * 8 * ROWB64;
-    dma16(slot_base<TB>(j) + ko, off[j], (lds_void*)(st + j * 32 * ROWB64));
+    // The gate/up weights of a short tile stream with the non-temporal policy: a light expert's
+    // weight rows are read by this tile alone, and left in L2 they only push out the tiles that
+    // full-height neighbours share (DeepSeek-V3-shaped decode at T = 64 and 256: gate/up -9%).
+    // Not the down weights: there the mixed order keeps an expert's short last m-tile next to
+    // its full-height siblings, which read the same weight rows (Kimi-K2-shaped down GEMM +7%).
+    if (GU && j >= TB) dma16<true>(slot_base<TB>(j) + ko, off[j], (lds_void*)(st + j * 32 * ROWB64));
+    else dma16(slot_base<TB>(j) + ko, off[j], (lds_void*)(st + j * 32 * ROWB64));
   }
 
   template <int TB>

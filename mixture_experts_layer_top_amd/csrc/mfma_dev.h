@@ -40,6 +40,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // The address is a uniform 64-bit base in SGPRs plus the lane's 32-bit byte offset (the
 // instruction's scalar-base form), so a lane keeps one offset register per load slot instead of a
 // 64-bit address.
+// NT: the non-temporal (streaming) cache policy, for bytes that no other tile reads.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, lds_void* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
   // (readfirstlane returns int: each half goes through uint32_t so that neither is sign-extended)
@@ -47,10 +49,16 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, lds_void* 
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | lo;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(sb), "s"(lds)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(off), "s"(sb), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(sb), "s"(lds)
+                 : "memory", "m0");
 }
 
 // The same for 4 bytes per lane: lane i's bytes land at dst + 4 * i.
