@@ -531,7 +531,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(experts would shard across GPUs with an all-to-all dispatch; not built).",
               file=sys.stderr)
         return 2
