@@ -69,6 +69,15 @@ __device__ __forceinline__ uint4 gload16(const void* base, uint32_t off) {
   const u32x4 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>((gchar*)base + off);
   return __builtin_bit_cast(uint4, v);
 }
+// The same with the non-temporal (streaming) cache policy, for weight bytes that one load reads
+// whole (the tiled narrow-format layouts: 1 KB contiguous per wavefront) and nothing reads again.
+// (Not for loads that take part of a 128-byte line each: evicted early, the line is fetched again
+// for the rest -- the row-major bf16 streaming tile measured slower with it.)
+__device__ __forceinline__ uint4 gload16_nt(const void* base, uint32_t off) {
+  const u32x4 v = __builtin_nontemporal_load(
+      reinterpret_cast<__attribute__((address_space(1))) const u32x4*>((gchar*)base + off));
+  return __builtin_bit_cast(uint4, v);
+}
 __device__ __forceinline__ uint2 gload8(const void* base, uint32_t off) {
   const u32x2 v = *reinterpret_cast<__attribute__((address_space(1))) const u32x2*>((gchar*)base + off);
   return __builtin_bit_cast(uint2, v);

@@ -234,8 +234,10 @@ __device__ __forceinline__ void stream_tile_w4(const Seg& sg, int m0, int rows, 
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
         const uint32_t wo = wblk[h] + (c0 + i) * 1024 + lane * 16;
-        bt.w0[h][i] = gload16(sg.w0, wo);
-        if (GU) bt.w1[h][i] = gload16(sg.w1, wo);
+        // gate/up: whole 1 KB units of the tiled layout, read once, with the non-temporal policy
+        // (gate/up -7 to -8% at T = 16 and 64); the down weights keep the default one (+2-3%)
+        bt.w0[h][i] = GU ? gload16_nt(sg.w0, wo) : gload16(sg.w0, wo);
+        if (GU) bt.w1[h][i] = gload16_nt(sg.w1, wo);
       }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

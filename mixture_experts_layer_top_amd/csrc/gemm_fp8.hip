@@ -100,9 +100,9 @@ __device__ __forceinline__ void fp8_gateup_tile(const Seg& sg, int m0, int rows,
   auto load = [&](Blk& b, int kb) {
     const uint32_t ko = (uint32_t)kb * 128;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      b.wg[g] = as_i32x8(gload16(sg.w0, woff[g] + ko * 16), gload16(sg.w0, woff[g] + ko * 16 + 1024));
-      b.wu[g] = as_i32x8(gload16(sg.w1, woff[g] + ko * 16), gload16(sg.w1, woff[g] + ko * 16 + 1024));
+    for (int g = 0; g < 2; ++g) {  // (weights: non-temporal, see gload16_nt; -6% per layer)
+      b.wg[g] = as_i32x8(gload16_nt(sg.w0, woff[g] + ko * 16), gload16_nt(sg.w0, woff[g] + ko * 16 + 1024));
+      b.wu[g] = as_i32x8(gload16_nt(sg.w1, woff[g] + ko * 16), gload16_nt(sg.w1, woff[g] + ko * 16 + 1024));
     }
 #pragma unroll
     for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
@@ -196,7 +196,7 @@ __device__ __forceinline__ void fp8_down_tile(const Seg& sg, int m0, int rows, i
   struct Blk { i32x8 w, xb[MQ]; float sw, sx[MQ]; };
   auto load = [&](Blk& b, int kb) {
     const uint32_t ko = (uint32_t)kb * 128;
-    b.w = as_i32x8(gload16(sg.w0, woff + ko * 16), gload16(sg.w0, woff + ko * 16 + 1024));
+    b.w = as_i32x8(gload16_nt(sg.w0, woff + ko * 16), gload16_nt(sg.w0, woff + ko * 16 + 1024));
 #pragma unroll
     for (int q = 0; q < MQ; ++q) b.xb[q] = as_i32x8(gload16(sg.a, xoff[q] + ko), gload16(sg.a, xoff[q] + ko + 16));
     b.sw = gload_f32(sg.s0, nb * nkb + kb);

@@ -71,6 +71,9 @@ hipError_t launch_quant_act_mx(const void* x, int T, int d, uint8_t* xq, uint8_t
 __device__ __forceinline__ i32x4 gload16i(const void* base, uint32_t off) {
   return __builtin_bit_cast(i32x4, gload16(base, off));
 }
+__device__ __forceinline__ i32x4 gload16i_nt(const void* base, uint32_t off) {
+  return __builtin_bit_cast(i32x4, gload16_nt(base, off));
+}
 
 __device__ __forceinline__ f32x4 mfma_mx(const i32x4& w, uint32_t sw, const i32x8& x, uint32_t sx,
                                          const f32x4& c) {
@@ -247,8 +250,8 @@ __device__ __forceinline__ void stream_tile_mx(const Seg& sg, int m0, int rows, 
     b.c = c;
 #pragma unroll
     for (int s = 0; s < NR; ++s) {
-      b.w0[s] = gload16i(sg.w0, wblk[s] + c * 1024);
-      if (GU) b.w1[s] = gload16i(sg.w1, wblk[s] + c * 1024);
+      b.w0[s] = gload16i_nt(sg.w0, wblk[s] + c * 1024);
+      if (GU) b.w1[s] = gload16i_nt(sg.w1, wblk[s] + c * 1024);
     }
 #pragma unroll
     for (int q = 0; q < MQ; ++q) {
