@@ -1127,7 +1127,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_bf16(const Seg* __restrict__
   Q.sbase = meta[kMetaSplitBase];
   Q.S = meta[kMetaSplitS];
   Q.nq = Q.sbase + (Q.ntiles - Q.sbase) * Q.S;
-  Q.chunk = max(1, (int)gridDim.x / kXcds);
+  // XCD chunk of the one-queue orders: twice the CUs of an XCD for the mixed order (DeepSeek-V3-
+  // shaped decode at T = 256: down GEMM 2.5-4.6% faster, other shapes unchanged), one round of
+  // them otherwise
+  Q.chunk = __builtin_amdgcn_readfirstlane(max(1, (int)gridDim.x / kXcds) *
+                                           (Q.order == kOrderMix ? 2 : 1));
   for (int i = threadIdx.x; i < Q.nseg; i += blockDim.x) seg_base[i] = segs[i].tile_base;
   __syncthreads();
   if (Q.S > 1) mfma_persistent<GU, true>(Q, split_part, &slot);
