@@ -99,9 +99,12 @@ def test_permute_bit_exact(moe, T, E, k):
 # combine and grouped FFN, each fed with the oracle's own intermediates
 # ------------------------------------------------------------------------------------------------
 
-def test_combine_matches_oracle(moe):
-    rng = np.random.default_rng(3)
-    T, E, k, d = 77, 16, 4, 384
+# d / 8 threads per token row: 48 (one 256-thread workgroup with idle lanes), 64 and 192
+# (64-thread workgroups), 256 (256), 896 (seven of 128, the Kimi-K2 and DeepSeek-V3 width)
+@pytest.mark.parametrize("T,E,k,d", [(77, 16, 4, 384), (33, 8, 2, 512), (50, 12, 3, 1536),
+                                     (19, 16, 8, 2048), (41, 64, 8, 7168)])
+def test_combine_matches_oracle(moe, T, E, k, d):
+    rng = np.random.default_rng(3 + d)
     L = rng.standard_normal((T, E)).astype(np.float32)
     rids, rw = O.route(L, k)
     _, rsd = O.permute(rids, E)
