@@ -105,6 +105,12 @@ __device__ __forceinline__ void gstore16(void* base, size_t off, uint4 v) {
   *reinterpret_cast<__attribute__((address_space(1))) u32x4*>((gwchar*)base + off) =
       __builtin_bit_cast(u32x4, v);
 }
+// The same with the non-temporal policy, for output that nothing reads again before it leaves the
+// caches.
+__device__ __forceinline__ void gstore16_nt(void* base, size_t off, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                              reinterpret_cast<__attribute__((address_space(1))) u32x4*>((gwchar*)base + off));
+}
 __device__ __forceinline__ void gstore4(void* base, size_t off, uint32_t v) {
   *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>((gwchar*)base + off) = v;
 }

@@ -630,9 +630,12 @@ __device__ __forceinline__ void MfmaTileStoreLds(const f32x16 (&acc)[4][4], void
   const int col = n0 + c * 8;
   const int nr = rows < H ? rows : H;
   if (col < N) {  // (down: the last tile of a row may be half full)
-    for (int t = tid / CPR; t < nr; t += RPP)
-      gstore16(out, ((size_t)(row0 + m0 + t) * N + col) * 2,
-               *reinterpret_cast<const uint4*>(g_ring + t * RS + c * 16));
+    for (int t = tid / CPR; t < nr; t += RPP) {
+      const uint4 v = *reinterpret_cast<const uint4*>(g_ring + t * RS + c * 16);
+      // h is read back by the down GEMM right away; y only by the combine, after the whole GEMM
+      if (GU) gstore16(out, ((size_t)(row0 + m0 + t) * N + col) * 2, v);
+      else gstore16_nt(out, ((size_t)(row0 + m0 + t) * N + col) * 2, v);
+    }
   }
 }
 
